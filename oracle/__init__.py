@@ -1,0 +1,145 @@
+"""Reference implementations of the variable-length attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the library under test imports,
+loads or calls this package; only ``tests/``, ``__graft_entry__.smoke()``
+and the benchmark's CPU-baseline leg do.  It shares no code with the HIP
+path: the only common module is the seeded input generator ``workloads``,
+which holds no attention arithmetic.
+
+* ``forward`` / ``forward_rows`` -- the double-precision C implementation in
+  ``varlen_oracle.c`` (a three-pass softmax per query row, in the order of
+  the boostr CPU forward ``varlen_attention_fwd``), threaded over
+  (sequence, head, 64-row) units.
+* ``brute.dense_forward`` -- an independent dense numpy checker for small
+  inputs (full score matrix, boolean mask, ``scipy.special.logsumexp``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "varlen_oracle.c")
+_LIB_DIR = os.path.join(_HERE, "_build")
+_LIB = os.path.join(_LIB_DIR, "libvarlen_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+class _Args(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("wl", ctypes.c_int32), ("wr", ctypes.c_int32), ("scale", ctypes.c_double),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("cu_q", ctypes.c_void_p), ("cu_k", ctypes.c_void_p),
+        ("seqused_k", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+        ("bt_stride", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("sinks", ctypes.c_void_p),
+    ]
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc into ``oracle/_build``."""
+    os.makedirs(_LIB_DIR, exist_ok=True)
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared",
+                        "-pthread", _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            lib = ctypes.CDLL(build())
+            lib.oracle_varlen_fwd.argtypes = [ctypes.POINTER(_Args), ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_int]
+            lib.oracle_varlen_fwd.restype = ctypes.c_int
+            lib.oracle_varlen_fwd_rows.argtypes = [ctypes.POINTER(_Args), ctypes.c_void_p,
+                                                   ctypes.c_int64, ctypes.c_void_p,
+                                                   ctypes.c_void_p, ctypes.c_int]
+            lib.oracle_varlen_fwd_rows.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _make_args(case: dict, keep: list) -> _Args:
+    def c(a, dt):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a, dtype=dt)
+        keep.append(a)
+        return a
+    elt = np.uint16 if case["dtype"] == "bf16" else np.float32
+    a = _Args()
+    a.dtype = 1 if case["dtype"] == "bf16" else 0
+    a.B, a.H, a.Hkv, a.D = case["B"], case["H"], case["Hkv"], case["D"]
+    a.causal = 1 if case["causal"] else 0
+    a.wl, a.wr = case["window_left"], case["window_right"]
+    a.scale = float(case["scale"])
+    a.q = _ptr(c(case["q"], elt))
+    a.cu_q = _ptr(c(case["cu_q"], np.int32))
+    if case.get("paged"):
+        a.k = _ptr(c(case["k_cache"], elt))
+        a.v = _ptr(c(case["v_cache"], elt))
+        a.seqused_k = _ptr(c(case["seqused_k"], np.int32))
+        bt = c(case["block_table"], np.int32)
+        a.block_table = _ptr(bt)
+        a.bt_stride = bt.shape[1]
+        a.block_size = case["block_size"]
+    else:
+        a.k = _ptr(c(case["k"], elt))
+        a.v = _ptr(c(case["v"], elt))
+        a.cu_k = _ptr(c(case["cu_k"], np.int32))
+    a.sinks = _ptr(c(case.get("sinks"), np.float32))
+    return a
+
+
+def forward(case: dict, nthreads: int | None = None):
+    """All rows.  Returns (out float64 [T_q, H, D], lse float64 [T_q, H])."""
+    lib = _load()
+    keep: list = []
+    a = _make_args(case, keep)
+    out = np.zeros((case["T_q"], case["H"], case["D"]), dtype=np.float64)
+    lse = np.zeros((case["T_q"], case["H"]), dtype=np.float64)
+    rc = lib.oracle_varlen_fwd(ctypes.byref(a), out.ctypes.data, lse.ctypes.data,
+                               nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (rc={rc})")
+    return out, lse
+
+
+def forward_rows(case: dict, tokens, heads, nthreads: int | None = None):
+    """Selected (token, head) pairs.  Returns (out [n, D], lse [n]) in float64."""
+    lib = _load()
+    keep: list = []
+    a = _make_args(case, keep)
+    pairs = (np.asarray(tokens, dtype=np.int64) * case["H"]
+             + np.asarray(heads, dtype=np.int64))
+    pairs = np.ascontiguousarray(pairs)
+    out = np.zeros((len(pairs), case["D"]), dtype=np.float64)
+    lse = np.zeros(len(pairs), dtype=np.float64)
+    rc = lib.oracle_varlen_fwd_rows(ctypes.byref(a), pairs.ctypes.data, len(pairs),
+                                    out.ctypes.data, lse.ctypes.data,
+                                    nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (rc={rc})")
+    return out, lse
