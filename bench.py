@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the variable-length attention forward on one MI355X.
+
+A step is one call of the forward (work-partition pre-pass + attention
+kernels) over one batch of seeded synthetic input already resident in HBM,
+through the C ABI's out variant with preallocated out / lse / workspace.
+
+Main workload: bf16 causal GQA prefill, 16 sequences with lengths drawn
+uniformly from [128, 4096] (seed 1002, 33,781 tokens), 32 query heads,
+8 kv heads, head_dim 128, scale 1/sqrt(128).  The value is mask-adjusted
+TFLOP/s: 4 * head_dim FLOPs per unmasked (query, key) pair per head.
+
+Also reported (same JSON line, key "also"): the full-attention Ulysses-shard
+shape, the sliding-window + sinks MQA shape (bound by HBM) and the paged
+decode shape (bound by HBM), each with its own step time and roofline.
+
+The roofline figure is for the dominant kernel: its average duration is the
+step time minus the pre-pass time, both measured here with HIP events on
+the stream the kernels run on.  cpu_baseline times the fp64 oracle on a
+bounded sample of rows of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- work counts
+def visible_pairs(case) -> np.ndarray:
+    """Unmasked (query, key) pairs per query row (same for every head)."""
+    INF = 1 << 40
+    left = case["window_left"] if case["window_left"] >= 0 else INF
+    right = 0 if case["causal"] else (case["window_right"] if case["window_right"] >= 0 else INF)
+    lens_q = np.diff(case["cu_q"]).astype(np.int64)
+    lens_k = (case["seqused_k"] if case["paged"] else np.diff(case["cu_k"])).astype(np.int64)
+    out = np.zeros(case["T_q"], np.int64)
+    for b in range(case["B"]):
+        s = int(case["cu_q"][b])
+        i = np.arange(lens_q[b], dtype=np.int64)
+        p = i + lens_k[b] - lens_q[b]
+        lo = np.maximum(0, p - left)
+        hi = np.minimum(lens_k[b] - 1, p + right)
+        out[s:s + lens_q[b]] = np.maximum(0, hi - lo + 1)
+    return out
+
+
+def flops(case) -> float:
+    return float(4 * case["D"] * case["H"] * visible_pairs(case).sum())
+
+
+def alg_bytes(case) -> float:
+    es = 2 if case["dtype"] == "bf16" else 4
+    H, Hkv, D = case["H"], case["Hkv"], case["D"]
+    qo = 2.0 * case["T_q"] * H * D * es
+    lse = 4.0 * case["T_q"] * H
+    if case["paged"]:
+        kv_rows = float(np.sum(case["seqused_k"]))
+        meta = 4.0 * (case["B"] + 1) + 4.0 * case["B"] + 4.0 * sum(
+            (int(x) + case["block_size"] - 1) // case["block_size"] for x in case["seqused_k"])
+    else:
+        kv_rows = float(case["T_k"])
+        meta = 8.0 * (case["B"] + 1)
+    return qo + lse + 2.0 * kv_rows * Hkv * D * es + meta
+
+
+# ---------------------------------------------------------------- GPU timing
+def _dev(a, torch):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def time_case(case, steps, warmup, torch):
+    import variable_length_attention_amd as va
+    q = _dev(case["q"], torch)
+    cu_q = _dev(case["cu_q"], torch)
+    sinks = _dev(case.get("sinks"), torch)
+    win = (case["window_left"], case["window_right"])
+    out = torch.empty_like(q)
+    lse = torch.empty((case["T_q"], case["H"]), dtype=torch.float32, device="cuda")
+    if case["paged"]:
+        kc, vc = _dev(case["k_cache"], torch), _dev(case["v_cache"], torch)
+        bt, su = _dev(case["block_table"], torch), _dev(case["seqused_k"], torch)
+        prob = va.make_problem(q, kc.shape[2], 0, case["B"], case["max_q"], case["max_k"], case["scale"],
+                               case["causal"], win, kc.shape[0], kc.shape[1], bt.shape[1])
+        ws = torch.empty(va.workspace_size(prob, True), dtype=torch.uint8, device="cuda")
+
+        def step():
+            va.varlen_attn_paged(q, kc, vc, bt, cu_q, su, case["max_q"], case["max_k"],
+                                 scale=case["scale"], causal=case["causal"], window=win, sinks=sinks,
+                                 out=out, lse=lse, workspace=ws)
+        seqlens = su
+    else:
+        k, v, cu_k = _dev(case["k"], torch), _dev(case["v"], torch), _dev(case["cu_k"], torch)
+        prob = va.make_problem(q, k.shape[1], k.shape[0], case["B"], case["max_q"], case["max_k"],
+                               case["scale"], case["causal"], win)
+        ws = torch.empty(va.workspace_size(prob, False), dtype=torch.uint8, device="cuda")
+
+        def step():
+            va.varlen_attn_out(out, q, k, v, cu_q, cu_k, case["max_q"], case["max_k"], scale=case["scale"],
+                               causal=case["causal"], window=win, sinks=sinks, lse=lse, workspace=ws)
+        seqlens = cu_k
+    path = va.kernel_path(prob, case["paged"])
+
+    # pre-pass alone, through the plan entry point (count only)
+    import ctypes
+    from variable_length_attention_amd import _lib
+    lib = _lib.load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def plan_step():
+        _lib.check(lib.varlen_attn_plan(ctypes.byref(prob), 1 if case["paged"] else 0,
+                                        ctypes.c_void_p(cu_q.data_ptr()), ctypes.c_void_p(seqlens.data_ptr()),
+                                        None, 0, None,
+                                        ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()), stream))
+
+    def timed(fn, n, w):
+        for _ in range(w):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms_step = timed(step, steps, warmup)
+    ms_plan = timed(plan_step, steps, max(1, warmup))
+    return ms_step, ms_plan, path
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_baseline(case, budget_s=15.0):
+    import oracle
+    threads = min(16, oracle.default_threads())
+    vis = visible_pairs(case)
+    rng = np.random.default_rng(12345)
+    done_flops, done_rows, spent = 0.0, 0, 0.0
+    n = 64
+    while spent < budget_s:
+        toks = rng.integers(0, case["T_q"], n)
+        heads = rng.integers(0, case["H"], n)
+        t0 = time.perf_counter()
+        oracle.forward_rows(case, toks, heads, nthreads=threads)
+        dt = time.perf_counter() - t0
+        spent += dt
+        done_rows += n
+        done_flops += float(4 * case["D"] * vis[toks].sum())
+        if dt < budget_s / 4:
+            n *= 2
+    return {"value": done_flops / spent / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done_rows} random (token, head) rows of the same workload, "
+                      f"{done_flops / 1e9:.1f} mask-adjusted GFLOP in {spent:.1f} s (fp64)"}
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only-main", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--configs", default="2,3,4,5", help="workloads to time (first is the main one)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the attention forward "
+              "is measured per GPU; sharding across GPUs is not part of this library.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    cfgs = [int(x) for x in args.configs.split(",")]
+    if args.only_main:
+        cfgs = cfgs[:1]
+    results = {}
+    main_case = None
+    for n in cfgs:
+        spec = W.config(n)
+        log(f"config {n} ({spec.name}): generating input")
+        case = W.make_case(spec)
+        log(f"config {n}: timing {args.steps} steps after {args.warmup} warm-up")
+        ms_step, ms_plan, path = time_case(case, args.steps, args.warmup, torch)
+        fl, by = flops(case), alg_bytes(case)
+        ms_kernel = max(ms_step - ms_plan, 1e-6)
+        hbm_bound = path == 1 or (fl / by) < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+        r = {"workload": spec.name, "ms_per_step": ms_step, "ms_prepass": ms_plan,
+             "tflops": fl / (ms_step * 1e-3) / 1e12, "gbs": by / (ms_step * 1e-3) / 1e9,
+             "tokens_per_s": case["T_q"] / (ms_step * 1e-3), "flop": fl, "bytes": by,
+             "kernel_path": ["prefill_bf16", "decode_bf16", "f32"][path]}
+        if hbm_bound:
+            ach = by / (ms_kernel * 1e-3) / 1e9
+            r["roofline"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": ach / PEAK_HBM_GBS, "traffic": None}
+        else:
+            ach = fl / (ms_kernel * 1e-3) / 1e12
+            r["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": ach / PEAK_BF16_TFLOPS, "traffic": None}
+        log(f"config {n}: {ms_step:.4f} ms/step (pre-pass {ms_plan:.4f} ms), {r['tflops']:.1f} TFLOP/s, "
+            f"{r['gbs']:.0f} GB/s, roofline {r['roofline']['frac'] * 100:.1f}% of {r['roofline']['bound']}")
+        results[n] = r
+        if main_case is None:
+            main_case = case
+        else:
+            del case
+    n0 = cfgs[0]
+    main = results[n0]
+    spec0 = W.config(n0)
+    line = {
+        "metric": "varlen attn fwd TFLOP/s (mask-adjusted)",
+        "value": main["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": main["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if spec0.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": spec0.name, "batch": main_case["B"], "total_tokens": main_case["T_q"],
+                   "num_heads": spec0.H, "num_kv_heads": spec0.Hkv, "head_dim": spec0.D,
+                   "causal": spec0.causal, "window": list(spec0.window), "sinks": spec0.sinks,
+                   "paged": spec0.paged, "seed": spec0.seed},
+        "roofline": main["roofline"],
+        "tokens_per_s": main["tokens_per_s"],
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on a sample of rows")
+        line["cpu_baseline"] = cpu_baseline(main_case)
+    line["also"] = {results[n]["workload"]: {k: v for k, v in results[n].items() if k != "workload"}
+                    for n in cfgs[1:]}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * varlen_attn.h -- C ABI of the variable-length packed attention forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (SparseAttnSharedkv README, formula section; boostr
+ * varlen_attention.rs, varlen_attention_fwd):
+ *
+ *   for every sequence b, query row i < Lq_b and query head h
+ *     c     = h / (H / H_kv)                       kv head shared by a GQA group
+ *     s_j   = scale * <q[cu_q[b]+i, h, :], k_j[c, :]>
+ *     A(i)  = { j < Lk_b : causal -> j <= p, window_left  >= 0 -> j >= p - window_left,
+ *                                          window_right >= 0 -> j <= p + window_right }
+ *             with p = i + Lk_b - Lq_b  (queries aligned to the end of the keys)
+ *     m     = max( {s_j : j in A(i)} U {sinks[h]} )
+ *     Z     = sum_{j in A(i)} exp(s_j - m) + exp(sinks[h] - m)
+ *     out[cu_q[b]+i, h, :] = sum_{j in A(i)} exp(s_j - m) / Z * v_j[c, :]
+ *     lse[cu_q[b]+i, h]    = m + ln Z                       (natural log, fp32)
+ *
+ *   The sink terms are dropped when `sinks` is NULL.  A row with no allowed
+ *   key and no sink gets out = 0 and lse = -inf (never NaN).
+ *
+ * Layouts (all row-major, contiguous, element strides implied by the shapes):
+ *   q, out        [total_q, H, D]                 "TND" packing
+ *   k, v          [total_k, H_kv, D]              contiguous mode
+ *   k_cache, v_cache [num_blocks, block_size, H_kv, D]   paged mode ("PA_ND")
+ *   block_table   int32 [batch, block_table_stride]; key j of sequence b is
+ *                 row (j % block_size) of block block_table[b][j / block_size]
+ *   cu_seqlens_q  int32 [batch + 1] prefix sums (cu[0] = 0, non-decreasing,
+ *                 cu[batch] = total_q); cu_seqlens_k likewise for keys
+ *   seqused_k     int32 [batch] key count per sequence (paged mode)
+ *   sinks         float32 [H] or NULL
+ *   lse           float32 [total_q, H] or NULL when not wanted
+ *   q, k, v, out share one dtype (VA_F32 or VA_BF16); out is rounded to
+ *   nearest-even.
+ *
+ * Ownership and streams: every pointer handed in is caller-owned device
+ * memory (except `va_problem`, which is host memory and only read during the
+ * call).  Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ * stream) and the call returns without synchronising; buffers must stay alive
+ * until the stream reaches the work.  The library keeps no pointer after a
+ * call returns.  Only `out`, `lse` and `workspace` are written; bytes of `out`
+ * outside [total_q, H, D] are never touched.
+ *
+ * Errors: every condition the host can check is checked before anything is
+ * enqueued; a failing call launches nothing and writes nothing, returns a
+ * non-zero va_status and leaves a message for varlen_attn_last_error().
+ * Device-resident preconditions are NOT checked (checking would need a
+ * synchronisation): cu_seqlens monotone with cu[batch] equal to the total,
+ * every length <= the max_seqlen given, seqused_k[b] <= block_table_stride *
+ * block_size, every block id used < num_blocks.  Violating them is undefined
+ * behaviour.
+ *
+ * ABI rule: a shipped declaration never changes; a changed signature gets a
+ * new _v2 name (the rule PyTorch applies to its stable C shim, per the pull
+ * request "[varlen_attn for inference] add out variant").
+ */
+#ifndef VARLEN_ATTN_H
+#define VARLEN_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VARLEN_ATTN_ABI_VERSION 1
+
+typedef enum {
+    VA_OK = 0,
+    VA_ERR_NULL = 1,         /* a required pointer is NULL                        */
+    VA_ERR_SHAPE = 2,        /* inconsistent sizes (H % H_kv, batch < 1, totals 0) */
+    VA_ERR_DTYPE = 3,        /* dtype not VA_F32 / VA_BF16                        */
+    VA_ERR_UNSUPPORTED = 4,  /* head_dim not 64 / 128, window < -1, ...           */
+    VA_ERR_ALIAS = 5,        /* out or lse overlaps an input or each other        */
+    VA_ERR_ALIGN = 6,        /* a data pointer is not 16-byte aligned             */
+    VA_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than required           */
+    VA_ERR_HIP = 8,          /* a HIP runtime call or kernel launch failed        */
+    VA_ERR_DEVICE_CHECK = 9  /* reserved: opt-in device-side argument check       */
+} va_status;
+
+typedef enum { VA_F32 = 0, VA_BF16 = 1 } va_dtype;
+
+/* Problem description, host memory.  Field meaning follows the argument list
+ * of the out-variant op in the pull request "[varlen_attn for inference] add
+ * out variant" (max_q / max_k, scale, window_size_left / right, seqused_k,
+ * page_table) and the SparseAttnSharedkv README parameter table. */
+typedef struct {
+    uint32_t struct_size;     /* sizeof(va_problem); allows appending fields      */
+    int32_t dtype;            /* va_dtype of q, k, v, out                          */
+    int32_t batch;            /* B >= 1                                            */
+    int32_t total_q;          /* rows of q / out (>= 1)                            */
+    int32_t total_k;          /* rows of k / v (contiguous mode; ignored if paged) */
+    int32_t num_heads;        /* H                                                 */
+    int32_t num_kv_heads;     /* H_kv, divides H                                   */
+    int32_t head_dim;         /* D: 64 or 128                                      */
+    int32_t max_seqlen_q;     /* host upper bound of every Lq_b (grid sizing only) */
+    int32_t max_seqlen_k;     /* host upper bound of every Lk_b                    */
+    float scale;              /* multiplies q.k (not the sink); > 0                */
+    int32_t causal;           /* 0 / 1; aligned to the end of the keys             */
+    int32_t window_left;      /* keys before the query position, -1 = unbounded   */
+    int32_t window_right;     /* keys after the query position, -1 = unbounded    */
+    int32_t num_blocks;       /* paged: blocks in the cache                        */
+    int32_t block_size;       /* paged: tokens per block, multiple of 16, <= 1024  */
+    int32_t block_table_stride; /* paged: int32 entries per block_table row        */
+} va_problem;
+
+/* Bytes of device workspace `varlen_attn_fwd_out` (paged = 0) or
+ * `varlen_attn_fwd_paged` (paged = 1) needs for this problem; 0 if the
+ * problem is invalid (the entry point then reports why). */
+size_t varlen_attn_workspace_size(const va_problem *p, int paged);
+
+/* Out variant, contiguous K/V: writes out [total_q, H, D] (and lse when not
+ * NULL) into caller buffers.  `workspace` is device memory of at least
+ * varlen_attn_workspace_size(p, 0) bytes, used only during the enqueued work;
+ * its contents on entry do not matter.  (Pull request "[varlen_attn for
+ * inference] add out variant": one implementation behind an allocating entry
+ * point and an out entry point.) */
+va_status varlen_attn_fwd_out(const va_problem *p, const void *q, const void *k,
+                              const void *v, const int32_t *cu_seqlens_q,
+                              const int32_t *cu_seqlens_k, const float *sinks,
+                              void *out, float *lse, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Allocating variant: same computation as varlen_attn_fwd_out (bitwise the
+ * same results).  Allocates *out (total_q * H * D elements of the dtype) and,
+ * when lse != NULL, *lse (total_q * H floats) stream-ordered on `stream`; the
+ * caller releases them with varlen_attn_free.  The workspace is allocated and
+ * released internally, stream-ordered.  On error nothing is allocated and
+ * *out / *lse are set to NULL. */
+va_status varlen_attn_fwd(const va_problem *p, const void *q, const void *k,
+                          const void *v, const int32_t *cu_seqlens_q,
+                          const int32_t *cu_seqlens_k, const float *sinks,
+                          void **out, float **lse, void *stream);
+
+/* Paged K/V (SparseAttnSharedkv README, PageAttention constraints; pull
+ * request "[varlen_attn for inference] add out variant", page_table and
+ * seqused_k arguments): key length of sequence b is seqused_k[b]; keys are
+ * read through block_table.  Caches may alias each other (K == V). */
+va_status varlen_attn_fwd_paged(const va_problem *p, const void *q, const void *k_cache,
+                                const void *v_cache, const int32_t *block_table,
+                                const int32_t *cu_seqlens_q, const int32_t *seqused_k,
+                                const float *sinks, void *out, float *lse,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Releases memory returned by varlen_attn_fwd, stream-ordered. */
+va_status varlen_attn_free(void *ptr, void *stream);
+
+/* Work partition of a call (the GPU pre-pass that maps ragged sequences to
+ * tiles, in the role of the partition metadata operator that precedes
+ * SparseAttnSharedkv): runs only that pre-pass and copies its list into
+ * `items` (device int32 [capacity][4]: sequence, first query row or split
+ * index, first key, end key) and the count into `count` (device int32 [1]),
+ * in execution order.  `seqlens_k` is cu_seqlens_k (paged = 0) or seqused_k
+ * (paged = 1).  With capacity 0, items and count may be NULL and only the
+ * pre-pass runs (used to time it).  For tests of the partition. */
+va_status varlen_attn_plan(const va_problem *p, int paged, const int32_t *cu_seqlens_q,
+                           const int32_t *seqlens_k, int32_t *items, int32_t capacity,
+                           int32_t *count, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Which kernel family a call with these arguments would use:
+ * 0 = prefill tiles, 1 = split-KV decode with combine, 2 = float32 path;
+ * -1 if invalid. */
+int varlen_attn_path(const va_problem *p, int paged);
+
+/* Thread-local text for the last non-OK status returned on this thread. */
+const char *varlen_attn_last_error(void);
+
+int varlen_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VARLEN_ATTN_H */

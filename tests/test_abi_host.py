@@ -1,0 +1,143 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every
+function include/varlen_attn.h declares, sizes workspaces, picks kernel
+paths, and rejects invalid arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from variable_length_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "varlen_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(varlen_attn_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_exactly_the_bound_functions():
+    assert _declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.varlen_attn_abi_version() == 1
+
+
+def test_problem_struct_size_matches_header():
+    # 17 four-byte fields
+    assert ctypes.sizeof(_lib.VaProblem) == 17 * 4
+
+
+def _prob(**kw):
+    p = _lib.VaProblem()
+    p.struct_size = ctypes.sizeof(_lib.VaProblem)
+    defaults = dict(dtype=1, batch=2, total_q=100, total_k=100, num_heads=8, num_kv_heads=2,
+                    head_dim=128, max_seqlen_q=60, max_seqlen_k=60, scale=0.088, causal=1,
+                    window_left=-1, window_right=-1, num_blocks=0, block_size=0, block_table_stride=0)
+    defaults.update(kw)
+    for k, v in defaults.items():
+        setattr(p, k, v)
+    return p
+
+
+# fake, aligned, never-dereferenced device addresses: every call below must
+# fail validation before anything is enqueued
+A = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(12)]
+
+
+def _fwd_out(p, q=A[0], k=A[1], v=A[2], cuq=A[3], cuk=A[4], sinks=None, out=A[5], lse=None,
+             ws=A[6], ws_bytes=1 << 30):
+    lib = _lib.load()
+    return lib.varlen_attn_fwd_out(ctypes.byref(p), q, k, v, cuq, cuk, sinks, out, lse, ws,
+                                   ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_heads=6, num_kv_heads=4), 2),        # H % H_kv != 0
+    (dict(dtype=7), 3),
+    (dict(head_dim=96), 4),
+    (dict(batch=0), 2),
+    (dict(total_q=0), 2),                          # empty tensors are not accepted
+    (dict(total_k=0), 2),
+    (dict(window_left=-2), 4),
+    (dict(max_seqlen_q=0), 2),
+    (dict(struct_size=8), 2),
+    (dict(scale=float("nan")), 4),
+])
+def test_invalid_problems_are_rejected(kw, code):
+    st = _fwd_out(_prob(**kw))
+    assert st == code
+    assert _lib.load().varlen_attn_last_error()
+
+
+def test_null_pointers_alignment_aliasing_workspace():
+    p = _prob()
+    assert _fwd_out(p, q=None) == 1
+    assert _fwd_out(p, cuk=None) == 1
+    assert _fwd_out(p, out=None) == 1
+    assert _fwd_out(p, q=ctypes.c_void_p(0x10000008)) == 6       # not 16-byte aligned
+    assert _fwd_out(p, out=A[0]) == 5                            # out aliases q
+    assert _fwd_out(p, lse=ctypes.c_void_p(A[5].value + 64)) == 5  # lse inside out
+    assert _fwd_out(p, ws=None) == 7
+    assert _fwd_out(p, ws_bytes=16) == 7
+
+
+def test_paged_block_size_and_stride_validation():
+    lib = _lib.load()
+
+    p = _prob(num_blocks=10, block_size=40, block_table_stride=8)
+    assert lib.varlen_attn_fwd_paged(ctypes.byref(p), A[0], A[1], A[2], A[7], A[3], A[8], None,
+                                     A[5], None, A[6], ctypes.c_size_t(1 << 30), None) == 4
+    p = _prob(num_blocks=10, block_size=64, block_table_stride=1, max_seqlen_k=200)
+    assert lib.varlen_attn_fwd_paged(ctypes.byref(p), A[0], A[1], A[2], A[7], A[3], A[8], None,
+                                     A[5], None, A[6], ctypes.c_size_t(1 << 30), None) == 2
+    p = _prob(num_blocks=10, block_size=2048, block_table_stride=8)
+    assert lib.varlen_attn_fwd_paged(ctypes.byref(p), A[0], A[1], A[2], A[7], A[3], A[8], None,
+                                     A[5], None, A[6], ctypes.c_size_t(1 << 30), None) == 4
+
+
+def test_allocating_entry_rejects_before_allocating():
+    lib = _lib.load()
+    out = ctypes.c_void_p(123)
+    p = _prob(num_heads=5, num_kv_heads=2)
+    st = lib.varlen_attn_fwd(ctypes.byref(p), A[0], A[1], A[2], A[3], A[4], None, ctypes.byref(out),
+                             None, None)
+    assert st == 2 and out.value is None
+
+
+def test_workspace_size_and_kernel_path():
+    lib = _lib.load()
+    # causal bf16 prefill, GQA 4 -> tile path
+    p = _prob(num_heads=32, num_kv_heads=8, total_q=33781, total_k=33781, batch=16,
+              max_seqlen_q=4096, max_seqlen_k=4096)
+    assert lib.varlen_attn_path(ctypes.byref(p), 0) == 0
+    ws = lib.varlen_attn_workspace_size(ctypes.byref(p), 0)
+    n_max = (33781 + 16 * 127) // 128
+    assert ws >= 16 * n_max * 2 + 4 * n_max
+    # decode shape: g * max_q = 4 * 4 = 16 -> split-KV path with partials
+    p = _prob(num_heads=32, num_kv_heads=8, total_q=327, batch=128, max_seqlen_q=4,
+              max_seqlen_k=32768, num_blocks=33690, block_size=64, block_table_stride=512)
+    assert lib.varlen_attn_path(ctypes.byref(p), 1) == 1
+    assert lib.varlen_attn_workspace_size(ctypes.byref(p), 1) > 16 * 128 * 4
+    # float32 always takes the float32 kernels
+    p = _prob(dtype=0, head_dim=64, num_heads=4, num_kv_heads=2)
+    assert lib.varlen_attn_path(ctypes.byref(p), 0) == 2
+    # invalid -> 0 bytes / -1
+    p = _prob(head_dim=80)
+    assert lib.varlen_attn_workspace_size(ctypes.byref(p), 0) == 0
+    assert lib.varlen_attn_path(ctypes.byref(p), 0) == -1
+
+
+def test_binding_raises_value_error_with_message():
+    with pytest.raises(ValueError, match="VA_ERR_SHAPE"):
+        _lib.check(2)
+    with pytest.raises(RuntimeError, match="VA_ERR_HIP"):
+        _lib.check(8)

@@ -1,0 +1,354 @@
+"""Parity of the HIP path (called through the C ABI) with the fp64 oracle.
+
+Tolerances (max-abs): float32 inputs 1e-5 on O and LSE; bf16 inputs 2e-2 on
+O and 1e-3 on LSE.  Index work (work partition, block-table gathers) is
+compared bit-exactly, as are the invariants that must hold bitwise
+(out variant vs allocating variant, run-to-run, block permutation).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from helpers import (TOL, announce, assert_close, dev, run_case, sample_pairs, sweep_cases,
+                     to_f64)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the GPU tests need an MI355X")
+    import variable_length_attention_amd._lib as L
+    L.load()  # fails loudly when the HIP library is missing
+    yield
+
+
+def _check_full(case, what):
+    announce(what)
+    out, lse = run_case(case, torch)
+    ref_out, ref_lse = oracle.forward(case)
+    return assert_close(case, to_f64(out), to_f64(lse), ref_out, ref_lse, what)
+
+
+# ------------------------------------------------------------------ configs
+def test_config1_tiny_f32_full():
+    case = W.make_case(W.config(1))
+    e = _check_full(case, "config1 f32 causal gqa")
+    assert e[0] <= 1e-5 and e[1] <= 1e-5
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_scaled_configs_full(n):
+    spec = W.scaled(W.config(n), B=6, max_len=300)
+    _check_full(W.make_case(spec), f"config{n} scaled")
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_scaled_configs_larger(n):
+    """Several 128-row tiles and a ragged tail per sequence."""
+    spec = W.scaled(W.config(n), B=4, max_len=700, seed=W.config(n).seed + 100)
+    if n == 5:
+        spec = W.Spec(**{**spec.__dict__, "lens_k": ("uniform", 300, 2000)})
+    _check_full(W.make_case(spec), f"config{n} scaled larger")
+
+
+@pytest.mark.parametrize("idx", range(14))
+def test_structural_sweep(idx):
+    case = sweep_cases()[idx]
+    if case["T_q"] == 0 or (not case["paged"] and case["T_k"] == 0):
+        with pytest.raises(ValueError):
+            run_case(case, torch)
+        return
+    _check_full(case, f"sweep {idx}")
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_full_size_configs_sampled(n):
+    """Full-size workload in the benchmark's launch configuration (out
+    variant, preallocated workspace); outputs checked on sampled rows."""
+    announce(f"config{n} full size: generating")
+    case = W.make_case(W.config(n))
+    announce(f"config{n} full size: running")
+    out, lse = run_case(case, torch)
+    toks, heads = sample_pairs(case, 192, seed=n)
+    announce(f"config{n} full size: oracle on {len(toks)} rows")
+    ref_o, ref_l = oracle.forward_rows(case, toks, heads)
+    o = to_f64(out[torch.from_numpy(toks).cuda(), torch.from_numpy(heads).cuda()])
+    l = to_f64(lse[torch.from_numpy(toks).cuda(), torch.from_numpy(heads).cuda()])
+    assert_close(case, o, l, ref_o, ref_l, f"config{n} full sampled")
+    # properties that hold for every row: finite outputs, LSE finite where keys exist
+    assert bool(torch.isfinite(out).all())
+    assert not bool(torch.isnan(lse).any())
+
+
+# ------------------------------------------------------------------ variants and invariants
+def test_f32_paged_and_window_sinks():
+    spec = W.Spec("f32paged", 901, "f32", 8, 2, 128, ("uniform", 1, 40, 5),
+                  lens_k=("uniform", 50, 300), causal=True, sinks=True, paged=True, block_size=32)
+    _check_full(W.make_case(spec), "f32 paged")
+    spec = W.Spec("f32win", 902, "f32", 4, 4, 64, ("uniform", 100, 300, 3), window=(17, 9), sinks=True)
+    _check_full(W.make_case(spec), "f32 window sinks")
+
+
+def test_bf16_prefill_paged_long_queries():
+    """Paged K/V with queries too long for the decode path (tile path gathers
+    through the block table)."""
+    spec = W.Spec("paged_prefill", 903, "bf16", 16, 2, 128, ("uniform", 20, 200, 4),
+                  lens_k=("uniform", 200, 600), causal=True, paged=True, block_size=16)
+    case = W.make_case(spec)
+    _check_full(case, "paged prefill")
+
+
+def test_out_variant_bitwise_equals_allocating_variant():
+    import variable_length_attention_amd as va
+    for spec in (W.scaled(W.config(2), B=5, max_len=400), W.config(1),
+                 W.scaled(W.config(4), B=3, max_len=300)):
+        case = W.make_case(spec)
+        announce(f"out vs alloc {spec.name}")
+        q, k, v = dev(case["q"], torch), dev(case["k"], torch), dev(case["v"], torch)
+        cq, ck = dev(case["cu_q"], torch), dev(case["cu_k"], torch)
+        sinks = dev(case.get("sinks"), torch)
+        win = (case["window_left"], case["window_right"])
+        out = torch.empty_like(q)
+        lse = va.varlen_attn_out(out, q, k, v, cq, ck, case["max_q"], case["max_k"], scale=case["scale"],
+                                 causal=case["causal"], window=win, sinks=sinks, return_lse=True)
+        out2, lse2 = va.varlen_attn_fwd(q, k, v, cq, ck, case["max_q"], case["max_k"], scale=case["scale"],
+                                        causal=case["causal"], window=win, sinks=sinks, return_lse=True)
+        out3, lse3 = va.varlen_attn(q, k, v, cq, ck, case["max_q"], case["max_k"], scale=case["scale"],
+                                    causal=case["causal"], window=win, sinks=sinks, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32),
+                           out2.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32))
+        assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+        assert torch.equal(out, out3) and torch.equal(lse.view(torch.int32), lse3.view(torch.int32))
+
+
+@pytest.mark.parametrize("n", [2, 4, 5])
+def test_run_to_run_bitwise_determinism(n):
+    case = W.make_case(W.scaled(W.config(n), B=6, max_len=500))
+    announce(f"determinism config{n}")
+    o1, l1 = run_case(case, torch)
+    o2, l2 = run_case(case, torch)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
+def test_block_permutation_invariance_bitwise():
+    spec = W.Spec("perm", 904, "bf16", 32, 8, 128, ("uniform", 1, 4, 12),
+                  lens_k=("uniform", 100, 3000), causal=True, paged=True, block_size=64, sinks=True)
+    case = W.make_case(spec)
+    announce("block permutation A")
+    o1, l1 = run_case(case, torch)
+    # same logical cache, another physical arrangement of its blocks
+    rng = np.random.default_rng(5)
+    n_used = case["num_blocks"] - 1
+    perm2 = rng.permutation(n_used)
+    kc2 = case["k_cache"].copy()
+    vc2 = case["v_cache"].copy()
+    bt2 = case["block_table"].copy()
+    valid = bt2 < n_used
+    kc2[perm2] = case["k_cache"][:n_used]
+    vc2[perm2] = case["v_cache"][:n_used]
+    bt2[valid] = perm2[case["block_table"][valid]]
+    case2 = dict(case, k_cache=kc2, v_cache=vc2, block_table=bt2)
+    announce("block permutation B")
+    o2, l2 = run_case(case2, torch)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+    ref_o, ref_l = oracle.forward(case)
+    assert_close(case, to_f64(o1), to_f64(l1), ref_o, ref_l, "perm vs oracle")
+
+
+def test_nan_poison_in_unowned_paged_slots():
+    """Tail slots of each last block and the spare block hold NaN: rows
+    outside the sequence must never reach the output (zero-filled)."""
+    spec = W.Spec("nanpoison", 905, "bf16", 8, 2, 128, ("uniform", 1, 4, 6),
+                  lens_k=("uniform", 70, 500), causal=True, paged=True, block_size=64)
+    case = W.make_case(spec)
+    nan_bits = np.uint16(0x7FC0)
+    bs = case["block_size"]
+    for b in range(case["B"]):
+        L = int(case["seqused_k"][b])
+        nb = (L + bs - 1) // bs
+        last = case["block_table"][b, nb - 1]
+        case["k_cache"][last, L - (nb - 1) * bs:] = nan_bits
+        case["v_cache"][last, L - (nb - 1) * bs:] = nan_bits
+    case["k_cache"][-1] = nan_bits
+    case["v_cache"][-1] = nan_bits
+    _check_full(case, "NaN poison decode")
+    spec2 = W.Spec(**{**spec.__dict__, "lens_q": ("uniform", 30, 60, 4), "name": "nanpoison_prefill"})
+    case2 = W.make_case(spec2)
+    for b in range(case2["B"]):
+        L = int(case2["seqused_k"][b])
+        nb = (L + bs - 1) // bs
+        last = case2["block_table"][b, nb - 1]
+        case2["v_cache"][last, L - (nb - 1) * bs:] = nan_bits
+        case2["k_cache"][last, L - (nb - 1) * bs:] = nan_bits
+    _check_full(case2, "NaN poison prefill")
+
+
+def test_guard_bands_untouched():
+    import variable_length_attention_amd as va
+    case = W.make_case(W.scaled(W.config(4), B=3, max_len=250))
+    announce("guard bands")
+    q, k, v = dev(case["q"], torch), dev(case["k"], torch), dev(case["v"], torch)
+    cq, ck = dev(case["cu_q"], torch), dev(case["cu_k"], torch)
+    sinks = dev(case["sinks"], torch)
+    G = 4096
+    big = torch.full((q.numel() + 2 * G,), 12345.0, dtype=torch.bfloat16, device="cuda")
+    out = big[G:G + q.numel()].view(q.shape)
+    lbig = torch.full((q.shape[0] * q.shape[1] + 2 * G,), -7.0, dtype=torch.float32, device="cuda")
+    lse = lbig[G:G + q.shape[0] * q.shape[1]].view(q.shape[0], q.shape[1])
+    va.varlen_attn_out(out, q, k, v, cq, ck, case["max_q"], case["max_k"], scale=case["scale"],
+                       window=(case["window_left"], case["window_right"]), sinks=sinks, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((big[:G] == 12345.0).all()) and bool((big[G + q.numel():] == 12345.0).all())
+    assert bool((lbig[:G] == -7.0).all()) and bool((lbig[G + lse.numel():] == -7.0).all())
+    ref_o, ref_l = oracle.forward(case)
+    assert_close(case, to_f64(out), to_f64(lse), ref_o, ref_l, "guard")
+
+
+def test_single_key_rows_are_value_rows_bitwise():
+    """Row 0 of a causal sequence has one key: weight exactly 1, so the bf16
+    output equals v_0 bit for bit and LSE equals the score."""
+    spec = W.Spec("onekey", 906, "bf16", 8, 2, 128, ("uniform", 1, 300, 5), causal=True)
+    case = W.make_case(spec)
+    announce("single-key rows")
+    out, lse = run_case(case, torch)
+    o = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    g = case["H"] // case["Hkv"]
+    for b in range(case["B"]):
+        t = int(case["cu_q"][b])
+        for h in range(case["H"]):
+            np.testing.assert_array_equal(o[t, h], case["v"][t, h // g])
+
+
+def test_empty_rows_and_sink_only_rows():
+    """More queries than keys with causal end alignment: leading rows see no
+    key (O = 0, LSE = -inf); with sinks they see only the sink (O = 0,
+    LSE = sigma)."""
+    for paged, sinks in ((False, False), (False, True), (True, True), (True, False)):
+        spec = W.Spec(f"empty{paged}{sinks}", 907, "bf16", 4, 2, 64, ("fixed", [6, 3, 200]),
+                      causal=True, sinks=sinks, paged=paged, block_size=16)
+        case = W.make_case(spec, lens_q=[6, 3, 200], lens_k=[2, 1, 150])
+        out, lse = run_case(case, torch)
+        o, l = to_f64(out), to_f64(lse)
+        ref_o, ref_l = oracle.forward(case)
+        assert_close(case, o, l, ref_o, ref_l, f"empty rows paged={paged} sinks={sinks}")
+        if sinks:
+            assert np.allclose(l[0], case["sinks"], atol=1e-6)
+        else:
+            assert np.all(np.isneginf(l[0:4]))
+        assert np.all(o[0:4] == 0)
+
+
+def test_stress_value_ranges_of_the_ascend_example():
+    """Inputs drawn like the SparseAttnSharedkv usage example (q ~ U(-10,10),
+    kv ~ U(-5,10)) at a reduced sliding-window + sinks shape: near one-hot
+    softmax rows and large scores."""
+    rng = np.random.default_rng(908)
+    lens = [300, 129, 64]
+    T = sum(lens)
+    H, Hkv, D = 16, 1, 128
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q = W.f32_to_bf16_bits(rng.uniform(-10, 10, (T, H, D)).astype(np.float32))
+    k = W.f32_to_bf16_bits(rng.uniform(-5, 10, (T, Hkv, D)).astype(np.float32))
+    v = W.f32_to_bf16_bits(rng.uniform(-5, 10, (T, Hkv, D)).astype(np.float32))
+    case = dict(B=3, H=H, Hkv=Hkv, D=D, dtype="bf16", scale=1 / np.sqrt(D), causal=False,
+                window_left=127, window_right=0, T_q=T, T_k=T, cu_q=cu, cu_k=cu, paged=False,
+                q=q, k=k, v=v, sinks=rng.random(H).astype(np.float32), max_q=300, max_k=300,
+                lens_q=np.asarray(lens), lens_k=np.asarray(lens))
+    out, lse = run_case(case, torch)
+    ref_o, ref_l = oracle.forward(case)
+    # |O| reaches 10 here: bf16 output rounding alone is up to 2^-5 = 0.031, so
+    # compare O relative to the value range and LSE absolutely (|LSE| ~ 1e2,
+    # fp32 ulp ~ 8e-6 there)
+    o = to_f64(out)
+    assert np.max(np.abs(o - ref_o) / np.maximum(1.0, np.abs(ref_o))) <= 2e-2 / 2 + 4e-3
+    assert np.max(np.abs(to_f64(lse) - ref_l)) <= 2e-3
+
+
+# ------------------------------------------------------------------ work partition
+def _plan_cpu(case, mode, bm=128, bn=64):
+    """Independent recomputation of the pre-pass list (deterministic order:
+    cost descending, then item index)."""
+    INF = 1 << 30
+    left = case["window_left"] if case["window_left"] >= 0 else INF
+    right = 0 if case["causal"] else (case["window_right"] if case["window_right"] >= 0 else INF)
+    lens_q = np.diff(case["cu_q"])
+    lens_k = case["seqused_k"] if case.get("paged") else np.diff(case["cu_k"])
+
+    def bounds(i, delta, Lk):
+        p = i + delta
+        lo = 0 if left >= INF else max(0, p - left)
+        hi = Lk - 1 if right >= INF else min(Lk - 1, p + right)
+        return lo, hi
+
+    def rows_range(i0, i1, delta, Lk):
+        lo, _ = bounds(i0, delta, Lk)
+        _, h1 = bounds(i1 - 1, delta, Lk)
+        return lo, max(h1 + 1, lo)
+
+    items = []
+    if mode == "prefill":
+        for b in range(case["B"]):
+            Lq, Lk = int(lens_q[b]), int(lens_k[b])
+            for s in range((Lq + bm - 1) // bm):
+                i0, i1 = s * bm, min(Lq, s * bm + bm)
+                lo, hi = rows_range(i0, i1, Lk - Lq, Lk) if Lk > 0 else (0, 0)
+                items.append(((hi - lo + bn - 1) // bn, (b, i0, lo, hi)))
+    else:
+        vis = []
+        for b in range(case["B"]):
+            Lq, Lk = int(lens_q[b]), int(lens_k[b])
+            vis.append(rows_range(0, Lq, Lk - Lq, Lk) if (Lq > 0 and Lk > 0) else (0, 0))
+        tot = sum(h - l for l, h in vis)
+        want = (tot * case["Hkv"] + 4095) // 4096
+        split = max(256, (want + 255) // 256 * 256)
+        idx = 0
+        for b in range(case["B"]):
+            lo, hi = vis[b]
+            n = max(1, (hi - lo + split - 1) // split)
+            for s in range(n):
+                k_lo = min(hi, lo + s * split)
+                k_hi = min(hi, k_lo + split)
+                items.append(((k_hi - k_lo + 255) // 256, (b, idx, k_lo, k_hi)))
+                idx += 1
+    order = sorted(range(len(items)), key=lambda i: (-min(items[i][0], 4095), i))
+    return np.asarray([items[i][1] for i in order], np.int32).reshape(-1, 4)
+
+
+@pytest.mark.parametrize("which", ["c2", "c4", "c5", "window_decode", "c1_f32"])
+def test_work_partition_bit_exact(which):
+    import variable_length_attention_amd as va
+    if which == "c2":
+        case, mode = W.make_case(W.scaled(W.config(2), B=16, max_len=4096)), "prefill"
+    elif which == "c4":
+        case, mode = W.make_case(W.scaled(W.config(4), B=8, max_len=2000)), "prefill"
+    elif which == "c5":
+        case, mode = W.make_case(W.scaled(W.config(5), B=40, max_len=3000)), "decode"
+    elif which == "window_decode":
+        spec = W.Spec("wd", 909, "bf16", 8, 8, 64, ("uniform", 1, 2, 30), lens_k=("uniform", 0, 5000),
+                      window=(300, 0), paged=False)
+        case, mode = W.make_case(spec), "decode"
+    else:
+        case, mode = W.make_case(W.config(1)), "prefill"
+    announce(f"plan {which}")
+    paged = bool(case.get("paged"))
+    seqlens = dev(case["seqused_k"] if paged else case["cu_k"], torch)
+    dtype = torch.float32 if case["dtype"] == "f32" else torch.bfloat16
+    items, path = va.plan(dev(case["cu_q"], torch), seqlens, num_heads=case["H"], num_kv_heads=case["Hkv"],
+                          head_dim=case["D"], dtype=dtype, total_q=max(1, case["T_q"]),
+                          total_k=max(1, case.get("T_k", 1)), max_seqlen_q=max(1, case["max_q"]),
+                          max_seqlen_k=case["max_k"], causal=case["causal"],
+                          window=(case["window_left"], case["window_right"]), paged=paged,
+                          num_blocks=case.get("num_blocks", 0), block_size=case.get("block_size", 0),
+                          block_table_stride=case["block_table"].shape[1] if paged else 0)
+    assert path == (1 if mode == "decode" else (2 if case["dtype"] == "f32" else 0))
+    bm, bn = (64, 32) if case["dtype"] == "f32" else (128, 64)
+    ref = _plan_cpu(case, mode, bm, bn)
+    np.testing.assert_array_equal(items.cpu().numpy(), ref)

@@ -1,0 +1,13 @@
+"""Variable-length packed attention forward for AMD Instinct MI355X (gfx950).
+
+softmax(Q K^T * scale) V over ragged sequences packed in TND layout and
+delimited by cu_seqlens, with GQA, causal / sliding-window masks, per-head
+sink logits and an optional paged KV cache; writes O into a caller buffer and
+returns the float32 log-sum-exp.  The computation runs in hand-written HIP
+kernels behind the C ABI of include/varlen_attn.h; this package only binds it.
+"""
+from .api import (kernel_path, make_problem, output_shapes, plan, varlen_attn, varlen_attn_fwd,
+                  varlen_attn_out, varlen_attn_paged, workspace_size)
+
+__all__ = ["varlen_attn", "varlen_attn_out", "varlen_attn_paged", "varlen_attn_fwd",
+           "workspace_size", "plan", "kernel_path", "output_shapes", "make_problem"]

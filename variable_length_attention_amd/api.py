@@ -1,0 +1,224 @@
+"""Python binding of the C ABI in include/varlen_attn.h.
+
+Argument marshalling only: tensor shapes become a ``va_problem``, tensor
+storage becomes device pointers, and the current torch stream becomes the
+``hipStream_t``.  Every step of the computation runs in the HIP library.
+PyTorch is used for device memory and streams only.
+
+Entry points (names follow the C ABI and the out-variant API of the pull
+request "[varlen_attn for inference] add out variant"):
+  varlen_attn        allocating: returns out (and lse)
+  varlen_attn_out    writes a caller-provided ``out``; returns lse or None
+  varlen_attn_paged  paged K/V through a block table (SparseAttnSharedkv
+                     README, PageAttention constraints)
+  varlen_attn_fwd    the library-allocating C entry point, results copied
+                     into torch tensors (for ABI tests)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+__all__ = ["varlen_attn", "varlen_attn_out", "varlen_attn_paged", "varlen_attn_fwd",
+           "workspace_size", "plan", "kernel_path", "output_shapes", "make_problem"]
+
+_DTYPES = {torch.float32: _lib.VA_F32, torch.bfloat16: _lib.VA_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def output_shapes(q: torch.Tensor):
+    """Shape inference (the analog of the op's meta function): out has q's
+    shape and dtype, lse is float32 [total_q, num_heads]."""
+    return tuple(q.shape), (q.shape[0], q.shape[1])
+
+
+def make_problem(q, num_kv_heads, total_k, batch, max_seqlen_q, max_seqlen_k, scale, causal,
+                 window, num_blocks=0, block_size=0, block_table_stride=0) -> _lib.VaProblem:
+    _need(q.dim() == 3, "q must be [total_q, num_heads, head_dim]")
+    _need(q.dtype in _DTYPES, f"dtype {q.dtype} not supported (float32 or bfloat16)")
+    p = _lib.VaProblem()
+    p.struct_size = ctypes.sizeof(_lib.VaProblem)
+    p.dtype = _DTYPES[q.dtype]
+    p.batch = int(batch)
+    p.total_q, p.num_heads, p.head_dim = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    p.total_k = int(total_k)
+    p.num_kv_heads = int(num_kv_heads)
+    p.max_seqlen_q, p.max_seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
+    p.scale = float(1.0 / math.sqrt(q.shape[2]) if scale is None else scale)
+    p.causal = 1 if causal else 0
+    p.window_left, p.window_right = int(window[0]), int(window[1])
+    p.num_blocks, p.block_size, p.block_table_stride = int(num_blocks), int(block_size), int(block_table_stride)
+    return p
+
+
+def _check_tensors(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        _need(t.is_cuda, "all tensors must be on a GPU")
+        _need(t.is_contiguous(), "all tensors must be contiguous")
+        dev = dev or t.device
+        _need(t.device == dev, "all tensors must be on the same device")
+    return dev
+
+
+def workspace_size(problem: _lib.VaProblem, paged: bool = False) -> int:
+    return int(_lib.load().varlen_attn_workspace_size(ctypes.byref(problem), 1 if paged else 0))
+
+
+def kernel_path(problem: _lib.VaProblem, paged: bool = False) -> int:
+    """0 = prefill tiles, 1 = split-KV decode + combine, 2 = float32 path."""
+    return int(_lib.load().varlen_attn_path(ctypes.byref(problem), 1 if paged else 0))
+
+
+def _workspace(problem, paged, dev, workspace):
+    need = workspace_size(problem, paged)
+    if need == 0:  # invalid problem: let the call report why
+        return workspace
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    return workspace
+
+
+def varlen_attn_out(out: torch.Tensor, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                    max_seqlen_k: int, *, scale: Optional[float] = None, causal: bool = False,
+                    window: Tuple[int, int] = (-1, -1), sinks=None, lse=None,
+                    return_lse: bool = False, workspace=None):
+    """Writes attention over contiguous packed K/V into ``out``; returns the
+    float32 LSE when ``return_lse`` (or an ``lse`` buffer is given), else None."""
+    dev = _check_tensors(out, q, k, v, cu_seqlens_q, cu_seqlens_k, sinks, lse, workspace)
+    _need(k.dim() == 3 and v.shape == k.shape, "k and v must be [total_k, num_kv_heads, head_dim]")
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32, "cu_seqlens must be int32")
+    _need(out.dtype == q.dtype and k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v, out must share a dtype")
+    _need(out.shape == q.shape, "out must have q's shape")
+    p = make_problem(q, k.shape[1], k.shape[0], cu_seqlens_q.numel() - 1, max_seqlen_q, max_seqlen_k,
+                     scale, causal, window)
+    if return_lse and lse is None:
+        lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=dev)
+    if sinks is not None:
+        _need(sinks.dtype == torch.float32 and sinks.numel() == q.shape[1], "sinks must be float32 [num_heads]")
+    ws = _workspace(p, False, dev, workspace)
+    st = _lib.load().varlen_attn_fwd_out(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(sinks),
+        _ptr(out), _ptr(lse), _ptr(ws), ctypes.c_size_t(0 if ws is None else ws.numel()), _stream(dev))
+    _lib.check(st)
+    return lse
+
+
+def varlen_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, *,
+                scale: Optional[float] = None, causal: bool = False,
+                window: Tuple[int, int] = (-1, -1), sinks=None, return_lse: bool = False):
+    """Allocating form: returns out, or (out, lse) when ``return_lse``."""
+    out = torch.empty_like(q)
+    lse = varlen_attn_out(out, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                          scale=scale, causal=causal, window=window, sinks=sinks,
+                          return_lse=return_lse)
+    return (out, lse) if return_lse else out
+
+
+def varlen_attn_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, max_seqlen_q: int,
+                      max_seqlen_k: int, *, scale: Optional[float] = None, causal: bool = False,
+                      window: Tuple[int, int] = (-1, -1), sinks=None, out=None, lse=None,
+                      return_lse: bool = False, workspace=None):
+    """Paged K/V: caches [num_blocks, block_size, num_kv_heads, head_dim],
+    block_table int32 [batch, stride], seqused_k int32 [batch]."""
+    dev = _check_tensors(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, sinks, out, lse,
+                         workspace)
+    _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape,
+          "caches must be [num_blocks, block_size, num_kv_heads, head_dim]")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2, "block_table must be int32 [batch, stride]")
+    _need(seqused_k.dtype == torch.int32 and cu_seqlens_q.dtype == torch.int32, "seqused_k / cu_seqlens_q must be int32")
+    p = make_problem(q, k_cache.shape[2], 0, cu_seqlens_q.numel() - 1, max_seqlen_q, max_seqlen_k, scale,
+                     causal, window, k_cache.shape[0], k_cache.shape[1], block_table.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=dev)
+    ws = _workspace(p, True, dev, workspace)
+    st = _lib.load().varlen_attn_fwd_paged(
+        ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cu_seqlens_q),
+        _ptr(seqused_k), _ptr(sinks), _ptr(out), _ptr(lse), _ptr(ws),
+        ctypes.c_size_t(0 if ws is None else ws.numel()), _stream(dev))
+    _lib.check(st)
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+_hip = None
+
+
+def _hip_rt():
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                        ctypes.c_void_p]
+        _hip.hipMemcpyAsync.restype = ctypes.c_int
+    return _hip
+
+
+def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, *,
+                    scale=None, causal=False, window=(-1, -1), sinks=None, return_lse=False):
+    """Calls the library-allocating C entry point ``varlen_attn_fwd`` and
+    copies its buffers into torch tensors before releasing them."""
+    dev = _check_tensors(q, k, v, cu_seqlens_q, cu_seqlens_k, sinks)
+    p = make_problem(q, k.shape[1], k.shape[0], cu_seqlens_q.numel() - 1, max_seqlen_q, max_seqlen_k,
+                     scale, causal, window)
+    lib = _lib.load()
+    o_ptr, l_ptr = ctypes.c_void_p(), ctypes.c_void_p()
+    s = _stream(dev)
+    st = lib.varlen_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
+                             _ptr(cu_seqlens_k), _ptr(sinks), ctypes.byref(o_ptr),
+                             ctypes.byref(l_ptr) if return_lse else None, s)
+    _lib.check(st)
+    out = torch.empty_like(q)
+    hip = _hip_rt()
+    D2D = 3
+    rc = hip.hipMemcpyAsync(ctypes.c_void_p(out.data_ptr()), o_ptr, out.numel() * out.element_size(), D2D, s)
+    lse = None
+    if return_lse:
+        lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=dev)
+        rc |= hip.hipMemcpyAsync(ctypes.c_void_p(lse.data_ptr()), l_ptr, lse.numel() * 4, D2D, s)
+        _lib.check(lib.varlen_attn_free(l_ptr, s))
+    _lib.check(lib.varlen_attn_free(o_ptr, s))
+    if rc != 0:
+        raise RuntimeError(f"hipMemcpyAsync failed ({rc})")
+    return (out, lse) if return_lse else out
+
+
+def plan(cu_seqlens_q, seqlens_k, *, num_heads, num_kv_heads, head_dim, dtype, total_q, total_k,
+         max_seqlen_q, max_seqlen_k, causal=False, window=(-1, -1), paged=False, num_blocks=0,
+         block_size=0, block_table_stride=0):
+    """Runs only the work-partition pre-pass; returns (items int32 [n, 4],
+    path) with items in execution order."""
+    dev = _check_tensors(cu_seqlens_q, seqlens_k)
+    fake_q = torch.empty((total_q, num_heads, head_dim), dtype=dtype, device="meta")
+    p = make_problem(fake_q, num_kv_heads, total_k, cu_seqlens_q.numel() - 1, max_seqlen_q, max_seqlen_k,
+                     None, causal, window, num_blocks, block_size, block_table_stride)
+    ws = _workspace(p, paged, dev, None)
+    cap = max(1, ws.numel() // 16)
+    items = torch.empty((cap, 4), dtype=torch.int32, device=dev)
+    count = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = _lib.load().varlen_attn_plan(ctypes.byref(p), 1 if paged else 0, _ptr(cu_seqlens_q),
+                                      _ptr(seqlens_k), _ptr(items), ctypes.c_int32(cap), _ptr(count),
+                                      _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+    _lib.check(st)
+    n = int(count.item())
+    return items[:n].clone(), kernel_path(p, paged)

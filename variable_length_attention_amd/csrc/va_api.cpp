@@ -1,0 +1,401 @@
+// C ABI of the varlen attention library: argument validation, workspace
+// layout, kernel choice and launches on the caller's stream.  No torch here;
+// declarations and contracts are in include/varlen_attn.h.
+//
+// Structure follows the out-variant pull request for PyTorch's varlen
+// attention ("[varlen_attn for inference] add out variant"): one core
+// implementation (`run`) behind an out entry point and an allocating entry
+// point, so the two are bitwise identical.
+#include "../../include/varlen_attn.h"
+#include "va_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+va_status fail(va_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+bool log_enabled()
+{
+    static const bool on = [] {
+        const char *e = std::getenv("VARLEN_ATTN_LOG");
+        return e && e[0] == '1';
+    }();
+    return on;
+}
+
+enum Path { kPathPrefill = 0, kPathDecode = 1, kPathF32 = 2 };
+
+struct Layout {
+    int path = -1;
+    int n_max = 0;
+    int bm = 0, bn = 0;
+    long long grid = 0;
+    size_t off_count = 0, off_seq = 0, off_unsorted = 0, off_cost = 0, off_items = 0;
+    size_t off_part_ml = 0, off_part_o = 0, total = 0;
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Validation of the problem description alone (no pointers).
+va_status check_problem(const va_problem *p, int paged)
+{
+    if (!p) return fail(VA_ERR_NULL, "problem descriptor is NULL");
+    if (p->struct_size < sizeof(va_problem))
+        return fail(VA_ERR_SHAPE, "va_problem.struct_size %u is smaller than %zu", p->struct_size,
+                    sizeof(va_problem));
+    if (p->dtype != VA_F32 && p->dtype != VA_BF16)
+        return fail(VA_ERR_DTYPE, "dtype %d is not VA_F32 (0) or VA_BF16 (1)", p->dtype);
+    if (p->batch < 1) return fail(VA_ERR_SHAPE, "batch %d < 1", p->batch);
+    if (p->total_q < 1) return fail(VA_ERR_SHAPE, "total_q %d < 1 (empty tensors are not accepted)", p->total_q);
+    if (!paged && p->total_k < 1)
+        return fail(VA_ERR_SHAPE, "total_k %d < 1 (empty tensors are not accepted)", p->total_k);
+    if (p->num_heads < 1 || p->num_kv_heads < 1)
+        return fail(VA_ERR_SHAPE, "num_heads %d / num_kv_heads %d must be >= 1", p->num_heads, p->num_kv_heads);
+    if (p->num_heads % p->num_kv_heads != 0)
+        return fail(VA_ERR_SHAPE, "num_heads %d is not a multiple of num_kv_heads %d", p->num_heads,
+                    p->num_kv_heads);
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return fail(VA_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", p->head_dim);
+    if (p->max_seqlen_q < 1 || p->max_seqlen_q > va::kMaxSeqlen)
+        return fail(VA_ERR_SHAPE, "max_seqlen_q %d outside [1, %d]", p->max_seqlen_q, va::kMaxSeqlen);
+    if (p->max_seqlen_k < 0 || p->max_seqlen_k > va::kMaxSeqlen)
+        return fail(VA_ERR_SHAPE, "max_seqlen_k %d outside [0, %d]", p->max_seqlen_k, va::kMaxSeqlen);
+    if (!std::isfinite(p->scale)) return fail(VA_ERR_UNSUPPORTED, "scale is not finite");
+    if (p->causal != 0 && p->causal != 1) return fail(VA_ERR_UNSUPPORTED, "causal must be 0 or 1");
+    if (p->window_left < -1 || p->window_right < -1)
+        return fail(VA_ERR_UNSUPPORTED, "window (%d, %d): values below -1 are not defined", p->window_left,
+                    p->window_right);
+    if (paged) {
+        if (p->num_blocks < 1) return fail(VA_ERR_SHAPE, "num_blocks %d < 1", p->num_blocks);
+        if (p->block_size < 16 || p->block_size > 1024 || p->block_size % 16 != 0)
+            return fail(VA_ERR_UNSUPPORTED, "block_size %d is not a multiple of 16 in [16, 1024]", p->block_size);
+        const long long need = ((long long)p->max_seqlen_k + p->block_size - 1) / p->block_size;
+        if (p->block_table_stride < 1 || p->block_table_stride < need)
+            return fail(VA_ERR_SHAPE, "block_table_stride %d < ceil(max_seqlen_k / block_size) = %lld",
+                        p->block_table_stride, need);
+    }
+    return VA_OK;
+}
+
+va_status make_layout(const va_problem *p, int paged, Layout &L)
+{
+    const int g = p->num_heads / p->num_kv_heads;
+    if (p->dtype == VA_F32) {
+        L.path = kPathF32;
+        L.bm = va::kBMf32;
+        L.bn = va::kBNf32;
+    } else if ((long long)g * p->max_seqlen_q <= va::kDecRows) {
+        L.path = kPathDecode;
+    } else {
+        L.path = kPathPrefill;
+        L.bm = va::kBM;
+        L.bn = va::kBN;
+    }
+    long long n_max;
+    if (L.path == kPathDecode) {
+        n_max = va::kDecTargetUnits / p->num_kv_heads + (long long)p->batch + 1;
+        L.grid = n_max * p->num_kv_heads;
+    } else {
+        n_max = ((long long)p->total_q + (long long)p->batch * (L.bm - 1)) / L.bm;
+        L.grid = n_max * p->num_heads;
+    }
+    if (L.grid > 0x7fffffffLL || n_max > 0x7fffffffLL)
+        return fail(VA_ERR_UNSUPPORTED, "problem needs %lld workgroups, above the launch limit", L.grid);
+    L.n_max = (int)n_max;
+    size_t off = 0;
+    L.off_count = off; off = align_up(off + 4, 256);
+    L.off_seq = off; off = align_up(off + 4 * ((size_t)p->batch + 1), 256);
+    L.off_unsorted = off; off = align_up(off + 16 * (size_t)n_max, 256);
+    L.off_cost = off; off = align_up(off + 4 * (size_t)n_max, 256);
+    L.off_items = off; off = align_up(off + 16 * (size_t)n_max, 256);
+    if (L.path == kPathDecode) {
+        const size_t rows = (size_t)n_max * p->num_kv_heads * va::kDecRows;
+        L.off_part_ml = off; off = align_up(off + 8 * rows, 256);
+        L.off_part_o = off; off = align_up(off + 4 * rows * p->head_dim, 256);
+    }
+    L.total = off;
+    return VA_OK;
+}
+
+struct Range {
+    const void *p;
+    size_t bytes;
+};
+
+bool overlaps(const Range &a, const Range &b)
+{
+    if (!a.p || !b.p || !a.bytes || !b.bytes) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Call {
+    const va_problem *p;
+    int paged;
+    const void *q, *k, *v;
+    const int32_t *cu_q, *cu_k, *seqused_k, *block_table;
+    const float *sinks;
+    void *out;
+    float *lse;
+    void *ws;
+    size_t ws_bytes;
+};
+
+va_status check_pointers(const Call &c, const Layout &L)
+{
+    const va_problem *p = c.p;
+    if (!c.q || !c.k || !c.v) return fail(VA_ERR_NULL, "q, k and v must be non-NULL");
+    if (!c.cu_q) return fail(VA_ERR_NULL, "cu_seqlens_q must be non-NULL");
+    if (c.paged) {
+        if (!c.block_table || !c.seqused_k) return fail(VA_ERR_NULL, "block_table and seqused_k must be non-NULL");
+    } else if (!c.cu_k) {
+        return fail(VA_ERR_NULL, "cu_seqlens_k must be non-NULL");
+    }
+    if (!c.out) return fail(VA_ERR_NULL, "out must be non-NULL");
+    if (L.total > 0 && !c.ws) return fail(VA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
+    if (c.ws_bytes < L.total)
+        return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", c.ws_bytes, L.total);
+    if (!aligned(c.q, 16) || !aligned(c.k, 16) || !aligned(c.v, 16) || !aligned(c.out, 16) ||
+        (c.ws && !aligned(c.ws, 16)))
+        return fail(VA_ERR_ALIGN, "q, k, v, out and workspace must be 16-byte aligned");
+    if (!aligned(c.cu_q, 4) || (c.cu_k && !aligned(c.cu_k, 4)) || (c.seqused_k && !aligned(c.seqused_k, 4)) ||
+        (c.block_table && !aligned(c.block_table, 4)) || (c.sinks && !aligned(c.sinks, 4)) ||
+        (c.lse && !aligned(c.lse, 4)))
+        return fail(VA_ERR_ALIGN, "int32 / float32 arrays must be 4-byte aligned");
+
+    const size_t es = p->dtype == VA_BF16 ? 2 : 4;
+    const size_t D = (size_t)p->head_dim;
+    const size_t kv_rows = c.paged ? (size_t)p->num_blocks * p->block_size : (size_t)p->total_k;
+    const Range out{c.out, (size_t)p->total_q * p->num_heads * D * es};
+    const Range lse{c.lse, c.lse ? (size_t)p->total_q * p->num_heads * 4 : 0};
+    const Range ins[] = {
+        {c.q, (size_t)p->total_q * p->num_heads * D * es},
+        {c.k, kv_rows * p->num_kv_heads * D * es},
+        {c.v, kv_rows * p->num_kv_heads * D * es},
+        {c.cu_q, 4 * ((size_t)p->batch + 1)},
+        {c.cu_k, c.cu_k ? 4 * ((size_t)p->batch + 1) : 0},
+        {c.seqused_k, c.seqused_k ? 4 * (size_t)p->batch : 0},
+        {c.block_table, c.block_table ? 4 * (size_t)p->batch * p->block_table_stride : 0},
+        {c.sinks, c.sinks ? 4 * (size_t)p->num_heads : 0},
+        {c.ws, c.ws_bytes},
+    };
+    for (const Range &r : ins) {
+        if (overlaps(out, r)) return fail(VA_ERR_ALIAS, "out overlaps an input, the workspace or lse");
+        if (overlaps(lse, r)) return fail(VA_ERR_ALIAS, "lse overlaps an input or the workspace");
+    }
+    if (overlaps(out, lse)) return fail(VA_ERR_ALIAS, "out overlaps lse");
+    return VA_OK;
+}
+
+va::AttnArgs make_args(const Call &c)
+{
+    const va_problem *p = c.p;
+    va::AttnArgs a;
+    a.q = c.q; a.k = c.k; a.v = c.v;
+    a.out = c.out; a.lse = c.lse;
+    a.cu_q = c.cu_q; a.cu_k = c.cu_k; a.seqused_k = c.seqused_k; a.block_table = c.block_table;
+    a.sinks = c.sinks;
+    a.B = p->batch; a.H = p->num_heads; a.Hkv = p->num_kv_heads; a.g = p->num_heads / p->num_kv_heads;
+    a.bt_stride = c.paged ? p->block_table_stride : 0;
+    a.block_size = c.paged ? p->block_size : 1;
+    a.left = p->window_left >= 0 ? p->window_left : va::kInfOff;
+    // causal caps the right side at the query position: min(window_right, 0)
+    // with window_right >= -1 and -1 meaning unbounded is always 0
+    if (p->causal) a.right = 0;
+    else a.right = p->window_right >= 0 ? p->window_right : va::kInfOff;
+    a.scale = p->scale;
+    a.scale_log2 = p->scale * va::kLog2e;
+    return a;
+}
+
+va::PlanArgs make_plan(const Call &c, const Layout &L, const va::AttnArgs &a)
+{
+    char *ws = (char *)c.ws;
+    va::PlanArgs pa;
+    pa.cu_q = c.cu_q;
+    pa.lens_k = c.paged ? c.seqused_k : c.cu_k;
+    pa.lens_k_is_prefix = c.paged ? 0 : 1;
+    pa.B = a.B; pa.Hkv = a.Hkv;
+    pa.left = a.left; pa.right = a.right;
+    pa.mode = L.path == kPathDecode ? va::kPlanDecode : va::kPlanPrefill;
+    pa.bm = L.bm; pa.bn = L.bn;
+    pa.n_max = L.n_max;
+    pa.count = (int32_t *)(ws + L.off_count);
+    pa.seq_off = (int32_t *)(ws + L.off_seq);
+    pa.unsorted = (int4 *)(ws + L.off_unsorted);
+    pa.cost = (int32_t *)(ws + L.off_cost);
+    pa.items = (int4 *)(ws + L.off_items);
+    return pa;
+}
+
+// The one implementation behind every entry point.
+va_status run(const Call &c, hipStream_t s)
+{
+    va_status st = check_problem(c.p, c.paged);
+    if (st) return st;
+    Layout L;
+    if ((st = make_layout(c.p, c.paged, L))) return st;
+    if ((st = check_pointers(c, L))) return st;
+    const va::AttnArgs a = make_args(c);
+    const va::PlanArgs pa = make_plan(c, L, a);
+    if (log_enabled())
+        fprintf(stderr, "[varlen_attn] path=%s D=%d paged=%d B=%d H=%d Hkv=%d total_q=%d grid=%lld ws=%zu\n",
+                L.path == kPathPrefill ? "prefill_bf16" : L.path == kPathDecode ? "decode_bf16" : "f32",
+                c.p->head_dim, c.paged, a.B, a.H, a.Hkv, c.p->total_q, L.grid, L.total);
+    hipError_t e = va::launch_plan(pa, s);
+    if (e == hipSuccess) {
+        if (L.path == kPathPrefill)
+            e = va::launch_prefill_bf16(a, c.p->head_dim, c.paged, pa.items, pa.count, (int)L.grid, s);
+        else if (L.path == kPathF32)
+            e = va::launch_prefill_f32(a, c.p->head_dim, c.paged, pa.items, pa.count, (int)L.grid, s);
+        else {
+            char *ws = (char *)c.ws;
+            float *po = (float *)(ws + L.off_part_o);
+            float2 *pml = (float2 *)(ws + L.off_part_ml);
+            e = va::launch_decode_bf16(a, c.p->head_dim, c.paged, pa.items, pa.count, (int)L.grid, po, pml, s);
+            if (e == hipSuccess) e = va::launch_decode_combine(a, c.p->head_dim, pa.seq_off, po, pml, s);
+        }
+    }
+    if (e != hipSuccess) return fail(VA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return VA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int varlen_attn_abi_version(void) { return VARLEN_ATTN_ABI_VERSION; }
+
+const char *varlen_attn_last_error(void) { return g_last_error.c_str(); }
+
+size_t varlen_attn_workspace_size(const va_problem *p, int paged)
+{
+    if (check_problem(p, paged != 0)) return 0;
+    Layout L;
+    if (make_layout(p, paged != 0, L)) return 0;
+    return L.total;
+}
+
+int varlen_attn_path(const va_problem *p, int paged)
+{
+    if (check_problem(p, paged != 0)) return -1;
+    Layout L;
+    if (make_layout(p, paged != 0, L)) return -1;
+    return L.path;
+}
+
+va_status varlen_attn_fwd_out(const va_problem *p, const void *q, const void *k, const void *v,
+                              const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                              const float *sinks, void *out, float *lse, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    Call c{p, 0, q, k, v, cu_seqlens_q, cu_seqlens_k, nullptr, nullptr, sinks, out, lse, workspace,
+           workspace_bytes};
+    return run(c, (hipStream_t)stream);
+}
+
+va_status varlen_attn_fwd_paged(const va_problem *p, const void *q, const void *k_cache,
+                                const void *v_cache, const int32_t *block_table,
+                                const int32_t *cu_seqlens_q, const int32_t *seqused_k,
+                                const float *sinks, void *out, float *lse, void *workspace,
+                                size_t workspace_bytes, void *stream)
+{
+    Call c{p, 1, q, k_cache, v_cache, cu_seqlens_q, nullptr, seqused_k, block_table, sinks, out, lse,
+           workspace, workspace_bytes};
+    return run(c, (hipStream_t)stream);
+}
+
+va_status varlen_attn_fwd(const va_problem *p, const void *q, const void *k, const void *v,
+                          const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, const float *sinks,
+                          void **out, float **lse, void *stream)
+{
+    if (!out) return fail(VA_ERR_NULL, "out (the address receiving the allocation) is NULL");
+    *out = nullptr;
+    if (lse) *lse = nullptr;
+    va_status st = check_problem(p, 0);
+    if (st) return st;
+    Layout L;
+    if ((st = make_layout(p, 0, L))) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const size_t es = p->dtype == VA_BF16 ? 2 : 4;
+    const size_t out_bytes = (size_t)p->total_q * p->num_heads * p->head_dim * es;
+    const size_t lse_bytes = (size_t)p->total_q * p->num_heads * 4;
+    void *o = nullptr, *l = nullptr, *w = nullptr;
+    if (hipMallocAsync(&o, out_bytes, s) != hipSuccess ||
+        (lse && hipMallocAsync(&l, lse_bytes, s) != hipSuccess) ||
+        hipMallocAsync(&w, L.total, s) != hipSuccess) {
+        if (o) (void)hipFreeAsync(o, s);
+        if (l) (void)hipFreeAsync(l, s);
+        if (w) (void)hipFreeAsync(w, s);
+        return fail(VA_ERR_HIP, "stream-ordered allocation failed");
+    }
+    Call c{p, 0, q, k, v, cu_seqlens_q, cu_seqlens_k, nullptr, nullptr, sinks, o, (float *)l, w, L.total};
+    st = run(c, s);
+    (void)hipFreeAsync(w, s);
+    if (st) {
+        (void)hipFreeAsync(o, s);
+        if (l) (void)hipFreeAsync(l, s);
+        return st;
+    }
+    *out = o;
+    if (lse) *lse = (float *)l;
+    return VA_OK;
+}
+
+va_status varlen_attn_free(void *ptr, void *stream)
+{
+    if (!ptr) return VA_OK;
+    hipError_t e = hipFreeAsync(ptr, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(VA_ERR_HIP, "hipFreeAsync failed: %s", hipGetErrorString(e));
+    return VA_OK;
+}
+
+va_status varlen_attn_plan(const va_problem *p, int paged, const int32_t *cu_seqlens_q,
+                           const int32_t *seqlens_k, int32_t *items, int32_t capacity, int32_t *count,
+                           void *workspace, size_t workspace_bytes, void *stream)
+{
+    va_status st = check_problem(p, paged != 0);
+    if (st) return st;
+    Layout L;
+    if ((st = make_layout(p, paged != 0, L))) return st;
+    if (!cu_seqlens_q || !seqlens_k)
+        return fail(VA_ERR_NULL, "cu_seqlens_q and seqlens_k must be non-NULL");
+    if ((capacity > 0 && !items) || (capacity > 0 && !count))
+        return fail(VA_ERR_NULL, "items and count must be non-NULL when capacity > 0");
+    if (!workspace || workspace_bytes < L.total)
+        return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                    workspace_bytes, L.total);
+    if (capacity < 0) return fail(VA_ERR_SHAPE, "capacity %d < 0", capacity);
+    Call c{p, paged != 0, nullptr, nullptr, nullptr, cu_seqlens_q, paged ? nullptr : seqlens_k,
+           paged ? seqlens_k : nullptr, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes};
+    const va::AttnArgs a = make_args(c);
+    const va::PlanArgs pa = make_plan(c, L, a);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = va::launch_plan(pa, s);
+    const size_t n = (size_t)(capacity < L.n_max ? capacity : L.n_max);
+    if (e == hipSuccess && n) e = hipMemcpyAsync(items, pa.items, n * 16, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && count) e = hipMemcpyAsync(count, pa.count, 4, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return fail(VA_ERR_HIP, "plan failed: %s", hipGetErrorString(e));
+    return VA_OK;
+}
+
+}  // extern "C"

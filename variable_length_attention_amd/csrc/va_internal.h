@@ -1,0 +1,103 @@
+// Internal declarations shared by the HIP sources of the varlen attention
+// library (kernels, work-partition pre-pass, host launcher).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace va {
+
+// ---------------------------------------------------------------- constants
+constexpr int kInfOff = 1 << 30;       // "unbounded" window offset
+constexpr int kMaxSeqlen = 1 << 29;    // keeps i + delta +- offsets inside int32
+constexpr int kBM = 128;               // bf16 prefill: query rows per workgroup
+constexpr int kBN = 64;                // bf16 prefill: key rows per tile
+constexpr int kBMf32 = 64;             // float32 path: query rows per workgroup
+constexpr int kBNf32 = 32;             // float32 path: key rows per tile
+constexpr int kDecRows = 16;           // decode: packed (head, query) rows per kv head
+constexpr int kDecChunk = 64;          // decode: keys per wave step
+constexpr int kDecQuantum = 256;       // decode: split sizes are multiples of this
+constexpr int kDecTargetUnits = 4096;  // decode: aim for about this many (split, kv head) units
+constexpr int kPlanThreads = 256;
+constexpr int kCostBins = 4096;        // counting-sort bins of the pre-pass
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- kernel arguments
+struct AttnArgs {
+    const void *q, *k, *v;
+    void *out;
+    float *lse;                  // may be null
+    const int32_t *cu_q;         // [B+1]
+    const int32_t *cu_k;         // [B+1] contiguous mode
+    const int32_t *seqused_k;    // [B]   paged mode
+    const int32_t *block_table;  // [B, bt_stride] paged mode
+    const float *sinks;          // [H] or null
+    int32_t B, H, Hkv, g;
+    int32_t bt_stride, block_size;
+    int32_t left, right;         // visible keys of query position p: [p-left, p+right]
+    float scale, scale_log2;     // scale and scale * log2(e)
+};
+
+enum PlanMode : int32_t { kPlanPrefill = 0, kPlanDecode = 1 };
+
+struct PlanArgs {
+    const int32_t *cu_q;
+    const int32_t *lens_k;       // cu_k (prefix sums) or seqused_k (counts)
+    int32_t lens_k_is_prefix;    // 1: cu_k, 0: seqused_k
+    int32_t B, Hkv;
+    int32_t left, right;
+    int32_t mode;                // PlanMode
+    int32_t bm;                  // prefill: rows per item
+    int32_t bn;                  // prefill: key rows per tile (cost unit)
+    int32_t n_max;               // capacity of the item arrays
+    int32_t *count;              // [1] number of items written
+    int32_t *seq_off;            // [B+1] first item (prefill) / first split slot (decode)
+    int4 *unsorted;              // [n_max]
+    int32_t *cost;               // [n_max]
+    int4 *items;                 // [n_max] sorted, execution order
+};
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_plan(const PlanArgs &pa, hipStream_t s);
+hipError_t launch_prefill_bf16(const AttnArgs &a, int head_dim, bool paged, const int4 *items,
+                               const int32_t *count, int grid, hipStream_t s);
+hipError_t launch_prefill_f32(const AttnArgs &a, int head_dim, bool paged, const int4 *items,
+                              const int32_t *count, int grid, hipStream_t s);
+hipError_t launch_decode_bf16(const AttnArgs &a, int head_dim, bool paged, const int4 *items,
+                              const int32_t *count, int grid, float *part_o, float2 *part_ml,
+                              hipStream_t s);
+hipError_t launch_decode_combine(const AttnArgs &a, int head_dim, const int32_t *seq_off,
+                                 const float *part_o, const float2 *part_ml, hipStream_t s);
+
+// ---------------------------------------------------------------- device helpers
+#if defined(__HIPCC__)
+// Visible keys [lo, hi] (inclusive, clipped to [0, Lk-1]) of query row i.
+__device__ __forceinline__ void row_bounds(int i, int delta, int Lk, int left, int right,
+                                           int &lo, int &hi)
+{
+    const int p = i + delta;
+    lo = left >= kInfOff ? 0 : max(0, p - left);
+    hi = right >= kInfOff ? Lk - 1 : min(Lk - 1, p + right);
+}
+
+// Workgroup -> (work item, head) with heads grouped per XCD: consecutive
+// workgroup ids are dealt round-robin to the 8 XCDs, so giving each XCD a
+// contiguous range of heads keeps one GQA group's K/V in one L2.
+__device__ __forceinline__ void map_block(int bid, int nheads, int &item, int &head)
+{
+    if ((nheads & 7) == 0) {
+        const int hpx = nheads >> 3;
+        const int x = bid & 7, r = bid >> 3;
+        item = r / hpx;
+        head = x * hpx + r % hpx;
+    } else {
+        item = bid / nheads;
+        head = bid % nheads;
+    }
+}
+#endif
+
+}  // namespace va

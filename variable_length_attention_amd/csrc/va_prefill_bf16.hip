@@ -1,0 +1,284 @@
+// bf16 prefill forward on gfx950 matrix cores.
+//
+// One workgroup = 4 waves = 128 query rows of one head (32 rows per wave);
+// key/value tiles of 64 rows are staged in LDS (double buffered, one barrier
+// per tile) and shared by the 4 waves.  Per wave and tile:
+//   S^T = K * Q^T      8 (D=128) x 2 MFMA 32x32x16 bf16, fp32 accumulate.
+//                      With keys on the MFMA M side, each lane ends up owning
+//                      one query row: the row max needs one cross-lane step
+//                      (lanes l and l^32) and the row sum none until the end.
+//   scale, mask, online softmax in fp32 registers (exp2 domain);
+//   O^T += V^T * P^T   4 x 4 MFMA 32x32x16; V^T operands come straight from
+//                      the row-major V tile through the transposing LDS read
+//                      ds_read_b64_tr_b16, P^T straight from the S^T
+//                      accumulators (same lane, same key order).
+// Tiles a wave cannot see are skipped; masks are evaluated only on tiles
+// that straddle a mask edge.
+//
+// Method: the online-softmax form of softmax(Q K^T * scale) V
+// (SparseAttnSharedkv README, formula section); it reaches the same value as
+// the three-pass row softmax of the boostr CPU forward up to rounding.  The
+// sink logit enters as the initial running max / sum (a key with a zero
+// value row); the returned LSE is max + ln(sum) as in that CPU forward.
+#include "va_internal.h"
+
+namespace va {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)((__attribute__((address_space(3))) uint16_t *)(p)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int D, bool PAGED>
+__global__ __launch_bounds__(256) void k1_prefill_bf16(AttnArgs a, const int4 *__restrict__ items,
+                                                       const int32_t *__restrict__ count)
+{
+    constexpr int BN = kBN;
+    constexpr int NCH = D / 8;         // 16-byte chunks per row
+    constexpr int NSEG = NCH / 4;      // 64-byte segments per row
+    constexpr int KS = D / 16;         // QK^T k-steps
+    constexpr int MD = D / 32;         // 32-wide blocks of the head dimension
+    constexpr int RSTEP = 256 / NCH;   // rows covered by one loader pass
+    constexpr int LPT = BN / RSTEP;    // loader passes per tile
+    constexpr int TILE = BN * D;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];  // K0 V0 K1 V1
+
+    int item, head;
+    map_block(blockIdx.x, a.H, item, head);
+    if (item >= *count) return;
+    const int4 it = items[item];
+    const int b = it.x, i0 = it.y, kv_lo = it.z, kv_hi = it.w;
+    const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
+    const int Lk = PAGED ? a.seqused_k[b] : a.cu_k[b + 1] - a.cu_k[b];
+    const int k0 = PAGED ? 0 : a.cu_k[b];
+    const int delta = Lk - Lq;
+    const int c = head / a.g;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, h2 = lane >> 5, l16 = lane & 15;
+    const int row = i0 + wave * 32 + n;
+    const bool row_ok = row < Lq;
+    int lo = 1, hi = 0;
+    if (row_ok) row_bounds(row, delta, Lk, a.left, a.right, lo, hi);
+
+    // keys this wave can see (wlo..whi) and keys all its rows see (flo..fhi)
+    int wlo = 1, whi = 0, flo = 0x7fffffff, fhi = -1;
+    {
+        const int w0 = i0 + wave * 32, w1 = min(w0 + 31, Lq - 1);
+        if (w0 < Lq) {
+            int l0, h0, l1, h1;
+            row_bounds(w0, delta, Lk, a.left, a.right, l0, h0);
+            row_bounds(w1, delta, Lk, a.left, a.right, l1, h1);
+            wlo = l0; whi = h1; flo = l1; fhi = h0;
+        }
+    }
+
+    // Q^T operand fragments: lane (row n, half h2) holds d = 16 ks + 8 h2 .. +8
+    bf16x8 qf[KS];
+    {
+        const uint16_t *qp = (const uint16_t *)a.q + ((size_t)(q0 + (row_ok ? row : 0)) * a.H + head) * D + h2 * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 x = row_ok ? *(const u32x4 *)(qp + ks * 16) : u32x4{0, 0, 0, 0};
+            qf[ks] = __builtin_bit_cast(bf16x8, x);
+        }
+    }
+
+    f32x16 o[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[md][v] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    if (a.sinks) {
+        m_run = a.sinks[head] * kLog2e;
+        l_run = h2 == 0 ? 1.f : 0.f;
+    }
+
+    const uint16_t *kbase = (const uint16_t *)a.k;
+    const uint16_t *vbase = (const uint16_t *)a.v;
+    const int cc = tid % NCH, r_first = tid / NCH;
+    u32x4 kr[LPT], vr[LPT];
+
+    auto gload = [&](int t) {
+        const int j0 = kv_lo + t * BN;
+#pragma unroll
+        for (int u = 0; u < LPT; ++u) {
+            const int j = j0 + r_first + u * RSTEP;
+            if (j < kv_hi) {
+                size_t off;
+                if (PAGED) {
+                    const int blk = a.block_table[(size_t)b * a.bt_stride + j / a.block_size];
+                    off = (((size_t)blk * a.block_size + j % a.block_size) * a.Hkv + c) * D;
+                } else {
+                    off = ((size_t)(k0 + j) * a.Hkv + c) * D;
+                }
+                off += cc * 8;
+                kr[u] = *(const u32x4 *)(kbase + off);
+                vr[u] = *(const u32x4 *)(vbase + off);
+            } else {
+                kr[u] = u32x4{0, 0, 0, 0};
+                vr[u] = u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    // K rows: chunk index XOR (row mod NCH) -> 16 consecutive rows of one
+    // chunk column hit 16 different chunks (conflict-free MFMA operand reads).
+    // V rows: 64-byte segment XOR (row mod NSEG) -> the 8 rows of one
+    // transposing read spread over all segments.
+    auto sstore = [&](int buf) {
+        uint16_t *sk = smem + buf * 2 * TILE;
+        uint16_t *sv = sk + TILE;
+#pragma unroll
+        for (int u = 0; u < LPT; ++u) {
+            const int r = r_first + u * RSTEP;
+            *(u32x4 *)(sk + r * D + ((cc ^ (r % NCH)) << 3)) = kr[u];
+            *(u32x4 *)(sv + r * D + ((cc ^ ((r % NSEG) << 2)) << 3)) = vr[u];
+        }
+    };
+
+    const int ntiles = (kv_hi - kv_lo + BN - 1) / BN;
+    if (ntiles > 0) {
+        gload(0);
+        sstore(0);
+        if (ntiles > 1) gload(1);
+    }
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int j0 = kv_lo + t * BN;
+        const uint16_t *sk = smem + (t & 1) * 2 * TILE;
+        const uint16_t *sv = sk + TILE;
+        if (j0 <= whi && j0 + BN - 1 >= wlo) {
+            f32x16 s[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) s[mb][v] = 0.f;
+                const int r = mb * 32 + n;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 kf = *(const bf16x8 *)(sk + r * D + (((ks * 2 + h2) ^ (r % NCH)) << 3));
+                    s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mb], 0, 0, 0);
+                }
+            }
+            // lane value v of block mb is key j0 + 32 mb + 8 (v/4) + 4 h2 + v%4
+            float mx = -INFINITY;
+            if (j0 >= flo && j0 + BN - 1 <= fhi) {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        s[mb][v] *= a.scale_log2;
+                        mx = fmaxf(mx, s[mb][v]);
+                    }
+            } else {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int j = j0 + mb * 32 + (v >> 2) * 8 + h2 * 4 + (v & 3);
+                        const float x = (j >= lo && j <= hi) ? s[mb][v] * a.scale_log2 : -INFINITY;
+                        s[mb][v] = x;
+                        mx = fmaxf(mx, x);
+                    }
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = fast_exp2(m_run - m_use);
+            float rs = 0.f;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float p = fast_exp2(s[mb][v] - m_use);
+                    s[mb][v] = p;
+                    rs += p;
+                }
+            l_run = l_run * alpha + rs;
+            m_run = m_new;
+#pragma unroll
+            for (int md = 0; md < MD; ++md)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
+
+            // O^T += V^T P^T over 4 steps of 16 keys
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4) {
+                const int mb = t4 >> 1, ib = (t4 & 1) * 2;
+                f32x8 pv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pv[e] = s[mb][ib * 4 + e];
+                const bf16x8 pf = __builtin_convertvector(pv, bf16x8);
+                const int rA = t4 * 16 + h2 * 4 + (l16 >> 2);
+                const int rB = rA + 8;
+#pragma unroll
+                for (int md = 0; md < MD; ++md) {
+                    const int col = md * 32 + ((lane & 31) >> 4) * 16 + (l16 & 3) * 4;
+                    const int segA = (col >> 3) ^ ((rA % NSEG) << 2);
+                    const int segB = (col >> 3) ^ ((rB % NSEG) << 2);
+                    const bf16x4 va = lds_read_tr(sv + rA * D + (segA << 3) + (col & 7));
+                    const bf16x4 vb = lds_read_tr(sv + rB * D + (segB << 3) + (col & 7));
+                    const bf16x8 vf = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+                    o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[md], 0, 0, 0);
+                }
+            }
+        }
+        if (t + 1 < ntiles) sstore((t + 1) & 1);
+        if (t + 2 < ntiles) gload(t + 2);
+        __syncthreads();
+    }
+
+    // epilogue: lane (row n, half h2) holds O[row][32 md + 8 i + 4 h2 + j]
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (row_ok) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        uint16_t *op = (uint16_t *)a.out + ((size_t)(q0 + row) * a.H + head) * D + h2 * 4;
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4 x;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] = o[md][i * 4 + j] * inv;
+                const bf16x4 y = __builtin_convertvector(x, bf16x4);
+                *(u32x2 *)(op + md * 32 + i * 8) = __builtin_bit_cast(u32x2, y);
+            }
+        if (h2 == 0 && a.lse)
+            a.lse[(size_t)(q0 + row) * a.H + head] =
+                l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const AttnArgs &a, int head_dim, bool paged, const int4 *items,
+                               const int32_t *count, int grid, hipStream_t s)
+{
+    const dim3 g(grid), blk(256);
+    if (head_dim == 128) {
+        if (paged) hipLaunchKernelGGL((k1_prefill_bf16<128, true>), g, blk, 0, s, a, items, count);
+        else hipLaunchKernelGGL((k1_prefill_bf16<128, false>), g, blk, 0, s, a, items, count);
+    } else {
+        if (paged) hipLaunchKernelGGL((k1_prefill_bf16<64, true>), g, blk, 0, s, a, items, count);
+        else hipLaunchKernelGGL((k1_prefill_bf16<64, false>), g, blk, 0, s, a, items, count);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace va
