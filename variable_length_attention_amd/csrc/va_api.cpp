@@ -77,7 +77,8 @@ va_status check_problem(const va_problem *p, int paged)
         return fail(VA_ERR_SHAPE, "max_seqlen_q %d outside [1, %d]", p->max_seqlen_q, va::kMaxSeqlen);
     if (p->max_seqlen_k < 0 || p->max_seqlen_k > va::kMaxSeqlen)
         return fail(VA_ERR_SHAPE, "max_seqlen_k %d outside [0, %d]", p->max_seqlen_k, va::kMaxSeqlen);
-    if (!std::isfinite(p->scale)) return fail(VA_ERR_UNSUPPORTED, "scale is not finite");
+    if (!std::isfinite(p->scale) || !(p->scale > 0.f))
+        return fail(VA_ERR_UNSUPPORTED, "scale must be finite and > 0");
     if (p->causal != 0 && p->causal != 1) return fail(VA_ERR_UNSUPPORTED, "causal must be 0 or 1");
     if (p->window_left < -1 || p->window_right < -1)
         return fail(VA_ERR_UNSUPPORTED, "window (%d, %d): values below -1 are not defined", p->window_left,
@@ -217,6 +218,9 @@ va::AttnArgs make_args(const Call &c)
     a.B = p->batch; a.H = p->num_heads; a.Hkv = p->num_kv_heads; a.g = p->num_heads / p->num_kv_heads;
     a.bt_stride = c.paged ? p->block_table_stride : 0;
     a.block_size = c.paged ? p->block_size : 1;
+    a.bs_shift = -1;
+    for (int sh = 0; sh < 11; ++sh)
+        if ((1 << sh) == a.block_size) a.bs_shift = sh;
     a.left = p->window_left >= 0 ? p->window_left : va::kInfOff;
     // causal caps the right side at the query position: min(window_right, 0)
     // with window_right >= -1 and -1 meaning unbounded is always 0

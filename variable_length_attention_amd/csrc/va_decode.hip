@@ -42,7 +42,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p)
 }
 
 template <int D, bool PAGED>
-__global__ __launch_bounds__(256) void k2_decode_bf16(AttnArgs a, const int4 *__restrict__ items,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_decode_bf16(AttnArgs a, const int4 *__restrict__ items,
                                                       const int32_t *__restrict__ count,
                                                       float *__restrict__ part_o,
                                                       float2 *__restrict__ part_ml)
@@ -100,13 +100,7 @@ __global__ __launch_bounds__(256) void k2_decode_bf16(AttnArgs a, const int4 *__
     const uint16_t *kbase = (const uint16_t *)a.k;
     const uint16_t *vbase = (const uint16_t *)a.v;
     uint16_t *sv = smem + wave * CH * D;
-    auto row_off = [&](int j) -> size_t {
-        if (PAGED) {
-            const int blk = a.block_table[(size_t)b * a.bt_stride + j / a.block_size];
-            return (((size_t)blk * a.block_size + j % a.block_size) * a.Hkv + c) * D;
-        }
-        return ((size_t)(k0 + j) * a.Hkv + c) * D;
-    };
+    auto row_off = [&](int j) -> size_t { return kv_row_offset<D, PAGED>(a, b, k0, c, j); };
 
     for (int j0 = kv_lo + wave * CH; j0 < kv_hi; j0 += 4 * CH) {
         // K rows j0 + 16 kb + n as A operands (d = 32 ks + 8 kq .. +8)
@@ -169,7 +163,10 @@ __global__ __launch_bounds__(256) void k2_decode_bf16(AttnArgs a, const int4 *__
                 }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        }
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);

@@ -37,6 +37,7 @@ struct AttnArgs {
     const float *sinks;          // [H] or null
     int32_t B, H, Hkv, g;
     int32_t bt_stride, block_size;
+    int32_t bs_shift;            // log2(block_size) when a power of two, else -1
     int32_t left, right;         // visible keys of query position p: [p-left, p+right]
     float scale, scale_log2;     // scale and scale * log2(e)
 };
@@ -81,6 +82,24 @@ __device__ __forceinline__ void row_bounds(int i, int delta, int Lk, int left, i
     const int p = i + delta;
     lo = left >= kInfOff ? 0 : max(0, p - left);
     hi = right >= kInfOff ? Lk - 1 : min(Lk - 1, p + right);
+}
+
+// Element offset of key/value row j (logical position in its sequence) of
+// kv head c: contiguous rows start at k0; paged rows go through the block
+// table (block j / block_size, slot j % block_size).
+template <int D, bool PAGED>
+__device__ __forceinline__ size_t kv_row_offset(const AttnArgs &a, int b, int k0, int c, int j)
+{
+    size_t row;
+    if (PAGED) {
+        const int blk_i = a.bs_shift >= 0 ? (j >> a.bs_shift) : j / a.block_size;
+        const int slot = a.bs_shift >= 0 ? (j & (a.block_size - 1)) : j % a.block_size;
+        const int blk = a.block_table[(size_t)b * a.bt_stride + blk_i];
+        row = (size_t)blk * a.block_size + slot;
+    } else {
+        row = (size_t)(k0 + j);
+    }
+    return (row * a.Hkv + c) * D;
 }
 
 // Workgroup -> (work item, head) with heads grouped per XCD: consecutive

@@ -43,8 +43,26 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Values of lanes l and l^32 combined (v_permlane32_swap exchanges the two
+// 32-lane halves, no LDS round trip).
+__device__ __forceinline__ float halves_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A row's running max is only moved when a tile raises it by more than this
+// (log2 units): until then probabilities exp2(s - m) stay below 2^8, far
+// inside fp32 / bf16 range, and the O / l rescale is skipped.
+constexpr float kRescaleSlack = 8.f;
+
 template <int D, bool PAGED>
-__global__ __launch_bounds__(256) void k1_prefill_bf16(AttnArgs a, const int4 *__restrict__ items,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k1_prefill_bf16(AttnArgs a, const int4 *__restrict__ items,
                                                        const int32_t *__restrict__ count)
 {
     constexpr int BN = kBN;
@@ -120,14 +138,7 @@ __global__ __launch_bounds__(256) void k1_prefill_bf16(AttnArgs a, const int4 *_
         for (int u = 0; u < LPT; ++u) {
             const int j = j0 + r_first + u * RSTEP;
             if (j < kv_hi) {
-                size_t off;
-                if (PAGED) {
-                    const int blk = a.block_table[(size_t)b * a.bt_stride + j / a.block_size];
-                    off = (((size_t)blk * a.block_size + j % a.block_size) * a.Hkv + c) * D;
-                } else {
-                    off = ((size_t)(k0 + j) * a.Hkv + c) * D;
-                }
-                off += cc * 8;
+                const size_t off = kv_row_offset<D, PAGED>(a, b, k0, c, j) + cc * 8;
                 kr[u] = *(const u32x4 *)(kbase + off);
                 vr[u] = *(const u32x4 *)(vbase + off);
             } else {
@@ -176,46 +187,46 @@ __global__ __launch_bounds__(256) void k1_prefill_bf16(AttnArgs a, const int4 *_
                     s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mb], 0, 0, 0);
                 }
             }
-            // lane value v of block mb is key j0 + 32 mb + 8 (v/4) + 4 h2 + v%4
+            // lane value v of block mb is key j0 + 32 mb + 8 (v/4) + 4 h2 + v%4;
+            // raw scores here, the scale enters through one FMA before exp2
             float mx = -INFINITY;
             if (j0 >= flo && j0 + BN - 1 <= fhi) {
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        s[mb][v] *= a.scale_log2;
-                        mx = fmaxf(mx, s[mb][v]);
-                    }
+                    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[mb][v]);
             } else {
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int j = j0 + mb * 32 + (v >> 2) * 8 + h2 * 4 + (v & 3);
-                        const float x = (j >= lo && j <= hi) ? s[mb][v] * a.scale_log2 : -INFINITY;
-                        s[mb][v] = x;
-                        mx = fmaxf(mx, x);
+                        if (j < lo || j > hi) s[mb][v] = -INFINITY;
+                        mx = fmaxf(mx, s[mb][v]);
                     }
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_use);
+            const float mx_c = halves_max(mx) * a.scale_log2;  // scale > 0
+            if (__ballot(mx_c > m_run + kRescaleSlack) != 0ull) {
+                const float m_new = fmaxf(m_run, mx_c);
+                const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+                l_run *= alpha;
+                m_run = m_new;
+#pragma unroll
+                for (int md = 0; md < MD; ++md)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
+            }
+            const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
             float rs = 0.f;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const float p = fast_exp2(s[mb][v] - m_use);
+                    const float p = fast_exp2(fmaf(s[mb][v], a.scale_log2, neg_m));
                     s[mb][v] = p;
                     rs += p;
                 }
-            l_run = l_run * alpha + rs;
-            m_run = m_new;
-#pragma unroll
-            for (int md = 0; md < MD; ++md)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
+            l_run += rs;
 
             // O^T += V^T P^T over 4 steps of 16 keys
 #pragma unroll
@@ -245,7 +256,7 @@ __global__ __launch_bounds__(256) void k1_prefill_bf16(AttnArgs a, const int4 *_
     }
 
     // epilogue: lane (row n, half h2) holds O[row][32 md + 8 i + 4 h2 + j]
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = halves_sum(l_run);
     if (row_ok) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         uint16_t *op = (uint16_t *)a.out + ((size_t)(q0 + row) * a.H + head) * D + h2 * 4;

@@ -60,13 +60,7 @@ __global__ __launch_bounds__(256) void k1_prefill_f32(AttnArgs a, const int4 *__
             const int j = j0 + r;
             float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
             if (j < kv_hi) {
-                size_t off;
-                if (PAGED) {
-                    const int blk = a.block_table[(size_t)b * a.bt_stride + j / a.block_size];
-                    off = (((size_t)blk * a.block_size + j % a.block_size) * a.Hkv + c) * D;
-                } else {
-                    off = ((size_t)(k0 + j) * a.Hkv + c) * D;
-                }
+                const size_t off = kv_row_offset<D, PAGED>(a, b, k0, c, j);
                 kx = *(const float4 *)(kbase + off + ch * 4);
                 vx = *(const float4 *)(vbase + off + ch * 4);
             }
