@@ -268,7 +268,11 @@ va_status run(const Call &c, hipStream_t s)
     hipError_t e = va::launch_plan(pa, s);
     if (e == hipSuccess) {
         if (L.path == kPathPrefill)
-            e = va::launch_prefill_bf16(a, c.p->head_dim, c.paged, pa.items, pa.count, (int)L.grid, s);
+        {
+            const size_t span = (size_t)c.p->max_seqlen_k * c.p->num_kv_heads * c.p->head_dim * 2;
+            const int mode = c.paged ? va::kLoadPaged : (span < ((size_t)1 << 31) ? va::kLoadBuffer : va::kLoadGlobal);
+            e = va::launch_prefill_bf16(a, c.p->head_dim, mode, pa.items, pa.count, (int)L.grid, s);
+        }
         else if (L.path == kPathF32)
             e = va::launch_prefill_f32(a, c.p->head_dim, c.paged, pa.items, pa.count, (int)L.grid, s);
         else {

@@ -44,6 +44,11 @@ struct AttnArgs {
 
 enum PlanMode : int32_t { kPlanPrefill = 0, kPlanDecode = 1 };
 
+// How the prefill kernel fetches K/V rows: buffer loads over one
+// sequence's rows (contiguous, every sequence span below 2 GiB), plain
+// global loads (contiguous, larger spans), or block-table gathers.
+enum LoadMode : int32_t { kLoadBuffer = 0, kLoadGlobal = 1, kLoadPaged = 2 };
+
 struct PlanArgs {
     const int32_t *cu_q;
     const int32_t *lens_k;       // cu_k (prefix sums) or seqused_k (counts)
@@ -63,7 +68,7 @@ struct PlanArgs {
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_plan(const PlanArgs &pa, hipStream_t s);
-hipError_t launch_prefill_bf16(const AttnArgs &a, int head_dim, bool paged, const int4 *items,
+hipError_t launch_prefill_bf16(const AttnArgs &a, int head_dim, int mode, const int4 *items,
                                const int32_t *count, int grid, hipStream_t s);
 hipError_t launch_prefill_f32(const AttnArgs &a, int head_dim, bool paged, const int4 *items,
                               const int32_t *count, int grid, hipStream_t s);
