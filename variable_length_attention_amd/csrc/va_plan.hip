@@ -65,9 +65,12 @@ __device__ int block_exclusive_scan(int v, int *s_tmp, int *total)
 __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
 {
     __shared__ int s_bins[kCostBins];
+    __shared__ uint32_t s_keys[kSortMax];   // (inverted cost, index) sort keys
+    __shared__ int s_off[kSortMax + 1];     // per-sequence item offsets when B <= kSortMax
     __shared__ int s_tmp[kPlanThreads];
     __shared__ long long s_red[kPlanThreads];
     const int tid = threadIdx.x;
+    const bool off_in_lds = a.B <= kSortMax;
 
     // 1. decode: split size from the total visible key count
     int split = 1;
@@ -116,23 +119,31 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
         }
         int chunk_total;
         const int ex = block_exclusive_scan(n, s_tmp, &chunk_total);
-        if (b < a.B) a.seq_off[b] = carry + ex;
+        if (b < a.B) {
+            a.seq_off[b] = carry + ex;
+            if (off_in_lds) s_off[b] = carry + ex;
+        }
         carry += chunk_total;
     }
-    if (tid == 0) a.seq_off[a.B] = carry;
+    if (tid == 0) {
+        a.seq_off[a.B] = carry;
+        if (off_in_lds) s_off[a.B] = carry;
+    }
     const int N = min(carry, a.n_max);
+    const bool use_sort = N <= kSortMax;
     for (int i = tid; i < kCostBins; i += kPlanThreads) s_bins[i] = 0;
     __syncthreads();
+    const int *offs = off_in_lds ? s_off : a.seq_off;
 
-    // 3. unsorted items, costs and the cost histogram
+    // 3. unsorted items, costs and (for the large-N path) the cost histogram
     for (int idx = tid; idx < N; idx += kPlanThreads) {
-        int lo_b = 0, hi_b = a.B - 1;  // last b with seq_off[b] <= idx
+        int lo_b = 0, hi_b = a.B - 1;  // last b with offs[b] <= idx
         while (lo_b < hi_b) {
             const int mid = (lo_b + hi_b + 1) >> 1;
-            if (a.seq_off[mid] <= idx) lo_b = mid; else hi_b = mid - 1;
+            if (offs[mid] <= idx) lo_b = mid; else hi_b = mid - 1;
         }
         const int b = lo_b;
-        const int s = idx - a.seq_off[b];
+        const int s = idx - offs[b];
         const int Lq = q_len(a, b), Lk = k_len(a, b);
         int4 it;
         int cost;
@@ -150,14 +161,43 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
             it = make_int4(b, idx, k_lo, k_hi);
             cost = (k_hi - k_lo + kDecQuantum - 1) / kDecQuantum;
         }
+        const int cbin = min(cost, kCostBins - 1);
         a.unsorted[idx] = it;
-        a.cost[idx] = cost;
-        atomicAdd(&s_bins[min(cost, kCostBins - 1)], 1);
+        if (use_sort) {
+            s_keys[idx] = ((uint32_t)(kCostBins - 1 - cbin) << 19) | (uint32_t)idx;
+        } else {
+            a.cost[idx] = cost;
+            atomicAdd(&s_bins[cbin], 1);
+        }
     }
     __syncthreads();
 
-    // 4. bucket start positions, highest cost first
-    {
+    if (use_sort) {
+        // 4a. bitonic sort of the keys: ascending key = descending cost,
+        // then ascending item index
+        int P = 1;
+        while (P < N) P <<= 1;
+        for (int i = N + tid; i < P; i += kPlanThreads) s_keys[i] = 0xffffffffu;
+        __syncthreads();
+        for (int k = 2; k <= P; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int t = tid; t < P / 2; t += kPlanThreads) {
+                    const int i = 2 * t - (t & (j - 1));  // lower element of the pair
+                    const int l = i + j;
+                    const uint32_t x = s_keys[i], y = s_keys[l];
+                    const bool up = (i & k) == 0;
+                    if ((x > y) == up) {
+                        s_keys[i] = y;
+                        s_keys[l] = x;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        for (int i = tid; i < N; i += kPlanThreads)
+            a.items[i] = a.unsorted[s_keys[i] & ((1u << 19) - 1u)];
+    } else {
+        // 4b. bucket start positions, highest cost first
         constexpr int per = kCostBins / kPlanThreads;
         int local = 0;
         for (int k = 0; k < per; ++k) local += s_bins[kCostBins - 1 - (tid * per + k)];
@@ -169,29 +209,28 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
             s_bins[bin] = run;
             run += c;
         }
-    }
-    __syncthreads();
-
-    // 5. stable placement by one wave, 64 items at a time in index order
-    if (tid < 64) {
-        const int lane = tid;
-        for (int base = 0; base < N; base += 64) {
-            const int idx = base + lane;
-            const bool active = idx < N;
-            const int c = active ? min(a.cost[idx], kCostBins - 1) : -1;
-            unsigned long long remaining = __ballot(active);
-            while (remaining) {
-                const int leader = __ffsll((long long)remaining) - 1;
-                const int lc = __shfl(c, leader);
-                const unsigned long long peers = __ballot(active && c == lc);
-                int start = lane == leader ? s_bins[lc] : 0;
-                start = __shfl(start, leader);
-                if (active && c == lc) {
-                    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
-                    a.items[start + rank] = a.unsorted[idx];
+        __syncthreads();
+        // 5. stable placement by one wave, 64 items at a time in index order
+        if (tid < 64) {
+            const int lane = tid;
+            for (int base = 0; base < N; base += 64) {
+                const int idx = base + lane;
+                const bool active = idx < N;
+                const int c = active ? min(a.cost[idx], kCostBins - 1) : -1;
+                unsigned long long remaining = __ballot(active);
+                while (remaining) {
+                    const int leader = __ffsll((long long)remaining) - 1;
+                    const int lc = __shfl(c, leader);
+                    const unsigned long long peers = __ballot(active && c == lc);
+                    int start = lane == leader ? s_bins[lc] : 0;
+                    start = __shfl(start, leader);
+                    if (active && c == lc) {
+                        const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+                        a.items[start + rank] = a.unsorted[idx];
+                    }
+                    if (lane == leader) s_bins[lc] = start + __popcll(peers);
+                    remaining &= ~peers;
                 }
-                if (lane == leader) s_bins[lc] = start + __popcll(peers);
-                remaining &= ~peers;
             }
         }
     }

@@ -63,6 +63,10 @@ __device__ __forceinline__ float halves_sum(float x)
 // inside fp32 / bf16 range, and the O / l rescale is skipped.
 constexpr float kRescaleSlack = 8.f;
 
+// Waits until this wave's global->LDS loads have landed (vmcnt 0, other
+// counters left alone).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k1_prefill_bf16(
     AttnArgs a, const int4 *__restrict__ items, const int32_t *__restrict__ count)
@@ -72,11 +76,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int NSEG = NCH / 4;      // 64-byte segments per row
     constexpr int KS = D / 16;         // QK^T k-steps
     constexpr int MD = D / 32;         // 32-wide blocks of the head dimension
-    constexpr int RSTEP = 256 / NCH;   // rows covered by one loader pass
-    constexpr int LPT = BN / RSTEP;    // loader passes per tile
+    constexpr int RPI = 64 / NCH;      // rows one 64-lane load instruction fills
+    constexpr int LPW = BN / RPI / 4;  // load instructions per wave per tile
     constexpr int ROWB = D * 2;        // bytes per LDS row
     constexpr int TILEB = BN * ROWB;   // bytes per K or V tile
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TILEB];  // K0 V0 K1 V1
+    // LDS: K ring [K0 | K1] then V ring [V0 | V1]; tile t lives in slot t & 1
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TILEB];
     char *const sbase = (char *)smem;
 
     int item, head;
@@ -108,6 +113,52 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             wlo = l0; whi = h1; flo = l1; fhi = h0;
         }
     }
+    const int ntiles = (kv_hi - kv_lo + BN - 1) / BN;
+    auto visible = [&](int t) {
+        const int j0 = kv_lo + t * BN;
+        return wlo <= whi && j0 <= whi && j0 + BN - 1 >= wlo;
+    };
+
+    // ---- tile loads, global -> LDS without staging registers.  One load
+    // instruction fills RPI consecutive rows (64 lanes x 16 bytes, lane-linear
+    // in LDS); each lane fetches the logical chunk that belongs at its
+    // physical slot.  K rows: chunk XOR (row mod NCH), so the rows of one MFMA
+    // operand read hit distinct chunks; V rows: 64-byte segment XOR (row mod
+    // NSEG), so the rows of one transposing read hit distinct segments.
+    const size_t rowstride = (size_t)a.Hkv * D * 2;
+    const char *kseq = (const char *)a.k + ((size_t)k0 * a.Hkv + c) * D * 2;
+    const char *vseq = (const char *)a.v + ((size_t)k0 * a.Hkv + c) * D * 2;
+    // lane's row / chunk for load instruction u
+    auto ld_row = [&](int u) { return (wave * LPW + u) * RPI + lane / NCH; };
+    auto ld_chunk = [&](int u, bool is_v) {
+        const int r = ld_row(u), p = lane % NCH;
+        return is_v ? p ^ ((r % NSEG) << 2) : p ^ (r % NCH);
+    };
+    auto issue = [&](int t, bool is_v, char *dst) {
+        const int j0 = kv_lo + t * BN;
+        const char *seq = is_v ? vseq : kseq;
+        if constexpr (MODE == kLoadBuffer) {
+            const uint32_t nrec = (uint32_t)((kv_hi - j0) * rowstride);
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(seq + j0 * rowstride), (short)0, nrec, 0x00020000);
+#pragma unroll
+            for (int u = 0; u < LPW; ++u) {
+                const uint32_t off = (uint32_t)(ld_row(u) * rowstride) + ld_chunk(u, is_v) * 16;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void *)(dst + (wave * LPW + u) * 1024), 16, off, 0, 0, 0);
+            }
+        } else {
+            const uint16_t *base = (const uint16_t *)(is_v ? a.v : a.k);
+#pragma unroll
+            for (int u = 0; u < LPW; ++u) {
+                const int j = min(j0 + ld_row(u), kv_hi - 1);
+                const size_t off = kv_row_offset<D, MODE == kLoadPaged>(a, b, k0, c, j) + ld_chunk(u, is_v) * 8;
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(base + off),
+                    (__attribute__((address_space(3))) void *)(dst + (wave * LPW + u) * 1024), 16, 0, 0);
+            }
+        }
+    };
 
     // Q^T operand fragments: lane (row n, half h2) holds d = 16 ks + 8 h2 .. +8
     bf16x8 qf[KS];
@@ -131,98 +182,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         l_run = h2 == 0 ? 1.f : 0.f;
     }
 
-    // LDS byte offsets, fixed per lane.  K rows: chunk index XOR (row mod NCH),
-    // so the 16 rows one MFMA operand read touches hit 16 different chunks.
-    // V rows: 64-byte segment XOR (row mod NSEG), so the 8 rows of one
-    // transposing read spread over all segments.
-    uint32_t koff[KS], voff[MD];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) koff[ks] = n * ROWB + ((((ks * 2 + h2) ^ (n % NCH))) << 4);
-#pragma unroll
-    for (int md = 0; md < MD; ++md) {
+    // LDS byte offsets of this lane's MFMA operand reads
+    auto koff = [&](int ks) -> uint32_t { return n * ROWB + ((((ks * 2 + h2) ^ (n % NCH))) << 4); };
+    auto voff = [&](int md) -> uint32_t {
         const int col = md * 32 + ((lane & 31) >> 4) * 16 + (l16 & 3) * 4;
         const int seg = (col >> 3) ^ ((q4 % NSEG) << 2);
-        voff[md] = (h2 * 4 + q4) * ROWB + (seg << 4) + (col & 7) * 2;
-    }
-    const int cc = tid % NCH, r_first = tid / NCH;
-    const uint32_t st_k = r_first * ROWB + ((cc ^ (r_first % NCH)) << 4);
-    const uint32_t st_v = r_first * ROWB + ((cc ^ ((r_first % NSEG) << 2)) << 4);
-
-    // global -> register loader for one tile.  Rows at or past kv_hi are
-    // never used unmasked: the buffer path reads them as zeros (out of the
-    // descriptor's range), the other paths re-read the last valid row.
-    const size_t rowstride = (size_t)a.Hkv * D * 2;
-    const char *kseq = (const char *)a.k + ((size_t)k0 * a.Hkv + c) * D * 2;
-    const char *vseq = (const char *)a.v + ((size_t)k0 * a.Hkv + c) * D * 2;
-    u32x4 kr[LPT], vr[LPT];
-    auto gload = [&](int t) {
-        const int j0 = kv_lo + t * BN;
-        if constexpr (MODE == kLoadBuffer) {
-            const uint32_t nrec = (uint32_t)((kv_hi - j0) * rowstride);
-            const __amdgpu_buffer_rsrc_t rk =
-                __builtin_amdgcn_make_buffer_rsrc((void *)(kseq + j0 * rowstride), (short)0, nrec, 0x00020000);
-            const __amdgpu_buffer_rsrc_t rv =
-                __builtin_amdgcn_make_buffer_rsrc((void *)(vseq + j0 * rowstride), (short)0, nrec, 0x00020000);
-#pragma unroll
-            for (int u = 0; u < LPT; ++u) {
-                const uint32_t off = (uint32_t)((r_first + u * RSTEP) * rowstride) + cc * 16;
-                kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-                vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < LPT; ++u) {
-                const int j = min(j0 + r_first + u * RSTEP, kv_hi - 1);
-                const size_t off = kv_row_offset<D, MODE == kLoadPaged>(a, b, k0, c, j) + cc * 8;
-                kr[u] = *(const u32x4 *)((const uint16_t *)a.k + off);
-                vr[u] = *(const u32x4 *)((const uint16_t *)a.v + off);
-            }
-        }
-    };
-    auto sstore = [&](auto BUFC) {
-        constexpr int BUF = decltype(BUFC)::value;
-        char *sk = sbase + BUF * 2 * TILEB;
-#pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            *(u32x4 *)(sk + st_k + u * RSTEP * ROWB) = kr[u];
-            *(u32x4 *)(sk + TILEB + st_v + u * RSTEP * ROWB) = vr[u];
-        }
+        return (h2 * 4 + q4) * ROWB + (seg << 4) + (col & 7) * 2;
     };
 
-    auto compute = [&](int j0, auto BUFC) {
-        constexpr int BUF = decltype(BUFC)::value;
-        const char *kt = sbase + BUF * 2 * TILEB;
-        const char *vt = kt + TILEB;
-        // S^T = K Q^T, two independent 32-key accumulator chains
-        f32x16 s[2];
+    // ---- the three pieces of work per tile
+    // S^T = K Q^T: lane value v of block mb is key j0 + 32 mb + 8 (v/4) + 4 h2 + v%4
+    auto qk = [&](f32x16 (&S)[2], const char *kt) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) { s[0][v] = 0.f; s[1][v] = 0.f; }
+        for (int v = 0; v < 16; ++v) { S[0][v] = 0.f; S[1][v] = 0.f; }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 kf0 = *(const bf16x8 *)(kt + koff[ks]);
-            const bf16x8 kf1 = *(const bf16x8 *)(kt + koff[ks] + 32 * ROWB);
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[ks], s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[ks], s[1], 0, 0, 0);
+            const bf16x8 kf0 = *(const bf16x8 *)(kt + koff(ks));
+            const bf16x8 kf1 = *(const bf16x8 *)(kt + koff(ks) + 32 * ROWB);
+            S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[ks], S[0], 0, 0, 0);
+            S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[ks], S[1], 0, 0, 0);
         }
-        // lane value v of block mb is key j0 + 32 mb + 8 (v/4) + 4 h2 + v%4;
-        // raw scores here, the scale enters through one FMA before exp2
+    };
+    // mask (edge tiles only) and row max, then move the running max if the
+    // tile raises it by more than the slack (raw scores; scale > 0)
+    auto row_max = [&](f32x16 (&S)[2], int t) {
+        const int j0 = kv_lo + t * BN;
         float mx = -INFINITY;
         if (j0 >= flo && j0 + BN - 1 <= fhi) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[mb][v]);
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[mb][v]);
         } else {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int j = j0 + mb * 32 + (v >> 2) * 8 + h2 * 4 + (v & 3);
-                    if (j < lo || j > hi) s[mb][v] = -INFINITY;
-                    mx = fmaxf(mx, s[mb][v]);
+                    if (j < lo || j > hi) S[mb][v] = -INFINITY;
+                    mx = fmaxf(mx, S[mb][v]);
                 }
         }
-        const float mx_c = halves_max(mx) * a.scale_log2;  // scale > 0
+        const float mx_c = halves_max(mx) * a.scale_log2;
         if (__ballot(mx_c > m_run + kRescaleSlack) != 0ull) {
             const float m_new = fmaxf(m_run, mx_c);
             const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
@@ -233,57 +234,84 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
         }
-        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-        float rs = 0.f;
+    };
+    // probabilities of PV step t4 (keys 16 t4 .. +16) in bf16, laid out as
+    // that step's P^T operand
+    auto probs = [&](f32x16 (&S)[2], int t4, float neg_m, float &rs) -> bf16x8 {
+        f32x8 pv;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int e = 0; e < 8; ++e) {
+            const float x = fast_exp2(fmaf(S[t4 >> 1][(t4 & 1) * 8 + e], a.scale_log2, neg_m));
+            pv[e] = x;
+            rs += x;
+        }
+        return __builtin_convertvector(pv, bf16x8);
+    };
+    // O^T += V^T P^T for one step of 16 keys
+    auto pv = [&](const bf16x8 &P, int t4, const char *vt) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float p = fast_exp2(fmaf(s[mb][v], a.scale_log2, neg_m));
-                s[mb][v] = p;
-                rs += p;
-            }
-        l_run += rs;
-
-        // O^T += V^T P^T over 4 steps of 16 keys
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-            const int mb = t4 >> 1, ib = (t4 & 1) * 2;
-            f32x8 pv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pv[e] = s[mb][ib * 4 + e];
-            const bf16x8 pf = __builtin_convertvector(pv, bf16x8);
-#pragma unroll
-            for (int md = 0; md < MD; ++md) {
-                const bf16x4 va = lds_read_tr((const uint16_t *)(vt + voff[md] + t4 * 16 * ROWB));
-                const bf16x4 vb = lds_read_tr((const uint16_t *)(vt + voff[md] + (t4 * 16 + 8) * ROWB));
-                const bf16x8 vf = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[md], 0, 0, 0);
-            }
+        for (int md = 0; md < MD; ++md) {
+            const bf16x4 va = lds_read_tr((const uint16_t *)(vt + voff(md) + t4 * 16 * ROWB));
+            const bf16x4 vb = lds_read_tr((const uint16_t *)(vt + voff(md) + (t4 * 16 + 8) * ROWB));
+            const bf16x8 vf = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+            o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P, o[md], 0, 0, 0);
         }
     };
 
-    const int ntiles = (kv_hi - kv_lo + BN - 1) / BN;
-    auto step = [&](int t, auto BUFC) {
+    // ---- software pipeline: iteration t runs QK^T of tile t+1 next to the
+    // softmax of tile t, then PV of tile t next to the row max of tile t+1.
+    // Loads issued at the top of iteration t (into slots freed by the
+    // previous barrier) land before its closing barrier.
+    f32x16 sa[2], sb[2];
+    if (ntiles > 0) {
+        issue(0, false, sbase);
+        issue(0, true, sbase + 2 * TILEB);
+        if (ntiles > 1) issue(1, false, sbase + TILEB);
+    }
+    wait_vmem();
+    __syncthreads();
+    bool vc = ntiles > 0 && visible(0);
+    if (vc) {
+        qk(sa, sbase);
+        row_max(sa, 0);
+    }
+    __syncthreads();  // K slot 0 is refilled by iteration 0
+
+    auto iteration = [&](int t, auto BUFC, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
         constexpr int BUF = decltype(BUFC)::value;
-        const int j0 = kv_lo + t * BN;
-        if (j0 <= whi && j0 + BN - 1 >= wlo) compute(j0, BUFC);
-        if (t + 1 < ntiles) sstore(std::integral_constant<int, BUF ^ 1>{});
-        if (t + 2 < ntiles) gload(t + 2);
+        char *k_next = sbase + (BUF ^ 1) * TILEB;          // K(t+1)
+        char *v_cur = sbase + 2 * TILEB + BUF * TILEB;     // V(t)
+        if (t + 2 < ntiles) issue(t + 2, false, sbase + BUF * TILEB);
+        if (t + 1 < ntiles) issue(t + 1, true, sbase + 2 * TILEB + (BUF ^ 1) * TILEB);
+        const bool vn = t + 1 < ntiles && visible(t + 1);
+        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+        float rs = 0.f;
+        bf16x8 p0, p1;
+        // QK^T of the next tile beside the first half of this tile's softmax
+        if (vn) qk(Sn, k_next);
+        if (vc) {
+            p0 = probs(Sc, 0, neg_m, rs);
+            p1 = probs(Sc, 1, neg_m, rs);
+            // PV of this tile beside the second half of its softmax
+            pv(p0, 0, v_cur);
+            const bf16x8 p2 = probs(Sc, 2, neg_m, rs);
+            pv(p1, 1, v_cur);
+            const bf16x8 p3 = probs(Sc, 3, neg_m, rs);
+            pv(p2, 2, v_cur);
+            pv(p3, 3, v_cur);
+            l_run += rs;
+        }
+        if (vn) row_max(Sn, t + 1);
+        vc = vn;
+        wait_vmem();
         __syncthreads();
     };
-    if (ntiles > 0) {
-        gload(0);
-        sstore(std::integral_constant<int, 0>{});
-        if (ntiles > 1) gload(1);
-    }
-    __syncthreads();
     int t = 0;
     for (; t + 1 < ntiles; t += 2) {
-        step(t, std::integral_constant<int, 0>{});
-        step(t + 1, std::integral_constant<int, 1>{});
+        iteration(t, std::integral_constant<int, 0>{}, sa, sb);
+        iteration(t + 1, std::integral_constant<int, 1>{}, sb, sa);
     }
-    if (t < ntiles) step(t, std::integral_constant<int, 0>{});
+    if (t < ntiles) iteration(t, std::integral_constant<int, 0>{}, sa, sb);
 
     // epilogue: lane (row n, half h2) holds O[row][32 md + 8 i + 4 h2 + j]
     const float l_tot = halves_sum(l_run);
