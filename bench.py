@@ -37,6 +37,15 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
+# Kernel source files whose hash keys the committed HBM-traffic measurements
+# (profiles/traffic.json): a measurement counts only for the exact sources
+# it was taken with.
+KERNEL_SOURCES = {
+    "prefill_bf16": ["va_prefill_bf16.hip", "va_internal.h"],
+    "decode_bf16": ["va_decode.hip", "va_internal.h"],
+    "f32": ["va_prefill_f32.hip", "va_internal.h"],
+}
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -151,6 +160,41 @@ def time_case(case, steps, warmup, torch):
     return ms_step, ms_plan, path
 
 
+# ---------------------------------------------------------------- HBM traffic
+def kernel_source_sha(path_name):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[path_name]:
+        with open(os.path.join(ROOT, "variable_length_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(path_name, workload):
+    """HBM bytes per launch of the dominant kernel from the committed
+    counter runs, or None when there is none for the current sources."""
+    fn = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(fn):
+        return None
+    with open(fn) as fh:
+        rec = json.load(fh).get(f"{path_name}/{workload}")
+    if not rec or rec.get("source_sha256") != kernel_source_sha(path_name):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def calibrate_copy(nbytes, reps):
+    """A plain device copy of known size, for scaling the FETCH_SIZE /
+    WRITE_SIZE counters (each copy reads and writes nbytes)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
 # ---------------------------------------------------------------- CPU baseline
 def cpu_baseline(case, budget_s=15.0):
     import oracle
@@ -184,7 +228,12 @@ def main():
     ap.add_argument("--only-main", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--configs", default="2,3,4,5", help="workloads to time (first is the main one)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, max(1, args.steps))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the attention forward "
               "is measured per GPU; sharding across GPUs is not part of this library.", file=sys.stderr)
@@ -212,14 +261,15 @@ def main():
              "tflops": fl / (ms_step * 1e-3) / 1e12, "gbs": by / (ms_step * 1e-3) / 1e9,
              "tokens_per_s": case["T_q"] / (ms_step * 1e-3), "flop": fl, "bytes": by,
              "kernel_path": ["prefill_bf16", "decode_bf16", "f32"][path]}
+        traffic = measured_traffic(r["kernel_path"], spec.name)
         if hbm_bound:
             ach = by / (ms_kernel * 1e-3) / 1e9
             r["roofline"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                             "frac": ach / PEAK_HBM_GBS, "traffic": None}
+                             "frac": ach / PEAK_HBM_GBS, "traffic": traffic}
         else:
             ach = fl / (ms_kernel * 1e-3) / 1e12
             r["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                             "frac": ach / PEAK_BF16_TFLOPS, "traffic": None}
+                             "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic}
         log(f"config {n}: {ms_step:.4f} ms/step (pre-pass {ms_plan:.4f} ms), {r['tflops']:.1f} TFLOP/s, "
             f"{r['gbs']:.0f} GB/s, roofline {r['roofline']['frac'] * 100:.1f}% of {r['roofline']['bound']}")
         results[n] = r
