@@ -23,6 +23,8 @@
 // variant": the op returns softmax_logsumexp).
 #include "va_internal.h"
 
+#include <type_traits>
+
 namespace va {
 
 namespace {
@@ -56,6 +58,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int VL = CH / RPP;         // V loader passes
     constexpr int ROWS = kDecRows;
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * CH * D];
+    __shared__ int s_tbl[kDecTableMax];
 
     int item, c;
     map_block(blockIdx.x, a.Hkv, item, c);
@@ -67,7 +70,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int k0 = PAGED ? 0 : a.cu_k[b];
     const int delta = Lk - Lq;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int n = lane & 15, kq = lane >> 4, l16 = lane & 15;
     const int rows = min(a.g * Lq, ROWS);
     const bool row_ok = n < rows;
@@ -100,32 +104,92 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint16_t *kbase = (const uint16_t *)a.k;
     const uint16_t *vbase = (const uint16_t *)a.v;
     uint16_t *sv = smem + wave * CH * D;
-    auto row_off = [&](int j) -> size_t { return kv_row_offset<D, PAGED>(a, b, k0, c, j); };
+    // Paged: the block ids of this split's keys are staged in LDS once, so
+    // a row's address needs no dependent global load (a wait for one would
+    // also drain every data load issued before it).
+    int blk0 = 0;
+    bool tbl = false;
+    if constexpr (PAGED) {
+        if (a.bs_shift >= 0 && kv_hi > kv_lo) {
+            blk0 = kv_lo >> a.bs_shift;
+            const int nblk = ((kv_hi - 1) >> a.bs_shift) - blk0 + 1;
+            tbl = nblk <= kDecTableMax;
+            if (tbl)
+                for (int i = tid; i < nblk; i += 256) s_tbl[i] = a.block_table[(size_t)b * a.bt_stride + blk0 + i];
+        }
+        __syncthreads();
+    }
+    // Address modes of the chunk loop (chosen once per split):
+    //  0  every 64-key chunk lies in one block (contiguous K/V, or paged with
+    //     power-of-two blocks >= 64 keys and a chunk-aligned split): one
+    //     buffer descriptor per chunk, per-lane offsets fixed, rows past
+    //     kv_hi read as zeros (outside the descriptor's range)
+    //  1  paged, power-of-two blocks: per-row block ids from the LDS table
+    //  2  anything else: per-row block-table lookups
+    const size_t rowstride = (size_t)a.Hkv * D * 2;  // bytes between key rows
+    auto chunk_loop = [&](auto AMC) {
+    constexpr int AM = decltype(AMC)::value;
+    // element offset of key row j (modes 1, 2; clamped into the split: rows
+    // past kv_hi are masked, so re-reading the last row is harmless)
+    auto row_off = [&](int j) -> size_t {
+        j = min(j, kv_hi - 1);
+        if constexpr (AM == 1) {
+            const int blk = s_tbl[(j >> a.bs_shift) - blk0];
+            return ((((size_t)blk << a.bs_shift) + (j & (a.block_size - 1))) * a.Hkv + c) * D;
+        } else {
+            return kv_row_offset<D, PAGED>(a, b, k0, c, j);
+        }
+    };
+    // mode 0 per-lane byte offsets (all in the range-checked vector offset):
+    // K operand rows n (+16 kb), d = 8 kq (+32 ks); V rows lane / NCH
+    // (+RPP u), chunk lane % NCH
+    const uint32_t koff0 = n * (uint32_t)rowstride + kq * 16;
+    const uint32_t voff0 = (lane / NCH) * (uint32_t)rowstride + (lane % NCH) * 16;
 
     for (int j0 = kv_lo + wave * CH; j0 < kv_hi; j0 += 4 * CH) {
-        // K rows j0 + 16 kb + n as A operands (d = 32 ks + 8 kq .. +8)
         bf16x8 kf[NKB][KS];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            const int j = j0 + kb * 16 + n;
-            if (j < kv_hi) {
-                const uint16_t *kp = kbase + row_off(j) + kq * 8;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(kp + ks * 32));
-            } else {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-            }
-        }
-        // V rows of the chunk, 16-byte chunk `cc` of row r
         u32x4 vr[VL];
         const int cc = lane % NCH;
+        if constexpr (AM == 0) {
+            size_t row0;  // first row of the chunk in the K/V arrays
+            if constexpr (PAGED) {
+                const int blk = __builtin_amdgcn_readfirstlane(s_tbl[(j0 >> a.bs_shift) - blk0]);
+                row0 = ((size_t)blk << a.bs_shift) + (j0 & (a.block_size - 1));
+            } else {
+                row0 = (size_t)(k0 + j0);
+            }
+            const size_t base = (row0 * a.Hkv + c) * D * 2;
+            const uint32_t nrec = (uint32_t)(min(kv_hi - j0, CH) * rowstride);
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)((const char *)a.k + base), (short)0, nrec, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)((const char *)a.v + base), (short)0, nrec, 0x00020000);
 #pragma unroll
-        for (int u = 0; u < VL; ++u) {
-            const int r = u * RPP + lane / NCH;
-            const int j = j0 + r;
-            vr[u] = j < kv_hi ? *(const u32x4 *)(vbase + row_off(j) + cc * 8) : u32x4{0, 0, 0, 0};
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    kf[kb][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                        rk, koff0 + (uint32_t)(kb * 16 * rowstride) + ks * 64, 0, 0));
+#pragma unroll
+            for (int u = 0; u < VL; ++u)
+                vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff0 + (uint32_t)(u * RPP * rowstride), 0, 0);
+        } else {
+            // K rows j0 + 16 kb + n as A operands (d = 32 ks + 8 kq .. +8)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const uint16_t *kp = kbase + row_off(j0 + kb * 16 + n) + kq * 8;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(kp + ks * 32));
+            }
+            // V rows of the chunk, 16-byte chunk `cc` of row r
+#pragma unroll
+            for (int u = 0; u < VL; ++u) {
+                const int r = u * RPP + lane / NCH;
+                vr[u] = *(const u32x4 *)(vbase + row_off(j0 + r) + cc * 8);
+            }
         }
+        // keep every load of the chunk ahead of the math that consumes them
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 s[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -209,6 +273,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         __builtin_amdgcn_wave_barrier();
     }
+    };
+    const bool aligned_blocks = PAGED && tbl && a.bs_shift >= 6 && (kv_lo & (CH - 1)) == 0;
+    if (!PAGED || aligned_blocks) chunk_loop(std::integral_constant<int, 0>{});
+    else if (tbl) chunk_loop(std::integral_constant<int, 1>{});
+    else chunk_loop(std::integral_constant<int, 2>{});
 
     // merge the 4 wave states (LDS reused)
     float l_w = l_run + __shfl_xor(l_run, 16);

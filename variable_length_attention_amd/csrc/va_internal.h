@@ -19,6 +19,7 @@ constexpr int kDecRows = 16;           // decode: packed (head, query) rows per 
 constexpr int kDecChunk = 64;          // decode: keys per wave step
 constexpr int kDecQuantum = 256;       // decode: split sizes are multiples of this
 constexpr int kDecTargetUnits = 4096;  // decode: aim for about this many (split, kv head) units
+constexpr int kDecTableMax = 2048;     // decode: block ids of one split staged in LDS
 constexpr int kPlanThreads = 256;
 constexpr int kCostBins = 4096;        // cost classes of the pre-pass ordering
 constexpr int kSortMax = 4096;         // pre-pass sorts up to this many items in LDS

@@ -95,7 +95,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int delta = Lk - Lq;
     const int c = head / a.g;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int n = lane & 31, h2 = lane >> 5, l16 = lane & 15, q4 = l16 >> 2;
     const int row = i0 + wave * 32 + n;
     const bool row_ok = row < Lq;
