@@ -314,24 +314,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     if (t < ntiles) iteration(t, std::integral_constant<int, 0>{}, sa, sb);
 
-    // epilogue: lane (row n, half h2) holds O[row][32 md + 8 i + 4 h2 + j]
+    // epilogue: lane (row n, half h2) holds O[row][32 md + 8 i + 4 h2 + j].
+    // The O tile goes through LDS (the K/V slots are free after the last
+    // barrier) so that global stores write whole rows with 16-byte lanes:
+    // a workgroup's stores then complete sooner, and it holds its slot until
+    // they have.
     const float l_tot = halves_sum(l_run);
-    if (row_ok) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t *op = (uint16_t *)a.out + ((size_t)(q0 + row) * a.H + head) * D + h2 * 4;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    char *ow = sbase + wave * 32 * ROWB;  // this wave's 32 rows, 16-byte chunk XOR (row mod NCH)
 #pragma unroll
-        for (int md = 0; md < MD; ++md)
+    for (int md = 0; md < MD; ++md)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f32x4 x;
+        for (int i = 0; i < 4; ++i) {
+            f32x4 x;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) x[j] = o[md][i * 4 + j] * inv;
-                const bf16x4 y = __builtin_convertvector(x, bf16x4);
-                *(u32x2 *)(op + md * 32 + i * 8) = __builtin_bit_cast(u32x2, y);
-            }
-        if (h2 == 0 && a.lse)
-            a.lse[(size_t)(q0 + row) * a.H + head] =
-                l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+            for (int j = 0; j < 4; ++j) x[j] = o[md][i * 4 + j] * inv;
+            const bf16x4 y = __builtin_convertvector(x, bf16x4);
+            const int phys = (md * 4 + i) ^ (n % NCH);
+            *(u32x2 *)(ow + n * ROWB + phys * 16 + h2 * 8) = __builtin_bit_cast(u32x2, y);
+        }
+    if (row_ok && h2 == 0 && a.lse)
+        a.lse[(size_t)(q0 + row) * a.H + head] =
+            l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    __syncthreads();
+    {
+        constexpr int RPW = 64 / NCH;  // rows one 64-lane pass covers
+        const int cidx = lane % NCH;
+#pragma unroll
+        for (int u = 0; u < 32 / RPW; ++u) {
+            const int r = u * RPW + lane / NCH;
+            const int orow = i0 + wave * 32 + r;
+            const u32x4 v = *(const u32x4 *)(ow + r * ROWB + ((cidx ^ (r % NCH)) << 4));
+            if (orow < Lq)
+                *(u32x4 *)((uint16_t *)a.out + ((size_t)(q0 + orow) * a.H + head) * D + cidx * 8) = v;
+        }
     }
 }
 
