@@ -322,7 +322,25 @@ def _plan_cpu(case, mode, bm=128, bn=64):
     return np.asarray([items[i][1] for i in order], np.int32).reshape(-1, 4)
 
 
-@pytest.mark.parametrize("which", ["c2", "c4", "c5", "window_decode", "c1_f32"])
+def _lengths_only_case(B, lo, hi, seed, H=8, Hkv=2, D=128, causal=True, decode_k=None):
+    """Sequence lengths only (the partition needs nothing else).  With
+    decode_k=(lo, hi) every sequence has one query row and that many keys."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(lo, hi, B, endpoint=True)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cu_k, max_k = cu, int(lens.max())
+    if decode_k is not None:
+        lens_k = rng.integers(decode_k[0], decode_k[1], B, endpoint=True)
+        cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+        max_k = int(lens_k.max())
+    return dict(B=B, H=H, Hkv=Hkv, D=D, dtype="bf16", causal=causal, window_left=-1,
+                window_right=-1, cu_q=cu, cu_k=cu_k, T_q=int(cu[-1]), T_k=int(cu_k[-1]),
+                max_q=int(lens.max()), max_k=max_k, paged=False)
+
+
+@pytest.mark.parametrize("which", ["c2", "c4", "c5", "window_decode", "c1_f32", "bitonic_range",
+                                   "placement_range", "many_seqs_sort", "many_seqs_placement",
+                                   "many_seqs_decode"])
 def test_work_partition_bit_exact(which):
     import variable_length_attention_amd as va
     if which == "c2":
@@ -335,6 +353,17 @@ def test_work_partition_bit_exact(which):
         spec = W.Spec("wd", 909, "bf16", 8, 8, 64, ("uniform", 1, 2, 30), lens_k=("uniform", 0, 5000),
                       window=(300, 0), paged=False)
         case, mode = W.make_case(spec), "decode"
+    elif which == "bitonic_range":      # 1025..2048 items: LDS bitonic sort
+        case, mode = _lengths_only_case(300, 100, 900, 11), "prefill"
+    elif which == "placement_range":    # > 2048 items: counting placement
+        case, mode = _lengths_only_case(1500, 200, 900, 12), "prefill"
+    # more than 2048 sequences: lengths read from global memory, not LDS
+    elif which == "many_seqs_sort":     # ~1970 items, many empty sequences
+        case, mode = _lengths_only_case(2300, 0, 6, 13), "prefill"
+    elif which == "many_seqs_placement":
+        case, mode = _lengths_only_case(3000, 100, 400, 14), "prefill"
+    elif which == "many_seqs_decode":
+        case, mode = _lengths_only_case(2600, 1, 1, 15, decode_k=(0, 3000)), "decode"
     else:
         case, mode = W.make_case(W.config(1)), "prefill"
     announce(f"plan {which}")

@@ -20,9 +20,11 @@ constexpr int kDecChunk = 64;          // decode: keys per wave step
 constexpr int kDecQuantum = 256;       // decode: split sizes are multiples of this
 constexpr int kDecTargetUnits = 4096;  // decode: aim for about this many (split, kv head) units
 constexpr int kDecTableMax = 2048;     // decode: block ids of one split staged in LDS
-constexpr int kPlanThreads = 256;
+constexpr int kPlanThreads = 512;
 constexpr int kCostBins = 4096;        // cost classes of the pre-pass ordering
-constexpr int kSortMax = 4096;         // pre-pass sorts up to this many items in LDS
+constexpr int kSortMax = 2048;         // pre-pass sorts up to this many items in LDS
+constexpr int kRankSortMax = 1024;     // ... by ranking (no barriers) up to this many
+constexpr int kPlanSeqs = 2048;        // pre-pass keeps up to this many sequences' lengths in LDS
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

@@ -20,16 +20,6 @@ namespace va {
 
 namespace {
 
-__device__ __forceinline__ int q_len(const PlanArgs &a, int b)
-{
-    return a.cu_q[b + 1] - a.cu_q[b];
-}
-
-__device__ __forceinline__ int k_len(const PlanArgs &a, int b)
-{
-    return a.lens_k_is_prefix ? a.lens_k[b + 1] - a.lens_k[b] : a.lens_k[b];
-}
-
 // Visible key range [lo, hi) of query rows [i0, i1), i1 > i0.  Both bounds of
 // a row are non-decreasing in the row index, so the first row gives the low
 // end and the last row the high end (a superset when some rows are empty).
@@ -43,54 +33,79 @@ __device__ __forceinline__ void rows_range(int i0, int i1, int delta, int Lk, in
     hi = max(h1 + 1, lo);
 }
 
-// Exclusive scan of one value per thread over the workgroup; returns the
-// prefix and writes the total to *total.
-__device__ int block_exclusive_scan(int v, int *s_tmp, int *total)
+constexpr int kWaves = kPlanThreads / 64;
+
+// Exclusive scan of one value per thread over the workgroup (wave scans
+// with cross-lane shuffles, then one pass over the wave totals); returns
+// the prefix and writes the total to *total.
+__device__ int block_exclusive_scan(int v, int *s_w, int *total)
 {
-    const int tid = threadIdx.x;
-    s_tmp[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        int x = tid >= off ? s_tmp[tid - off] : 0;
-        __syncthreads();
-        s_tmp[tid] += x;
-        __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
     }
-    const int incl = s_tmp[tid];
-    *total = s_tmp[kPlanThreads - 1];
+    if (lane == 63) s_w[w] = x;
     __syncthreads();
-    return incl - v;
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const int t = s_w[i];
+        before += i < w ? t : 0;
+        tot += t;
+    }
+    *total = tot;
+    __syncthreads();
+    return before + x - v;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
 {
-    __shared__ int s_bins[kCostBins];
-    __shared__ uint32_t s_keys[kSortMax];   // (inverted cost, index) sort keys
-    __shared__ int s_off[kSortMax + 1];     // per-sequence item offsets when B <= kSortMax
-    __shared__ int s_tmp[kPlanThreads];
-    __shared__ long long s_red[kPlanThreads];
+    __shared__ int s_lq[kPlanSeqs], s_lk[kPlanSeqs];  // per-sequence lengths (B <= kPlanSeqs)
+    __shared__ int s_off[kPlanSeqs + 1];              // first item of each sequence
+    __shared__ uint32_t s_keys[kSortMax];             // (inverted cost, index) sort keys
+    __shared__ int s_bins[kCostBins];                 // counting placement (large lists)
+    __shared__ int s_w[kWaves];
+    __shared__ long long s_w64[kWaves];
     const int tid = threadIdx.x;
-    const bool off_in_lds = a.B <= kSortMax;
+    const bool seq_lds = a.B <= kPlanSeqs;
+
+    // 0. per-sequence lengths into LDS once
+    if (seq_lds)
+        for (int b = tid; b < a.B; b += kPlanThreads) {
+            s_lq[b] = a.cu_q[b + 1] - a.cu_q[b];
+            s_lk[b] = a.lens_k_is_prefix ? a.lens_k[b + 1] - a.lens_k[b] : a.lens_k[b];
+        }
+    __syncthreads();
+    auto q_len = [&](int b) { return seq_lds ? s_lq[b] : a.cu_q[b + 1] - a.cu_q[b]; };
+    auto k_len = [&](int b) {
+        return seq_lds ? s_lk[b] : (a.lens_k_is_prefix ? a.lens_k[b + 1] - a.lens_k[b] : a.lens_k[b]);
+    };
+    auto vis_range = [&](int b, int &lo, int &hi) {  // keys any query row of b sees
+        const int Lq = q_len(b), Lk = k_len(b);
+        lo = hi = 0;
+        if (Lq > 0 && Lk > 0) rows_range(0, Lq, Lk - Lq, Lk, a.left, a.right, lo, hi);
+    };
 
     // 1. decode: split size from the total visible key count
     int split = 1;
     if (a.mode == kPlanDecode) {
         long long vis = 0;
         for (int b = tid; b < a.B; b += kPlanThreads) {
-            const int Lq = q_len(a, b), Lk = k_len(a, b);
-            if (Lq > 0 && Lk > 0) {
-                int lo, hi;
-                rows_range(0, Lq, Lk - Lq, Lk, a.left, a.right, lo, hi);
-                vis += hi - lo;
-            }
+            int lo, hi;
+            vis_range(b, lo, hi);
+            vis += hi - lo;
         }
-        s_red[tid] = vis;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) vis += __shfl_xor(vis, off);
+        if ((tid & 63) == 0) s_w64[tid >> 6] = vis;
         __syncthreads();
-        for (int off = kPlanThreads / 2; off > 0; off >>= 1) {
-            if (tid < off) s_red[tid] += s_red[tid + off];
-            __syncthreads();
-        }
-        const long long want = (s_red[0] * a.Hkv + kDecTargetUnits - 1) / kDecTargetUnits;
+        long long tot = 0;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) tot += s_w64[i];
+        const long long want = (tot * a.Hkv + kDecTargetUnits - 1) / kDecTargetUnits;
         long long sz = (want + kDecQuantum - 1) / kDecQuantum * kDecQuantum;
         if (sz < kDecQuantum) sz = kDecQuantum;
         if (sz > kMaxSeqlen) sz = kMaxSeqlen;
@@ -103,40 +118,32 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
         const int b = base + tid;
         int n = 0;
         if (b < a.B) {
-            const int Lq = q_len(a, b);
             if (a.mode == kPlanPrefill) {
-                n = (Lq + a.bm - 1) / a.bm;
+                n = (q_len(b) + a.bm - 1) / a.bm;
             } else {
-                const int Lk = k_len(a, b);
-                int vis = 0;
-                if (Lq > 0 && Lk > 0) {
-                    int lo, hi;
-                    rows_range(0, Lq, Lk - Lq, Lk, a.left, a.right, lo, hi);
-                    vis = hi - lo;
-                }
-                n = max(1, (vis + split - 1) / split);
+                int lo, hi;
+                vis_range(b, lo, hi);
+                n = max(1, (hi - lo + split - 1) / split);
             }
         }
         int chunk_total;
-        const int ex = block_exclusive_scan(n, s_tmp, &chunk_total);
+        const int ex = block_exclusive_scan(n, s_w, &chunk_total);
         if (b < a.B) {
             a.seq_off[b] = carry + ex;
-            if (off_in_lds) s_off[b] = carry + ex;
+            if (seq_lds) s_off[b] = carry + ex;
         }
         carry += chunk_total;
     }
     if (tid == 0) {
         a.seq_off[a.B] = carry;
-        if (off_in_lds) s_off[a.B] = carry;
+        if (seq_lds) s_off[a.B] = carry;
     }
     const int N = min(carry, a.n_max);
-    const bool use_sort = N <= kSortMax;
-    for (int i = tid; i < kCostBins; i += kPlanThreads) s_bins[i] = 0;
     __syncthreads();
-    const int *offs = off_in_lds ? s_off : a.seq_off;
+    const int *offs = seq_lds ? s_off : a.seq_off;
 
-    // 3. unsorted items, costs and (for the large-N path) the cost histogram
-    for (int idx = tid; idx < N; idx += kPlanThreads) {
+    // item idx: (sequence, first query row | split slot, key range) and cost
+    auto make_item = [&](int idx, int &cost) -> int4 {
         int lo_b = 0, hi_b = a.B - 1;  // last b with offs[b] <= idx
         while (lo_b < hi_b) {
             const int mid = (lo_b + hi_b + 1) >> 1;
@@ -144,65 +151,79 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
         }
         const int b = lo_b;
         const int s = idx - offs[b];
-        const int Lq = q_len(a, b), Lk = k_len(a, b);
-        int4 it;
-        int cost;
         if (a.mode == kPlanPrefill) {
+            const int Lq = q_len(b), Lk = k_len(b);
             const int i0 = s * a.bm, i1 = min(Lq, i0 + a.bm);
             int lo = 0, hi = 0;
             if (Lk > 0) rows_range(i0, i1, Lk - Lq, Lk, a.left, a.right, lo, hi);
-            it = make_int4(b, i0, lo, hi);
             cost = (hi - lo + a.bn - 1) / a.bn;
-        } else {
-            int lo = 0, hi = 0;
-            if (Lq > 0 && Lk > 0) rows_range(0, Lq, Lk - Lq, Lk, a.left, a.right, lo, hi);
-            const int k_lo = min(hi, lo + s * split);
-            const int k_hi = min(hi, k_lo + split);
-            it = make_int4(b, idx, k_lo, k_hi);
-            cost = (k_hi - k_lo + kDecQuantum - 1) / kDecQuantum;
+            return make_int4(b, i0, lo, hi);
         }
-        const int cbin = min(cost, kCostBins - 1);
-        a.unsorted[idx] = it;
-        if (use_sort) {
-            s_keys[idx] = ((uint32_t)(kCostBins - 1 - cbin) << 19) | (uint32_t)idx;
-        } else {
-            a.cost[idx] = cost;
-            atomicAdd(&s_bins[cbin], 1);
-        }
-    }
-    __syncthreads();
+        int lo, hi;
+        vis_range(b, lo, hi);
+        const int k_lo = min(hi, lo + s * split);
+        const int k_hi = min(hi, k_lo + split);
+        cost = (k_hi - k_lo + kDecQuantum - 1) / kDecQuantum;
+        return make_int4(b, idx, k_lo, k_hi);
+    };
 
-    if (use_sort) {
-        // 4a. bitonic sort of the keys: ascending key = descending cost,
-        // then ascending item index
-        int P = 1;
-        while (P < N) P <<= 1;
-        for (int i = N + tid; i < P; i += kPlanThreads) s_keys[i] = 0xffffffffu;
+    if (N <= kSortMax) {
+        // 3a. sort keys in LDS: ascending key = descending cost, then index
+        for (int idx = tid; idx < N; idx += kPlanThreads) {
+            int cost;
+            make_item(idx, cost);
+            s_keys[idx] = ((uint32_t)(kCostBins - 1 - min(cost, kCostBins - 1)) << 19) | (uint32_t)idx;
+        }
         __syncthreads();
-        for (int k = 2; k <= P; k <<= 1) {
-            for (int j = k >> 1; j > 0; j >>= 1) {
-                for (int t = tid; t < P / 2; t += kPlanThreads) {
-                    const int i = 2 * t - (t & (j - 1));  // lower element of the pair
-                    const int l = i + j;
-                    const uint32_t x = s_keys[i], y = s_keys[l];
-                    const bool up = (i & k) == 0;
-                    if ((x > y) == up) {
-                        s_keys[i] = y;
-                        s_keys[l] = x;
+        if (N <= kRankSortMax) {
+            // rank = number of smaller keys (keys are unique): a permutation
+            for (int i = tid; i < N; i += kPlanThreads) {
+                const uint32_t key = s_keys[i];
+                int rank = 0;
+                for (int j = 0; j < N; ++j) rank += s_keys[j] < key;
+                int cost;
+                a.items[rank] = make_item((int)(key & ((1u << 19) - 1u)), cost);
+            }
+        } else {
+            int P = 1;
+            while (P < N) P <<= 1;
+            for (int i = N + tid; i < P; i += kPlanThreads) s_keys[i] = 0xffffffffu;
+            __syncthreads();
+            for (int k = 2; k <= P; k <<= 1) {
+                for (int j = k >> 1; j > 0; j >>= 1) {
+                    for (int t = tid; t < P / 2; t += kPlanThreads) {
+                        const int i = 2 * t - (t & (j - 1));  // lower element of the pair
+                        const int l = i + j;
+                        const uint32_t x = s_keys[i], y = s_keys[l];
+                        if ((x > y) == ((i & k) == 0)) {
+                            s_keys[i] = y;
+                            s_keys[l] = x;
+                        }
                     }
+                    __syncthreads();
                 }
-                __syncthreads();
+            }
+            for (int i = tid; i < N; i += kPlanThreads) {
+                int cost;
+                a.items[i] = make_item((int)(s_keys[i] & ((1u << 19) - 1u)), cost);
             }
         }
-        for (int i = tid; i < N; i += kPlanThreads)
-            a.items[i] = a.unsorted[s_keys[i] & ((1u << 19) - 1u)];
     } else {
-        // 4b. bucket start positions, highest cost first
+        // 3b. large lists: counting placement, highest cost first, stable
+        for (int i = tid; i < kCostBins; i += kPlanThreads) s_bins[i] = 0;
+        __syncthreads();
+        for (int idx = tid; idx < N; idx += kPlanThreads) {
+            int cost;
+            a.unsorted[idx] = make_item(idx, cost);
+            a.cost[idx] = cost;
+            atomicAdd(&s_bins[min(cost, kCostBins - 1)], 1);
+        }
+        __syncthreads();
         constexpr int per = kCostBins / kPlanThreads;
         int local = 0;
         for (int k = 0; k < per; ++k) local += s_bins[kCostBins - 1 - (tid * per + k)];
         int total;
-        int run = block_exclusive_scan(local, s_tmp, &total);
+        int run = block_exclusive_scan(local, s_w, &total);
         for (int k = 0; k < per; ++k) {
             const int bin = kCostBins - 1 - (tid * per + k);
             const int c = s_bins[bin];
@@ -210,8 +231,7 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
             run += c;
         }
         __syncthreads();
-        // 5. stable placement by one wave, 64 items at a time in index order
-        if (tid < 64) {
+        if (tid < 64) {  // one wave, 64 items at a time in index order
             const int lane = tid;
             for (int base = 0; base < N; base += 64) {
                 const int idx = base + lane;
