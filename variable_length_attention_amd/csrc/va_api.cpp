@@ -47,7 +47,7 @@ struct Layout {
     int n_max = 0;
     int bm = 0, bn = 0;
     long long grid = 0;
-    size_t off_count = 0, off_seq = 0, off_unsorted = 0, off_cost = 0, off_items = 0;
+    size_t off_count = 0, off_seq = 0, off_unsorted = 0, off_cost = 0, off_items = 0, off_seqinfo = 0;
     size_t off_part_ml = 0, off_part_o = 0, total = 0;
 };
 
@@ -126,6 +126,7 @@ va_status make_layout(const va_problem *p, int paged, Layout &L)
     L.off_unsorted = off; off = align_up(off + 16 * (size_t)n_max, 256);
     L.off_cost = off; off = align_up(off + 4 * (size_t)n_max, 256);
     L.off_items = off; off = align_up(off + 16 * (size_t)n_max, 256);
+    L.off_seqinfo = off; off = align_up(off + 16 * (size_t)n_max, 256);
     if (L.path == kPathDecode) {
         const size_t rows = (size_t)n_max * p->num_kv_heads * va::kDecRows;
         L.off_part_ml = off; off = align_up(off + 8 * rows, 256);
@@ -248,6 +249,7 @@ va::PlanArgs make_plan(const Call &c, const Layout &L, const va::AttnArgs &a)
     pa.unsorted = (int4 *)(ws + L.off_unsorted);
     pa.cost = (int32_t *)(ws + L.off_cost);
     pa.items = (int4 *)(ws + L.off_items);
+    pa.seqinfo = (int4 *)(ws + L.off_seqinfo);
     return pa;
 }
 
@@ -271,15 +273,15 @@ va_status run(const Call &c, hipStream_t s)
         {
             const size_t span = (size_t)c.p->max_seqlen_k * c.p->num_kv_heads * c.p->head_dim * 2;
             const int mode = c.paged ? va::kLoadPaged : (span < ((size_t)1 << 31) ? va::kLoadBuffer : va::kLoadGlobal);
-            e = va::launch_prefill_bf16(a, c.p->head_dim, mode, pa.items, pa.count, (int)L.grid, s);
+            e = va::launch_prefill_bf16(a, c.p->head_dim, mode, pa.items, pa.seqinfo, pa.count, (int)L.grid, s);
         }
         else if (L.path == kPathF32)
-            e = va::launch_prefill_f32(a, c.p->head_dim, c.paged, pa.items, pa.count, (int)L.grid, s);
+            e = va::launch_prefill_f32(a, c.p->head_dim, c.paged, pa.items, pa.seqinfo, pa.count, (int)L.grid, s);
         else {
             char *ws = (char *)c.ws;
             float *po = (float *)(ws + L.off_part_o);
             float2 *pml = (float2 *)(ws + L.off_part_ml);
-            e = va::launch_decode_bf16(a, c.p->head_dim, c.paged, pa.items, pa.count, (int)L.grid, po, pml, s);
+            e = va::launch_decode_bf16(a, c.p->head_dim, c.paged, pa.items, pa.seqinfo, pa.count, (int)L.grid, po, pml, s);
             if (e == hipSuccess) e = va::launch_decode_combine(a, c.p->head_dim, pa.seq_off, po, pml, s);
         }
     }

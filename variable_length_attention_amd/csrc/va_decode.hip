@@ -45,6 +45,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p)
 
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_decode_bf16(AttnArgs a, const int4 *__restrict__ items,
+                                                      const int4 *__restrict__ seqinfo,
                                                       const int32_t *__restrict__ count,
                                                       float *__restrict__ part_o,
                                                       float2 *__restrict__ part_ml)
@@ -62,12 +63,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     int item, c;
     map_block(blockIdx.x, a.Hkv, item, c);
-    if (item >= *count) return;
+    const int n_items = *count;
     const int4 it = items[item];
+    const int4 si = seqinfo[item];
+    asm volatile("" ::"s"(it.x), "s"(si.x), "s"(n_items));
+    if (item >= n_items) return;
     const int b = it.x, slot = it.y, kv_lo = it.z, kv_hi = it.w;
-    const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
-    const int Lk = PAGED ? a.seqused_k[b] : a.cu_k[b + 1] - a.cu_k[b];
-    const int k0 = PAGED ? 0 : a.cu_k[b];
+    const int q0 = si.x, Lq = si.y, k0 = si.z, Lk = si.w;
     const int delta = Lk - Lq;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -92,7 +94,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const uint16_t *qp = (const uint16_t *)a.q + ((size_t)(q0 + (row_ok ? qi : 0)) * a.H + (row_ok ? head : 0)) * D + kq * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            u32x4 x = row_ok ? *(const u32x4 *)(qp + ks * 32) : u32x4{0, 0, 0, 0};
+            u32x4 x = *(const u32x4 *)(qp + ks * 32);
+            if (!row_ok) x = u32x4{0, 0, 0, 0};
             qf[ks] = __builtin_bit_cast(bf16x8, x);
         }
     }
@@ -367,16 +370,16 @@ __global__ __launch_bounds__(256) void k3_combine(AttnArgs a, const int32_t *__r
 }  // namespace
 
 hipError_t launch_decode_bf16(const AttnArgs &a, int head_dim, bool paged, const int4 *items,
-                              const int32_t *count, int grid, float *part_o, float2 *part_ml,
-                              hipStream_t s)
+                              const int4 *seqinfo, const int32_t *count, int grid, float *part_o,
+                              float2 *part_ml, hipStream_t s)
 {
     const dim3 g(grid), blk(256);
     if (head_dim == 128) {
-        if (paged) hipLaunchKernelGGL((k2_decode_bf16<128, true>), g, blk, 0, s, a, items, count, part_o, part_ml);
-        else hipLaunchKernelGGL((k2_decode_bf16<128, false>), g, blk, 0, s, a, items, count, part_o, part_ml);
+        if (paged) hipLaunchKernelGGL((k2_decode_bf16<128, true>), g, blk, 0, s, a, items, seqinfo, count, part_o, part_ml);
+        else hipLaunchKernelGGL((k2_decode_bf16<128, false>), g, blk, 0, s, a, items, seqinfo, count, part_o, part_ml);
     } else {
-        if (paged) hipLaunchKernelGGL((k2_decode_bf16<64, true>), g, blk, 0, s, a, items, count, part_o, part_ml);
-        else hipLaunchKernelGGL((k2_decode_bf16<64, false>), g, blk, 0, s, a, items, count, part_o, part_ml);
+        if (paged) hipLaunchKernelGGL((k2_decode_bf16<64, true>), g, blk, 0, s, a, items, seqinfo, count, part_o, part_ml);
+        else hipLaunchKernelGGL((k2_decode_bf16<64, false>), g, blk, 0, s, a, items, seqinfo, count, part_o, part_ml);
     }
     return hipGetLastError();
 }

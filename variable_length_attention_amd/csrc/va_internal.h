@@ -68,17 +68,19 @@ struct PlanArgs {
     int4 *unsorted;              // [n_max]
     int32_t *cost;               // [n_max]
     int4 *items;                 // [n_max] sorted, execution order
+    int4 *seqinfo;               // [n_max] per item: (first query row, query rows,
+                                 //  first key row (contiguous; 0 paged), key rows)
 };
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_plan(const PlanArgs &pa, hipStream_t s);
 hipError_t launch_prefill_bf16(const AttnArgs &a, int head_dim, int mode, const int4 *items,
-                               const int32_t *count, int grid, hipStream_t s);
+                               const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);
 hipError_t launch_prefill_f32(const AttnArgs &a, int head_dim, bool paged, const int4 *items,
-                              const int32_t *count, int grid, hipStream_t s);
+                              const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);
 hipError_t launch_decode_bf16(const AttnArgs &a, int head_dim, bool paged, const int4 *items,
-                              const int32_t *count, int grid, float *part_o, float2 *part_ml,
-                              hipStream_t s);
+                              const int4 *seqinfo, const int32_t *count, int grid, float *part_o,
+                              float2 *part_ml, hipStream_t s);
 hipError_t launch_decode_combine(const AttnArgs &a, int head_dim, const int32_t *seq_off,
                                  const float *part_o, const float2 *part_ml, hipStream_t s);
 

@@ -64,6 +64,7 @@ __device__ int block_exclusive_scan(int v, int *s_w, int *total)
 __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
 {
     __shared__ int s_lq[kPlanSeqs], s_lk[kPlanSeqs];  // per-sequence lengths (B <= kPlanSeqs)
+    __shared__ int s_q0[kPlanSeqs], s_k0[kPlanSeqs];  // per-sequence first query / key row
     __shared__ int s_off[kPlanSeqs + 1];              // first item of each sequence
     __shared__ uint32_t s_keys[kSortMax];             // (inverted cost, index) sort keys
     __shared__ int s_bins[kCostBins];                 // counting placement (large lists)
@@ -75,13 +76,21 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
     // 0. per-sequence lengths into LDS once
     if (seq_lds)
         for (int b = tid; b < a.B; b += kPlanThreads) {
-            s_lq[b] = a.cu_q[b + 1] - a.cu_q[b];
-            s_lk[b] = a.lens_k_is_prefix ? a.lens_k[b + 1] - a.lens_k[b] : a.lens_k[b];
+            const int q0 = a.cu_q[b], k0 = a.lens_k_is_prefix ? a.lens_k[b] : 0;
+            s_q0[b] = q0;
+            s_k0[b] = k0;
+            s_lq[b] = a.cu_q[b + 1] - q0;
+            s_lk[b] = a.lens_k_is_prefix ? a.lens_k[b + 1] - k0 : a.lens_k[b];
         }
     __syncthreads();
     auto q_len = [&](int b) { return seq_lds ? s_lq[b] : a.cu_q[b + 1] - a.cu_q[b]; };
     auto k_len = [&](int b) {
         return seq_lds ? s_lk[b] : (a.lens_k_is_prefix ? a.lens_k[b + 1] - a.lens_k[b] : a.lens_k[b]);
+    };
+    // (first query row, query rows, first key row, key rows) of sequence b
+    auto seq_info = [&](int b) {
+        if (seq_lds) return make_int4(s_q0[b], s_lq[b], s_k0[b], s_lk[b]);
+        return make_int4(a.cu_q[b], q_len(b), a.lens_k_is_prefix ? a.lens_k[b] : 0, k_len(b));
     };
     auto vis_range = [&](int b, int &lo, int &hi) {  // keys any query row of b sees
         const int Lq = q_len(b), Lk = k_len(b);
@@ -182,7 +191,9 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
                 int rank = 0;
                 for (int j = 0; j < N; ++j) rank += s_keys[j] < key;
                 int cost;
-                a.items[rank] = make_item((int)(key & ((1u << 19) - 1u)), cost);
+                const int4 itm = make_item((int)(key & ((1u << 19) - 1u)), cost);
+                a.items[rank] = itm;
+                a.seqinfo[rank] = seq_info(itm.x);
             }
         } else {
             int P = 1;
@@ -205,7 +216,9 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
             }
             for (int i = tid; i < N; i += kPlanThreads) {
                 int cost;
-                a.items[i] = make_item((int)(s_keys[i] & ((1u << 19) - 1u)), cost);
+                const int4 itm = make_item((int)(s_keys[i] & ((1u << 19) - 1u)), cost);
+                a.items[i] = itm;
+                a.seqinfo[i] = seq_info(itm.x);
             }
         }
     } else {
@@ -246,7 +259,9 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
                     start = __shfl(start, leader);
                     if (active && c == lc) {
                         const int rank = __popcll(peers & ((1ull << lane) - 1ull));
-                        a.items[start + rank] = a.unsorted[idx];
+                        const int4 itm = a.unsorted[idx];
+                        a.items[start + rank] = itm;
+                        a.seqinfo[start + rank] = seq_info(itm.x);
                     }
                     if (lane == leader) s_bins[lc] = start + __popcll(peers);
                     remaining &= ~peers;

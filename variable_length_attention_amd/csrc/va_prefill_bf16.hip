@@ -69,7 +69,7 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 
 template <int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k1_prefill_bf16(
-    AttnArgs a, const int4 *__restrict__ items, const int32_t *__restrict__ count)
+    AttnArgs a, const int4 *__restrict__ items, const int4 *__restrict__ seqinfo, const int32_t *__restrict__ count)
 {
     constexpr int BN = kBN;
     constexpr int NCH = D / 8;         // 16-byte chunks per row
@@ -86,12 +86,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     int item, head;
     map_block(blockIdx.x, a.H, item, head);
-    if (item >= *count) return;
+    // the item, its sequence's offsets and the item count in one round trip
+    // (item < capacity always holds, so the first two reads stay in bounds)
+    const int n_items = *count;
     const int4 it = items[item];
+    const int4 si = seqinfo[item];
+    asm volatile("" ::"s"(it.x), "s"(si.x), "s"(n_items));
+    if (item >= n_items) return;
     const int b = it.x, i0 = it.y, kv_lo = it.z, kv_hi = it.w;
-    const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
-    const int Lk = MODE == kLoadPaged ? a.seqused_k[b] : a.cu_k[b + 1] - a.cu_k[b];
-    const int k0 = MODE == kLoadPaged ? 0 : a.cu_k[b];
+    const int q0 = si.x, Lq = si.y, k0 = si.z, Lk = si.w;
     const int delta = Lk - Lq;
     const int c = head / a.g;
 
@@ -167,7 +170,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const uint16_t *qp = (const uint16_t *)a.q + ((size_t)(q0 + (row_ok ? row : 0)) * a.H + head) * D + h2 * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            u32x4 x = row_ok ? *(const u32x4 *)(qp + ks * 16) : u32x4{0, 0, 0, 0};
+            // unconditional load (rows past the end read row 0), then zeroed
+            u32x4 x = *(const u32x4 *)(qp + ks * 16);
+            if (!row_ok) x = u32x4{0, 0, 0, 0};
             qf[ks] = __builtin_bit_cast(bf16x8, x);
         }
     }
@@ -178,10 +183,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[md][v] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
-    if (a.sinks) {
-        m_run = a.sinks[head] * kLog2e;
-        l_run = h2 == 0 ? 1.f : 0.f;
-    }
 
     // LDS byte offsets of this lane's MFMA operand reads
     auto koff = [&](int ks) -> uint32_t { return n * ROWB + ((((ks * 2 + h2) ^ (n % NCH))) << 4); };
@@ -215,13 +216,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[mb][v]);
         } else {
+            // key j is visible iff (unsigned)(j - lo) <= (unsigned)(hi - lo).
+            // Rows that see nothing (hi < lo) get span 0 and offsets >= 1,
+            // which hides every key.  Selects, no branches.
+            const bool none = hi < lo;
+            const uint32_t span = none ? 0u : (uint32_t)(hi - lo);
+            const int jb = none ? 1 : j0 + h2 * 4 - lo;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int j = j0 + mb * 32 + (v >> 2) * 8 + h2 * 4 + (v & 3);
-                    if (j < lo || j > hi) S[mb][v] = -INFINITY;
-                    mx = fmaxf(mx, S[mb][v]);
+                    const uint32_t d = (uint32_t)(jb + mb * 32 + (v >> 2) * 8 + (v & 3));
+                    const float x = d > span ? -INFINITY : S[mb][v];
+                    S[mb][v] = x;
+                    mx = fmaxf(mx, x);
                 }
         }
         const float mx_c = halves_max(mx) * a.scale_log2;
@@ -268,6 +276,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         issue(0, false, sbase);
         issue(0, true, sbase + 2 * TILEB);
         if (ntiles > 1) issue(1, false, sbase + TILEB);
+    }
+    // the sink logit is read after the first tiles are in flight, so that
+    // its wait does not hold them back
+    if (a.sinks) {
+        m_run = a.sinks[head] * kLog2e;
+        l_run = h2 == 0 ? 1.f : 0.f;
     }
     wait_vmem();
     __syncthreads();
@@ -354,10 +368,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }  // namespace
 
 hipError_t launch_prefill_bf16(const AttnArgs &a, int head_dim, int mode, const int4 *items,
-                               const int32_t *count, int grid, hipStream_t s)
+                               const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s)
 {
     const dim3 g(grid), blk(256);
-#define VA_LAUNCH(DD, MM) hipLaunchKernelGGL((k1_prefill_bf16<DD, MM>), g, blk, 0, s, a, items, count)
+#define VA_LAUNCH(DD, MM) hipLaunchKernelGGL((k1_prefill_bf16<DD, MM>), g, blk, 0, s, a, items, seqinfo, count)
     if (head_dim == 128) {
         if (mode == kLoadBuffer) VA_LAUNCH(128, kLoadBuffer);
         else if (mode == kLoadGlobal) VA_LAUNCH(128, kLoadGlobal);

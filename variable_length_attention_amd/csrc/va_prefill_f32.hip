@@ -15,6 +15,7 @@ namespace {
 
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void k1_prefill_f32(AttnArgs a, const int4 *__restrict__ items,
+                                                      const int4 *__restrict__ seqinfo,
                                                       const int32_t *__restrict__ count)
 {
     constexpr int BN = kBNf32;
@@ -24,12 +25,13 @@ __global__ __launch_bounds__(256) void k1_prefill_f32(AttnArgs a, const int4 *__
 
     int item, head;
     map_block(blockIdx.x, a.H, item, head);
-    if (item >= *count) return;
+    const int n_items = *count;
     const int4 it = items[item];
+    const int4 si = seqinfo[item];
+    asm volatile("" ::"s"(it.x), "s"(si.x), "s"(n_items));
+    if (item >= n_items) return;
     const int b = it.x, i0 = it.y, kv_lo = it.z, kv_hi = it.w;
-    const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
-    const int Lk = PAGED ? a.seqused_k[b] : a.cu_k[b + 1] - a.cu_k[b];
-    const int k0 = PAGED ? 0 : a.cu_k[b];
+    const int q0 = si.x, Lq = si.y, k0 = si.z, Lk = si.w;
     const int c = head / a.g;
 
     const int tid = threadIdx.x, part = tid & 3;
@@ -129,15 +131,15 @@ __global__ __launch_bounds__(256) void k1_prefill_f32(AttnArgs a, const int4 *__
 }  // namespace
 
 hipError_t launch_prefill_f32(const AttnArgs &a, int head_dim, bool paged, const int4 *items,
-                              const int32_t *count, int grid, hipStream_t s)
+                              const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s)
 {
     const dim3 g(grid), blk(256);
     if (head_dim == 128) {
-        if (paged) hipLaunchKernelGGL((k1_prefill_f32<128, true>), g, blk, 0, s, a, items, count);
-        else hipLaunchKernelGGL((k1_prefill_f32<128, false>), g, blk, 0, s, a, items, count);
+        if (paged) hipLaunchKernelGGL((k1_prefill_f32<128, true>), g, blk, 0, s, a, items, seqinfo, count);
+        else hipLaunchKernelGGL((k1_prefill_f32<128, false>), g, blk, 0, s, a, items, seqinfo, count);
     } else {
-        if (paged) hipLaunchKernelGGL((k1_prefill_f32<64, true>), g, blk, 0, s, a, items, count);
-        else hipLaunchKernelGGL((k1_prefill_f32<64, false>), g, blk, 0, s, a, items, count);
+        if (paged) hipLaunchKernelGGL((k1_prefill_f32<64, true>), g, blk, 0, s, a, items, seqinfo, count);
+        else hipLaunchKernelGGL((k1_prefill_f32<64, false>), g, blk, 0, s, a, items, seqinfo, count);
     }
     return hipGetLastError();
 }
