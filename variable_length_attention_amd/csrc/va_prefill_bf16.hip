@@ -63,9 +63,44 @@ __device__ __forceinline__ float halves_sum(float x)
 // inside fp32 / bf16 range, and the O / l rescale is skipped.
 constexpr float kRescaleSlack = 8.f;
 
-// Waits until this wave's global->LDS loads have landed (vmcnt 0, other
-// counters left alone).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Global -> LDS copies of 16 bytes per lane (lane i writes LDS bytes
+// [lds + 16 i, lds + 16 i + 16)).  They are issued from inline assembly so
+// that the compiler's wait-count analysis does not see them: it would make
+// every transposing LDS read wait for all copies in flight, and the copies
+// are spread through the tile's compute (one between MFMA groups) instead
+// of being issued in a burst that stalls on the CU's address unit.  The
+// kernel orders copies and reads itself (a vector-memory wait and a barrier
+// before a slot is read; copies never target the slot being read).  The
+// instructions have no register results; M0 carries the LDS address
+// (uniform per wave).
+__device__ __forceinline__ void copy16_buffer(u32x4 rsrc, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds)
+                 : "m0");
+}
+__device__ __forceinline__ void copy16_global(const void *src, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)(p);
+}
+
+// Waits until at most N of this wave's vector-memory operations are still
+// in flight (they complete in issue order); other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep()
+{
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+__device__ __forceinline__ void wait_vmem() { wait_vmem_keep<0>(); }
 
 template <int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k1_prefill_bf16(
@@ -83,6 +118,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // LDS: K ring [K0 | K1] then V ring [V0 | V1]; tile t lives in slot t & 1
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TILEB];
     char *const sbase = (char *)smem;
+    char *const kring = sbase;
+    char *const vring = sbase + 2 * TILEB;
 
     int item, head;
     map_block(blockIdx.x, a.H, item, head);
@@ -138,30 +175,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int r = ld_row(u), p = lane % NCH;
         return is_v ? p ^ ((r % NSEG) << 2) : p ^ (r % NCH);
     };
-    auto issue = [&](int t, bool is_v, char *dst) {
+    // copy instruction u (rows (wave LPW + u) RPI ..) of tile t to dst.  A
+    // tile past the end (t >= ntiles) is harmless: buffer mode reads an
+    // empty range (zeros), the other modes re-read the last row; the
+    // destination slot is a free one either way.
+    // buffer mode: raw buffer over rows j0 .. kv_hi-1 of tile t (reads past
+    // the end return 0)
+    auto tile_rsrc = [&](int t, bool is_v) -> u32x4 {
         const int j0 = kv_lo + t * BN;
         const char *seq = is_v ? vseq : kseq;
+        const uint32_t nrec = j0 < kv_hi ? (uint32_t)((kv_hi - j0) * rowstride) : 0u;
+        const uint64_t addr = (uint64_t)(uintptr_t)(seq + j0 * rowstride);
+        return u32x4{(uint32_t)addr, (uint32_t)(addr >> 32) & 0xffffu, nrec, 0x00020000u};
+    };
+    auto issue_u = [&](int t, bool is_v, char *dst, int u, const u32x4 &rsrc) {
         if constexpr (MODE == kLoadBuffer) {
-            const uint32_t nrec = (uint32_t)((kv_hi - j0) * rowstride);
-            const __amdgpu_buffer_rsrc_t rs =
-                __builtin_amdgcn_make_buffer_rsrc((void *)(seq + j0 * rowstride), (short)0, nrec, 0x00020000);
-#pragma unroll
-            for (int u = 0; u < LPW; ++u) {
-                const uint32_t off = (uint32_t)(ld_row(u) * rowstride) + ld_chunk(u, is_v) * 16;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void *)(dst + (wave * LPW + u) * 1024), 16, off, 0, 0, 0);
-            }
+            (void)t;
+            const uint32_t off = (uint32_t)(ld_row(u) * rowstride) + ld_chunk(u, is_v) * 16;
+            copy16_buffer(rsrc, off, lds_addr(dst + (wave * LPW + u) * 1024));
         } else {
+            (void)rsrc;
+            const int j0 = kv_lo + t * BN;
             const uint16_t *base = (const uint16_t *)(is_v ? a.v : a.k);
-#pragma unroll
-            for (int u = 0; u < LPW; ++u) {
-                const int j = min(j0 + ld_row(u), kv_hi - 1);
-                const size_t off = kv_row_offset<D, MODE == kLoadPaged>(a, b, k0, c, j) + ld_chunk(u, is_v) * 8;
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)(base + off),
-                    (__attribute__((address_space(3))) void *)(dst + (wave * LPW + u) * 1024), 16, 0, 0);
-            }
+            const int j = min(j0 + ld_row(u), kv_hi - 1);
+            const size_t off = kv_row_offset<D, MODE == kLoadPaged>(a, b, k0, c, j) + ld_chunk(u, is_v) * 8;
+            copy16_global((const void *)(base + off), lds_addr(dst + (wave * LPW + u) * 1024));
         }
+    };
+    auto issue = [&](int t, bool is_v, char *dst) {
+        const u32x4 rsrc = MODE == kLoadBuffer ? tile_rsrc(t, is_v) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < LPW; ++u) issue_u(t, is_v, dst, u, rsrc);
     };
 
     // Q^T operand fragments: lane (row n, half h2) holds d = 16 ks + 8 h2 .. +8
@@ -194,7 +238,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     // ---- the three pieces of work per tile
     // S^T = K Q^T: lane value v of block mb is key j0 + 32 mb + 8 (v/4) + 4 h2 + v%4
-    auto qk = [&](f32x16 (&S)[2], const char *kt) {
+    auto qk = [&](f32x16 (&S)[2], const char *kt, auto &&hook) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) { S[0][v] = 0.f; S[1][v] = 0.f; }
 #pragma unroll
@@ -203,6 +247,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const bf16x8 kf1 = *(const bf16x8 *)(kt + koff(ks) + 32 * ROWB);
             S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[ks], S[0], 0, 0, 0);
             S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[ks], S[1], 0, 0, 0);
+            hook(ks);
         }
     };
     // mask (edge tiles only) and row max, then move the running max if the
@@ -273,9 +318,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // previous barrier) land before its closing barrier.
     f32x16 sa[2], sb[2];
     if (ntiles > 0) {
-        issue(0, false, sbase);
-        issue(0, true, sbase + 2 * TILEB);
-        if (ntiles > 1) issue(1, false, sbase + TILEB);
+        issue(0, false, kring);
+        issue(0, true, vring);
+        if (ntiles > 1) issue(1, false, kring + TILEB);
     }
     // the sink logit is read after the first tiles are in flight, so that
     // its wait does not hold them back
@@ -287,34 +332,52 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     bool vc = ntiles > 0 && visible(0);
     if (vc) {
-        qk(sa, sbase);
+        qk(sa, kring, [](int) {});
         row_max(sa, 0);
     }
     __syncthreads();  // K slot 0 is refilled by iteration 0
 
     auto iteration = [&](int t, auto BUFC, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
         constexpr int BUF = decltype(BUFC)::value;
-        char *k_next = sbase + (BUF ^ 1) * TILEB;          // K(t+1)
-        char *v_cur = sbase + 2 * TILEB + BUF * TILEB;     // V(t)
-        if (t + 2 < ntiles) issue(t + 2, false, sbase + BUF * TILEB);
-        if (t + 1 < ntiles) issue(t + 1, true, sbase + 2 * TILEB + (BUF ^ 1) * TILEB);
+        char *k_next = kring + (BUF ^ 1) * TILEB;         // K(t+1)
+        char *v_cur = vring + BUF * TILEB;                // V(t)
+        char *k_dst = kring + BUF * TILEB;                // K(t+2) goes where K(t) was
+        char *v_dst = vring + (BUF ^ 1) * TILEB;          // V(t+1) goes where V(t-1) was
         const bool vn = t + 1 < ntiles && visible(t + 1);
         const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-        float rs = 0.f;
-        bf16x8 p0, p1;
-        // QK^T of the next tile beside the first half of this tile's softmax
-        if (vn) qk(Sn, k_next);
+        // the copies for the coming tiles go out one at a time between the
+        // MFMA groups of this iteration (unconditionally: see issue_u)
+        constexpr int KEVERY = KS / LPW;
+        const u32x4 rs_k = MODE == kLoadBuffer ? tile_rsrc(t + 2, false) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 rs_v = MODE == kLoadBuffer ? tile_rsrc(t + 1, true) : u32x4{0u, 0u, 0u, 0u};
+        if (vn) {
+            qk(Sn, k_next, [&](int ks) {
+                if (ks % KEVERY == KEVERY - 1) issue_u(t + 2, false, k_dst, ks / KEVERY, rs_k);
+            });
+        } else {
+            issue(t + 2, false, k_dst);
+        }
         if (vc) {
-            p0 = probs(Sc, 0, neg_m, rs);
-            p1 = probs(Sc, 1, neg_m, rs);
-            // PV of this tile beside the second half of its softmax
+            constexpr int VEVERY = 4 / LPW;
+            auto vhook = [&](int t4) {
+                if (t4 % VEVERY == VEVERY - 1) issue_u(t + 1, true, v_dst, t4 / VEVERY, rs_v);
+            };
+            float rs = 0.f;
+            const bf16x8 p0 = probs(Sc, 0, neg_m, rs);
+            const bf16x8 p1 = probs(Sc, 1, neg_m, rs);
             pv(p0, 0, v_cur);
+            vhook(0);
             const bf16x8 p2 = probs(Sc, 2, neg_m, rs);
             pv(p1, 1, v_cur);
+            vhook(1);
             const bf16x8 p3 = probs(Sc, 3, neg_m, rs);
             pv(p2, 2, v_cur);
+            vhook(2);
             pv(p3, 3, v_cur);
+            vhook(3);
             l_run += rs;
+        } else {
+            issue(t + 1, true, v_dst);
         }
         if (vn) row_max(Sn, t + 1);
         vc = vn;
