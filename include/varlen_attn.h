@@ -44,11 +44,16 @@
  * Errors: every condition the host can check is checked before anything is
  * enqueued; a failing call launches nothing and writes nothing, returns a
  * non-zero va_status and leaves a message for varlen_attn_last_error().
- * Device-resident preconditions are NOT checked (checking would need a
- * synchronisation): cu_seqlens monotone with cu[batch] equal to the total,
- * every length <= the max_seqlen given, seqused_k[b] <= block_table_stride *
- * block_size, every block id used < num_blocks.  Violating them is undefined
- * behaviour.
+ * Device-resident preconditions are not checked by default (checking needs
+ * a synchronisation): cu_seqlens start at 0, never decrease and end at the
+ * row totals, every length <= the max_seqlen given, 0 <= seqused_k[b] <=
+ * block_table_stride * block_size, every block id used lies in
+ * [0, num_blocks).  Violating them is undefined behaviour.  With the
+ * environment variable VARLEN_ATTN_DEVICE_CHECK=1 (read on every call) each
+ * call first runs a device-side check of exactly these conditions on its
+ * stream, synchronises the stream, and returns VA_ERR_DEVICE_CHECK (nothing
+ * else enqueued, out / lse untouched; the workspace may have been written)
+ * when one fails.
  *
  * ABI rule: a shipped declaration never changes; a changed signature gets a
  * new _v2 name (the rule PyTorch applies to its stable C shim, per the pull
@@ -76,7 +81,7 @@ typedef enum {
     VA_ERR_ALIGN = 6,        /* a data pointer is not 16-byte aligned             */
     VA_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than required           */
     VA_ERR_HIP = 8,          /* a HIP runtime call or kernel launch failed        */
-    VA_ERR_DEVICE_CHECK = 9  /* reserved: opt-in device-side argument check       */
+    VA_ERR_DEVICE_CHECK = 9  /* opt-in device-side argument check failed (below)  */
 } va_status;
 
 typedef enum { VA_F32 = 0, VA_BF16 = 1 } va_dtype;

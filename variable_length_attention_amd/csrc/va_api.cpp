@@ -40,6 +40,14 @@ bool log_enabled()
     return on;
 }
 
+// VARLEN_ATTN_DEVICE_CHECK=1 turns on the device-side argument check (read
+// on every call so that it can be switched within a process).
+bool device_check_enabled()
+{
+    const char *e = std::getenv("VARLEN_ATTN_DEVICE_CHECK");
+    return e && e[0] == '1';
+}
+
 enum Path { kPathPrefill = 0, kPathDecode = 1, kPathF32 = 2 };
 
 struct Layout {
@@ -253,6 +261,40 @@ va::PlanArgs make_plan(const Call &c, const Layout &L, const va::AttnArgs &a)
     return pa;
 }
 
+// Device-side check of the argument contents; synchronises the stream.  The
+// result word lives in the workspace's item-count slot, which the pre-pass
+// overwrites afterwards.
+va_status device_check(const Call &c, const Layout &L, hipStream_t s)
+{
+    const va_problem *p = c.p;
+    va::CheckArgs ck;
+    ck.cu_q = c.cu_q;
+    ck.cu_k = c.paged ? nullptr : c.cu_k;
+    ck.seqused_k = c.paged ? c.seqused_k : nullptr;
+    ck.block_table = c.paged ? c.block_table : nullptr;
+    ck.B = p->batch; ck.total_q = p->total_q; ck.total_k = p->total_k;
+    ck.max_q = p->max_seqlen_q; ck.max_k = p->max_seqlen_k;
+    ck.bt_stride = c.paged ? p->block_table_stride : 0;
+    ck.block_size = c.paged ? p->block_size : 1;
+    ck.num_blocks = c.paged ? p->num_blocks : 0;
+    ck.flags = (uint32_t *)((char *)c.ws + L.off_count);
+    uint32_t flags = 0;
+    hipError_t e = va::launch_check(ck, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(&flags, ck.flags, 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(VA_ERR_HIP, "device check failed to run: %s", hipGetErrorString(e));
+    if (!flags) return VA_OK;
+    static const char *const what[] = {
+        "cu_seqlens_q[0] != 0", "cu_seqlens_q decreases", "cu_seqlens_q[batch] != total_q",
+        "a query length exceeds max_seqlen_q", "cu_seqlens_k[0] != 0", "cu_seqlens_k decreases",
+        "cu_seqlens_k[batch] != total_k", "a key length exceeds max_seqlen_k",
+        "seqused_k is negative or exceeds block_table_stride * block_size",
+        "a used block id is outside [0, num_blocks)"};
+    for (int i = 0; i < 10; ++i)
+        if (flags & (1u << i)) return fail(VA_ERR_DEVICE_CHECK, "device check: %s (flags 0x%x)", what[i], flags);
+    return fail(VA_ERR_DEVICE_CHECK, "device check failed (flags 0x%x)", flags);
+}
+
 // The one implementation behind every entry point.
 va_status run(const Call &c, hipStream_t s)
 {
@@ -263,6 +305,7 @@ va_status run(const Call &c, hipStream_t s)
     if ((st = check_pointers(c, L))) return st;
     const va::AttnArgs a = make_args(c);
     const va::PlanArgs pa = make_plan(c, L, a);
+    if (device_check_enabled() && (st = device_check(c, L, s))) return st;
     if (log_enabled())
         fprintf(stderr, "[varlen_attn] path=%s D=%d paged=%d B=%d H=%d Hkv=%d total_q=%d grid=%lld ws=%zu\n",
                 L.path == kPathPrefill ? "prefill_bf16" : L.path == kPathDecode ? "decode_bf16" : "f32",

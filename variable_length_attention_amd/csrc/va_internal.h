@@ -72,7 +72,31 @@ struct PlanArgs {
                                  //  first key row (contiguous; 0 paged), key rows)
 };
 
+// Opt-in device-side argument check (one bit per violated precondition).
+enum CheckFlag : uint32_t {
+    kChkCuQStart = 1u << 0,   // cu_seqlens_q[0] != 0
+    kChkCuQOrder = 1u << 1,   // cu_seqlens_q decreases
+    kChkCuQTotal = 1u << 2,   // cu_seqlens_q[B] != total_q
+    kChkLenQ = 1u << 3,       // a query length exceeds max_seqlen_q
+    kChkCuKStart = 1u << 4,   // cu_seqlens_k[0] != 0
+    kChkCuKOrder = 1u << 5,   // cu_seqlens_k decreases
+    kChkCuKTotal = 1u << 6,   // cu_seqlens_k[B] != total_k
+    kChkLenK = 1u << 7,       // a key length exceeds max_seqlen_k
+    kChkSeqused = 1u << 8,    // seqused_k < 0 or beyond its block-table row
+    kChkBlockId = 1u << 9,    // a used block id outside [0, num_blocks)
+};
+
+struct CheckArgs {
+    const int32_t *cu_q, *cu_k;        // cu_k null in paged mode
+    const int32_t *seqused_k;          // null in contiguous mode
+    const int32_t *block_table;
+    int32_t B, total_q, total_k, max_q, max_k;
+    int32_t bt_stride, block_size, num_blocks;
+    uint32_t *flags;                   // [1] result
+};
+
 // ---------------------------------------------------------------- launchers
+hipError_t launch_check(const CheckArgs &c, hipStream_t s);
 hipError_t launch_plan(const PlanArgs &pa, hipStream_t s);
 hipError_t launch_prefill_bf16(const AttnArgs &a, int head_dim, int mode, const int4 *items,
                                const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);
