@@ -6,6 +6,9 @@ and the benchmark's CPU-baseline leg do.  It shares no code with the HIP
 path: the only common module is the seeded input generator ``workloads``,
 which holds no attention arithmetic.
 
+* ``backward`` -- the double-precision C backward (the steps of the boostr
+  CPU backward ``varlen_attention_bwd``), given the forward's out and lse,
+  threaded over (sequence, kv head) units so the GQA sums need no locks.
 * ``forward`` / ``forward_rows`` -- the double-precision C implementation in
   ``varlen_oracle.c`` (a three-pass softmax per query row, in the order of
   the boostr CPU forward ``varlen_attention_fwd``), threaded over
@@ -66,6 +69,8 @@ def _load():
                                                    ctypes.c_int64, ctypes.c_void_p,
                                                    ctypes.c_void_p, ctypes.c_int]
             lib.oracle_varlen_fwd_rows.restype = ctypes.c_int
+            lib.oracle_varlen_bwd.argtypes = [ctypes.POINTER(_Args)] + [ctypes.c_void_p] * 6 + [ctypes.c_int]
+            lib.oracle_varlen_bwd.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -143,3 +148,25 @@ def forward_rows(case: dict, tokens, heads, nthreads: int | None = None):
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
     return out, lse
+
+
+def backward(case: dict, dout, out, lse, nthreads: int | None = None):
+    """Gradients of sum(dout * O) for a contiguous case, given the forward's
+    out [T_q, H, D] and lse [T_q, H] (any float arrays, used as float64).
+    Returns (dq [T_q, H, D], dk [T_k, Hkv, D], dv [T_k, Hkv, D]) in float64."""
+    if case.get("paged"):
+        raise ValueError("the backward oracle takes contiguous K/V")
+    lib = _load()
+    keep: list = []
+    a = _make_args(case, keep)
+    f = [np.ascontiguousarray(x, dtype=np.float64) for x in (dout, out, lse)]
+    T_k = int(np.asarray(case["cu_k"])[-1])
+    dq = np.zeros((case["T_q"], case["H"], case["D"]), dtype=np.float64)
+    dk = np.zeros((T_k, case["Hkv"], case["D"]), dtype=np.float64)
+    dv = np.zeros_like(dk)
+    rc = lib.oracle_varlen_bwd(ctypes.byref(a), f[0].ctypes.data, f[1].ctypes.data, f[2].ctypes.data,
+                               dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+                               nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (rc={rc})")
+    return dq, dk, dv

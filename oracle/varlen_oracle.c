@@ -31,6 +31,17 @@
  *     constraints and seqused_kv row).
  *
  * Inputs are float32 or raw bfloat16 bit patterns, widened exactly on the fly.
+ *
+ * The backward (oracle_varlen_bwd, contiguous K/V) follows the steps of the
+ * boostr CPU backward varlen_attention_bwd, given the forward's out and lse:
+ * for sequence b, query row i, head h (kv head c):
+ *   Dv   = sum_d dout[i,d] * out[i,d]
+ *   for every allowed key j:  s = scale <q_i, k_j>,  p = exp(s - lse_i),
+ *                             dp = <dout_i, v_j>,  ds = p (dp - Dv)
+ *                             dq_i += scale ds k_j,  dk_j += scale ds q_i,  dv_j += p dout_i
+ * dk and dv of kv head c sum over the H/H_kv query heads that share it.  The
+ * allowed-key set is the forward's (bottom-right causal, inclusive window);
+ * a sink only enters through lse (its own logit gets no gradient here).
  */
 #include <math.h>
 #include <pthread.h>
@@ -265,4 +276,87 @@ int oracle_varlen_fwd_rows(const oracle_args *a, const int64_t *pairs, int64_t n
     memset(&p, 0, sizeof p);
     p.a = a; p.pairs = pairs; p.n_pairs = n_pairs; p.out = out; p.lse = lse;
     return run_pool(&p, nthreads);
+}
+
+/* ---------------------------------------------------------------- backward */
+
+typedef struct {
+    const oracle_args *a;
+    const double *dout, *out, *lse;
+    double *dq, *dk, *dv;
+    int64_t n_units;   /* B * Hkv: one (sequence, kv head) per unit */
+    int64_t next;
+} bwd_pool_t;
+
+/* all query rows of sequence b and the query heads of kv head c */
+static void bwd_unit(const bwd_pool_t *p, int b, int c)
+{
+    const oracle_args *a = p->a;
+    const int D = a->D, g = a->H / a->Hkv;
+    const int Lq = a->cu_q[b + 1] - a->cu_q[b];
+    const int Lk = a->cu_k[b + 1] - a->cu_k[b];
+    const long delta = (long)Lk - (long)Lq;
+    for (int h = c * g; h < (c + 1) * g; ++h) {
+        for (int i = 0; i < Lq; ++i) {
+            const size_t t = (size_t)a->cu_q[b] + i;
+            const size_t qoff = (t * a->H + h) * (size_t)D;
+            const double l = p->lse[t * a->H + h];
+            double dv_row = 0.0;
+            for (int d = 0; d < D; ++d) dv_row += p->dout[qoff + d] * p->out[qoff + d];
+            for (int j = 0; j < Lk; ++j) {
+                if (!is_allowed(a, i, j, delta)) continue;
+                const size_t koff = kv_offset(a, b, j, c);
+                double s = 0.0, dp = 0.0;
+                for (int d = 0; d < D; ++d) {
+                    s += widen(a->dtype, a->q, qoff + d) * widen(a->dtype, a->k, koff + d);
+                    dp += p->dout[qoff + d] * widen(a->dtype, a->v, koff + d);
+                }
+                s *= a->scale;
+                const double pr = exp(s - l);
+                const double ds = pr * (dp - dv_row);
+                for (int d = 0; d < D; ++d) {
+                    p->dq[qoff + d] += a->scale * ds * widen(a->dtype, a->k, koff + d);
+                    p->dk[koff + d] += a->scale * ds * widen(a->dtype, a->q, qoff + d);
+                    p->dv[koff + d] += pr * p->dout[qoff + d];
+                }
+            }
+        }
+    }
+}
+
+static void *bwd_worker(void *arg)
+{
+    bwd_pool_t *p = (bwd_pool_t *)arg;
+    for (;;) {
+        int64_t u = __atomic_fetch_add(&p->next, 1, __ATOMIC_RELAXED);
+        if (u >= p->n_units) break;
+        bwd_unit(p, (int)(u / p->a->Hkv), (int)(u % p->a->Hkv));
+    }
+    return NULL;
+}
+
+/* Contiguous K/V only.  dout, out [T_q,H,D] and lse [T_q,H] in float64;
+ * dq [T_q,H,D], dk, dv [T_k,Hkv,D] float64, caller-allocated (zeroed here). */
+int oracle_varlen_bwd(const oracle_args *a, const double *dout, const double *out, const double *lse,
+                      double *dq, double *dk, double *dv, int nthreads)
+{
+    if (check_args(a) || a->block_table || !dout || !out || !lse || !dq || !dk || !dv) return -1;
+    const size_t Tq = a->B > 0 ? (size_t)a->cu_q[a->B] : 0, Tk = a->B > 0 ? (size_t)a->cu_k[a->B] : 0;
+    memset(dq, 0, sizeof(double) * Tq * a->H * a->D);
+    memset(dk, 0, sizeof(double) * Tk * a->Hkv * a->D);
+    memset(dv, 0, sizeof(double) * Tk * a->Hkv * a->D);
+    bwd_pool_t p;
+    memset(&p, 0, sizeof p);
+    p.a = a; p.dout = dout; p.out = out; p.lse = lse; p.dq = dq; p.dk = dk; p.dv = dv;
+    p.n_units = (int64_t)a->B * a->Hkv;
+    if (nthreads < 1) nthreads = 1;
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!th) return -2;
+    int started = 0;
+    for (int k = 0; k < nthreads; ++k)
+        if (pthread_create(&th[k], NULL, bwd_worker, &p) == 0) ++started;
+    if (started == 0) bwd_worker(&p);
+    for (int k = 0; k < started; ++k) pthread_join(th[k], NULL);
+    free(th);
+    return 0;
 }
