@@ -164,6 +164,28 @@ va_status varlen_attn_plan(const va_problem *p, int paged, const int32_t *cu_seq
                            int32_t *count, void *workspace, size_t workspace_bytes,
                            void *stream);
 
+/* Backward (bf16, contiguous K/V), following the boostr CPU backward
+ * varlen_attention_bwd: given dout [total_q, H, D] and the forward's out and
+ * lse (lse carries any sink), writes
+ *   dq [total_q, H, D] = scale * sum_j dS_ij k_j
+ *   dk [total_k, H_kv, D] = scale * sum_i dS_ij q_i,  dv [total_k, H_kv, D] = sum_i P_ij dout_i
+ * with P_ij = exp(scale <q_i, k_j> - lse_i) over the allowed keys of the
+ * forward (same causal / window arguments), dS_ij = P_ij (<dout_i, v_j> -
+ * sum_d dout_i,d out_i,d), and dk / dv of a kv head summed over the query
+ * heads that share it.  dq, dk, dv are in the input dtype (bf16; accumulated
+ * in float32) and fully overwritten; keys no query sees get zero gradients.
+ * The gradient of sink logits is not computed.  Same ownership, stream and
+ * error rules as the forward; dq, dk, dv may not overlap any input, the
+ * workspace or each other; p->dtype must be VA_BF16 (else
+ * VA_ERR_UNSUPPORTED).  `workspace` holds at least
+ * varlen_attn_bwd_workspace_size(p) bytes. */
+size_t varlen_attn_bwd_workspace_size(const va_problem *p);
+va_status varlen_attn_bwd(const va_problem *p, const void *dout, const void *q, const void *k,
+                          const void *v, const void *out, const float *lse,
+                          const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, void *dq,
+                          void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
 /* Which kernel family a call with these arguments would use:
  * 0 = prefill tiles, 1 = split-KV decode with combine, 2 = float32 path;
  * -1 if invalid. */

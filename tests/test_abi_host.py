@@ -141,3 +141,26 @@ def test_binding_raises_value_error_with_message():
         _lib.check(2)
     with pytest.raises(RuntimeError, match="VA_ERR_HIP"):
         _lib.check(8)
+
+
+def _bwd(p, dout=A[0], q=A[1], k=A[2], v=A[3], out=A[4], lse=A[5], cuq=A[6], cuk=A[7], dq=A[8],
+         dk=A[9], dv=A[10], ws=A[11], ws_bytes=1 << 30):
+    lib = _lib.load()
+    return lib.varlen_attn_bwd(ctypes.byref(p), dout, q, k, v, out, lse, cuq, cuk, dq, dk, dv, ws,
+                               ctypes.c_size_t(ws_bytes), None)
+
+
+def test_backward_rejects_before_launching():
+    lib = _lib.load()
+    p = _prob()
+    assert lib.varlen_attn_bwd_workspace_size(ctypes.byref(p)) > 4 * 100 * 8  # includes Dv [T_q, H]
+    assert lib.varlen_attn_bwd_workspace_size(ctypes.byref(_prob(dtype=0))) == 0
+    assert _bwd(_prob(dtype=0)) == 4                                   # float32: unsupported
+    assert _bwd(_prob(head_dim=96)) == 4
+    assert _bwd(p, dout=None) == 1
+    assert _bwd(p, lse=None) == 1
+    assert _bwd(p, dq=A[1]) == 5                                       # dq aliases q
+    assert _bwd(p, dv=ctypes.c_void_p(A[9].value + 256)) == 5          # dv inside dk
+    assert _bwd(p, dk=ctypes.c_void_p(A[9].value + 8)) == 6            # not 16-byte aligned
+    assert _bwd(p, ws_bytes=64) == 7
+    assert _bwd(p, ws=None) == 7

@@ -35,9 +35,9 @@ def _check_full(case, what):
 
 
 # ------------------------------------------------------------------ configs
-def test_config1_tiny_f32_full():
+def test_tiny_f32_causal_gqa_full():
     case = W.make_case(W.config(1))
-    e = _check_full(case, "config1 f32 causal gqa")
+    e = _check_full(case, "tiny_f32_causal_gqa (lengths 5, 17, 32)")
     assert e[0] <= 1e-5 and e[1] <= 1e-5
 
 

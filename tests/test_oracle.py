@@ -266,7 +266,7 @@ def _sweep_cases():
     return cases
 
 
-def test_oracle_matches_dense_bruteforce_config1():
+def test_oracle_matches_dense_bruteforce_tiny_f32_causal_gqa():
     case = W.make_case(W.config(1))
     out, lse = oracle.forward(case)
     out2, lse2 = brute.dense_forward(case)

@@ -24,7 +24,8 @@ VA_F32, VA_BF16 = 0, 1
 EXPORTED = [
     "varlen_attn_workspace_size", "varlen_attn_fwd_out", "varlen_attn_fwd",
     "varlen_attn_fwd_paged", "varlen_attn_free", "varlen_attn_plan", "varlen_attn_path",
-    "varlen_attn_last_error", "varlen_attn_abi_version",
+    "varlen_attn_last_error", "varlen_attn_abi_version", "varlen_attn_bwd_workspace_size",
+    "varlen_attn_bwd",
 ]
 
 
@@ -76,6 +77,10 @@ def load():
         lib.varlen_attn_path.restype = ctypes.c_int
         lib.varlen_attn_last_error.argtypes = []
         lib.varlen_attn_last_error.restype = ctypes.c_char_p
+        lib.varlen_attn_bwd_workspace_size.argtypes = [P]
+        lib.varlen_attn_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.varlen_attn_bwd.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, vp]
+        lib.varlen_attn_bwd.restype = ctypes.c_int
         lib.varlen_attn_abi_version.argtypes = []
         lib.varlen_attn_abi_version.restype = ctypes.c_int
         _lib = lib

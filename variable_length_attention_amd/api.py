@@ -24,7 +24,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["varlen_attn", "varlen_attn_out", "varlen_attn_paged", "varlen_attn_fwd",
+__all__ = ["varlen_attn", "varlen_attn_out", "varlen_attn_paged", "varlen_attn_fwd", "varlen_attn_bwd",
+           "bwd_workspace_size",
            "workspace_size", "plan", "kernel_path", "output_shapes", "make_problem"]
 
 _DTYPES = {torch.float32: _lib.VA_F32, torch.bfloat16: _lib.VA_BF16}
@@ -222,3 +223,37 @@ def plan(cu_seqlens_q, seqlens_k, *, num_heads, num_kv_heads, head_dim, dtype, t
     _lib.check(st)
     n = int(count.item())
     return items[:n].clone(), kernel_path(p, paged)
+
+
+def bwd_workspace_size(problem: _lib.VaProblem) -> int:
+    return int(_lib.load().varlen_attn_bwd_workspace_size(ctypes.byref(problem)))
+
+
+def varlen_attn_bwd(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                    max_seqlen_k: int, *, scale: Optional[float] = None, causal: bool = False,
+                    window: Tuple[int, int] = (-1, -1), dq=None, dk=None, dv=None, workspace=None):
+    """Backward of varlen_attn for bf16 contiguous K/V: returns (dq, dk, dv)
+    (allocated when not given) from dout and the forward's out / lse."""
+    dev = _check_tensors(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, dq, dk, dv, workspace)
+    _need(dout.shape == q.shape and out.shape == q.shape, "dout and out must have q's shape")
+    _need(k.dim() == 3 and v.shape == k.shape, "k and v must be [total_k, num_kv_heads, head_dim]")
+    _need(lse.dtype == torch.float32 and tuple(lse.shape) == (q.shape[0], q.shape[1]),
+          "lse must be float32 [total_q, num_heads]")
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32, "cu_seqlens must be int32")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape, "gradient shapes")
+    p = make_problem(q, k.shape[1], k.shape[0], cu_seqlens_q.numel() - 1, max_seqlen_q, max_seqlen_k,
+                     scale, causal, window)
+    need = bwd_workspace_size(p)
+    if need == 0:
+        _lib.check(_lib.load().varlen_attn_bwd(ctypes.byref(p), *([None] * 12), ctypes.c_size_t(0), None))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = _lib.load().varlen_attn_bwd(
+        ctypes.byref(p), _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_k), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+        _stream(dev))
+    _lib.check(st)
+    return dq, dk, dv

@@ -332,9 +332,139 @@ va_status run(const Call &c, hipStream_t s)
     return VA_OK;
 }
 
+// ---------------------------------------------------------------- backward
+// Workspace: the two pre-pass plans (query blocks for dQ, key blocks for
+// dK / dV) and Dv [T_q, H] fp32.
+struct PlanRegion {
+    size_t count = 0, seq = 0, unsorted = 0, cost = 0, items = 0, seqinfo = 0;
+    int n_max = 0;
+    long long grid = 0;
+};
+struct BwdLayout {
+    PlanRegion qp, kp;
+    size_t dvec = 0;
+    size_t total = 0;
+};
+
+size_t plan_region(size_t off, int B, int n_max, PlanRegion &r)
+{
+    r.n_max = n_max;
+    r.count = off; off = align_up(off + 4, 256);
+    r.seq = off; off = align_up(off + 4 * ((size_t)B + 1), 256);
+    r.unsorted = off; off = align_up(off + 16 * (size_t)n_max, 256);
+    r.cost = off; off = align_up(off + 4 * (size_t)n_max, 256);
+    r.items = off; off = align_up(off + 16 * (size_t)n_max, 256);
+    r.seqinfo = off; off = align_up(off + 16 * (size_t)n_max, 256);
+    return off;
+}
+
+va_status bwd_layout(const va_problem *p, BwdLayout &L)
+{
+    va_status st = check_problem(p, 0);
+    if (st) return st;
+    if (p->dtype != VA_BF16) return fail(VA_ERR_UNSUPPORTED, "the backward takes bf16 inputs");
+    const long long nq = ((long long)p->total_q + (long long)p->batch * (va::kBM - 1)) / va::kBM;
+    const long long nk = ((long long)p->total_k + (long long)p->batch * (va::kBwdKeys - 1)) / va::kBwdKeys;
+    const long long gq = nq * p->num_heads, gk = nk * p->num_kv_heads;
+    if (gq > 0x7fffffffLL || gk > 0x7fffffffLL)
+        return fail(VA_ERR_UNSUPPORTED, "problem needs %lld workgroups, above the launch limit", gq > gk ? gq : gk);
+    size_t off = plan_region(0, p->batch, (int)nq, L.qp);
+    off = plan_region(off, p->batch, (int)nk, L.kp);
+    L.qp.grid = gq;
+    L.kp.grid = gk;
+    L.dvec = off; off = align_up(off + 4 * (size_t)p->total_q * p->num_heads, 256);
+    L.total = off;
+    return VA_OK;
+}
+
+va::PlanArgs bwd_plan(const va_problem *p, const int32_t *cu_q, const int32_t *cu_k, const va::BwdArgs &a,
+                      char *ws, const PlanRegion &r, int mode)
+{
+    va::PlanArgs pa;
+    pa.cu_q = cu_q;
+    pa.lens_k = cu_k;
+    pa.lens_k_is_prefix = 1;
+    pa.B = p->batch; pa.Hkv = p->num_kv_heads;
+    pa.left = a.left; pa.right = a.right;
+    pa.mode = mode;
+    pa.bm = mode == va::kPlanBwdKeys ? va::kBwdKeys : va::kBM;
+    pa.bn = mode == va::kPlanBwdKeys ? va::kBwdQT : va::kBN;
+    pa.n_max = r.n_max;
+    pa.count = (int32_t *)(ws + r.count);
+    pa.seq_off = (int32_t *)(ws + r.seq);
+    pa.unsorted = (int4 *)(ws + r.unsorted);
+    pa.cost = (int32_t *)(ws + r.cost);
+    pa.items = (int4 *)(ws + r.items);
+    pa.seqinfo = (int4 *)(ws + r.seqinfo);
+    return pa;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t varlen_attn_bwd_workspace_size(const va_problem *p)
+{
+    BwdLayout L;
+    if (bwd_layout(p, L)) return 0;
+    return L.total;
+}
+
+va_status varlen_attn_bwd(const va_problem *p, const void *dout, const void *q, const void *k,
+                          const void *v, const void *out, const float *lse,
+                          const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, void *dq,
+                          void *dk, void *dv, void *workspace, size_t workspace_bytes, void *stream)
+{
+    BwdLayout L;
+    va_status st = bwd_layout(p, L);
+    if (st) return st;
+    if (!dout || !q || !k || !v || !out || !lse || !cu_seqlens_q || !cu_seqlens_k || !dq || !dk || !dv)
+        return fail(VA_ERR_NULL, "dout, q, k, v, out, lse, cu_seqlens_q/k, dq, dk and dv must be non-NULL");
+    if (!workspace || workspace_bytes < L.total)
+        return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                    workspace_bytes, L.total);
+    const void *al16[] = {dout, q, k, v, out, dq, dk, dv, workspace};
+    for (const void *ptr : al16)
+        if (!aligned(ptr, 16)) return fail(VA_ERR_ALIGN, "data pointers and the workspace must be 16-byte aligned");
+    if (!aligned(lse, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+        return fail(VA_ERR_ALIGN, "lse and cu_seqlens must be 4-byte aligned");
+    const size_t D = (size_t)p->head_dim;
+    const size_t qb = (size_t)p->total_q * p->num_heads * D * 2;
+    const size_t kb = (size_t)p->total_k * p->num_kv_heads * D * 2;
+    const Range outs[] = {{dq, qb}, {dk, kb}, {dv, kb}};
+    const Range ins[] = {{dout, qb}, {q, qb}, {k, kb}, {v, kb}, {out, qb},
+                         {lse, (size_t)p->total_q * p->num_heads * 4},
+                         {cu_seqlens_q, 4 * ((size_t)p->batch + 1)}, {cu_seqlens_k, 4 * ((size_t)p->batch + 1)},
+                         {workspace, workspace_bytes}};
+    for (int i = 0; i < 3; ++i) {
+        for (const Range &r : ins)
+            if (overlaps(outs[i], r)) return fail(VA_ERR_ALIAS, "dq, dk and dv must not overlap an input or the workspace");
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], outs[j])) return fail(VA_ERR_ALIAS, "dq, dk and dv must not overlap each other");
+    }
+    va::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.dout = dout; a.out = out; a.lse = lse;
+    char *ws = (char *)workspace;
+    a.dvec = (float *)(ws + L.dvec);
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.H = p->num_heads; a.Hkv = p->num_kv_heads; a.g = p->num_heads / p->num_kv_heads;
+    a.left = p->window_left >= 0 ? p->window_left : va::kInfOff;
+    if (p->causal) a.right = 0;
+    else a.right = p->window_right >= 0 ? p->window_right : va::kInfOff;
+    a.scale = p->scale;
+    a.scale_log2 = p->scale * va::kLog2e;
+    hipStream_t s = (hipStream_t)stream;
+    const va::PlanArgs pq = bwd_plan(p, cu_seqlens_q, cu_seqlens_k, a, ws, L.qp, va::kPlanPrefill);
+    const va::PlanArgs pk = bwd_plan(p, cu_seqlens_q, cu_seqlens_k, a, ws, L.kp, va::kPlanBwdKeys);
+    hipError_t e = va::launch_plan(pq, s);
+    if (e == hipSuccess) e = va::launch_plan(pk, s);
+    if (e == hipSuccess)
+        e = va::launch_backward_bf16(a, p->head_dim, p->total_q, pq.items, pq.seqinfo, pq.count, (int)L.qp.grid,
+                                     pk.items, pk.seqinfo, pk.count, (int)L.kp.grid, s);
+    if (e != hipSuccess) return fail(VA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return VA_OK;
+}
+
 
 int varlen_attn_abi_version(void) { return VARLEN_ATTN_ABI_VERSION; }
 

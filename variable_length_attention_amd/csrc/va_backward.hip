@@ -1,0 +1,535 @@
+// bf16 backward of the varlen attention forward on gfx950 matrix cores.
+//
+// Method: the steps of the boostr CPU backward varlen_attention_bwd, given
+// the forward's out and lse (a sink enters only through lse):
+//   Dv_i = sum_d dO_i,d O_i,d
+//   P_ij = exp(scale <q_i, k_j> - lse_i)            (allowed keys only)
+//   dP_ij = <dO_i, v_j>,  dS_ij = P_ij (dP_ij - Dv_i)
+//   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i
+// with dK / dV of a kv head summed over the query heads that share it.
+//
+// Three kernels, none with atomics (results are deterministic):
+//   B0 k_bwd_dot   Dv for every (row, head), fp32.
+//   B1 k_bwd_dq    one workgroup per (128-row query block, head), the work
+//                  items of the forward: per 64-key tile S^T = K Q^T and
+//                  dP^T = V dO^T (Q^T, dO^T in registers), dS^T from them,
+//                  dQ^T += K^T dS^T through transposing LDS reads.
+//   B2 k_bwd_dkdv  one workgroup per (128-key block, kv head); each wave
+//                  keeps its 32 keys' K and V operands in registers and
+//                  streams 64-row Q / dO tiles of every query head of the
+//                  GQA group: S = Q K^T, dP = dO V^T, dV^T += dO^T P and
+//                  dK^T += Q^T dS (keys on the MFMA N side).
+// K, V, Q and dO tiles are read both row-wise (16-byte operand reads) and
+// transposed (ds_read_b64_tr_b16); one XOR swizzle of the 16-byte chunks
+// serves both without bank conflicts.
+#include "va_internal.h"
+
+#include <type_traits>
+
+namespace va {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const char *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)((__attribute__((address_space(3))) char *)(p)));
+}
+
+// Physical 16-byte chunk of logical chunk c in LDS row r is c ^ swz(r).
+// For 256-byte rows (D = 128) the 16 rows of a row-wise operand read get 16
+// distinct chunks, and the 4 consecutive rows x 4 consecutive chunks of a
+// transposing read get 16 distinct chunks; for 128-byte rows (D = 64) the
+// same holds per pair of rows sharing a 256-byte bank line.
+template <int D>
+__device__ __forceinline__ int swz(int r)
+{
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// Global -> LDS copies of 16 bytes per lane (lane i writes LDS bytes
+// [lds + 16 i, +16)), issued from inline assembly so that the compiler's
+// wait-count analysis does not make the transposing reads wait for copies
+// of other slots; the kernels order copies and reads themselves (a
+// vector-memory wait and a barrier before a slot is read).  No register
+// results; M0 carries the LDS address (uniform per wave).
+__device__ __forceinline__ void copy16_buffer(u32x4 rsrc, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds)
+                 : "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)(p);
+}
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// raw buffer over `rows` rows of `rowstride` bytes from base (reads past
+// the end return 0)
+__device__ __forceinline__ u32x4 rows_rsrc(const void *base, int rows, size_t rowstride)
+{
+    const uint32_t nrec = rows > 0 ? (uint32_t)((size_t)rows * rowstride) : 0u;
+    const uint64_t addr = (uint64_t)(uintptr_t)base;
+    return u32x4{(uint32_t)addr, (uint32_t)(addr >> 32) & 0xffffu, nrec, 0x00020000u};
+}
+
+// Copies a tile of 64 rows x D (row-major, `rowstride` bytes apart, rows
+// past `rows` read as zero) into LDS at dst with the swizzle above; the 4
+// waves take 16 rows each.
+template <int D>
+__device__ __forceinline__ void copy_tile(const char *src, int rows, size_t rowstride, char *dst, int wave, int lane)
+{
+    constexpr int NCH = D / 8, RPI = 64 / NCH, LPW = 64 / RPI / 4;
+    const u32x4 rs = rows_rsrc(src, rows < 64 ? rows : 64, rowstride);
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+        const int r = (wave * LPW + u) * RPI + lane / NCH;
+        const int chunk = (lane % NCH) ^ swz<D>(r);
+        copy16_buffer(rs, (uint32_t)(r * rowstride) + chunk * 16, lds_addr(dst + (wave * LPW + u) * 1024));
+    }
+}
+
+// bf16 pairs of a 32-bit word widened to fp32
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// ------------------------------------------------------------------ B0
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_dot(const uint16_t *__restrict__ dout, const uint16_t *__restrict__ out,
+                                                 float *__restrict__ dvec, int rows)
+{
+    constexpr int LPR = D / 8;        // lanes per (row, head), 16 bytes each
+    constexpr int RPB = 256 / LPR;    // (row, head) pairs per workgroup
+    const int r = blockIdx.x * RPB + threadIdx.x / LPR;
+    const int l = threadIdx.x % LPR;
+    float acc = 0.f;
+    if (r < rows) {
+        const u32x4 x = *(const u32x4 *)(dout + (size_t)r * D + l * 8);
+        const u32x4 y = *(const u32x4 *)(out + (size_t)r * D + l * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc += bf_lo(x[e]) * bf_lo(y[e]) + bf_hi(x[e]) * bf_hi(y[e]);
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (l == 0 && r < rows) dvec[r] = acc;
+}
+
+// ------------------------------------------------------------------ B1
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dq(
+    BwdArgs a, const int4 *__restrict__ items, const int4 *__restrict__ seqinfo, const int32_t *__restrict__ count)
+{
+    constexpr int BN = 64;
+    constexpr int NCH = D / 8;
+    constexpr int KS = D / 16;
+    constexpr int MD = D / 32;
+    constexpr int ROWB = D * 2;
+    constexpr int TILEB = BN * ROWB;
+    // LDS: K ring [K0 | K1] then V ring [V0 | V1]; tile t in slot t & 1
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TILEB];
+    char *const kring = (char *)smem;
+    char *const vring = kring + 2 * TILEB;
+
+    int item, head;
+    map_block(blockIdx.x, a.H, item, head);
+    const int n_items = *count;
+    const int4 it = items[item];
+    const int4 si = seqinfo[item];
+    asm volatile("" ::"s"(it.x), "s"(si.x), "s"(n_items));
+    if (item >= n_items) return;
+    const int i0 = it.y, kv_lo = it.z, kv_hi = it.w;
+    const int q0 = si.x, Lq = si.y, k0 = si.z, Lk = si.w;
+    const int delta = Lk - Lq;
+    const int c = head / a.g;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, h2 = lane >> 5, l16 = lane & 15, q4 = l16 >> 2;
+    const int row = i0 + wave * 32 + n;
+    const bool row_ok = row < Lq;
+    int lo = 1, hi = 0;
+    if (row_ok) row_bounds(row, delta, Lk, a.left, a.right, lo, hi);
+    int wlo = 1, whi = 0, flo = 0x7fffffff, fhi = -1;
+    {
+        const int w0 = i0 + wave * 32, w1 = min(w0 + 31, Lq - 1);
+        if (w0 < Lq) {
+            int l0, h0, l1, h1;
+            row_bounds(w0, delta, Lk, a.left, a.right, l0, h0);
+            row_bounds(w1, delta, Lk, a.left, a.right, l1, h1);
+            wlo = l0; whi = h1; flo = l1; fhi = h0;
+        }
+    }
+    const int ntiles = (kv_hi - kv_lo + BN - 1) / BN;
+    auto visible = [&](int t) {
+        const int j0 = kv_lo + t * BN;
+        return wlo <= whi && j0 <= whi && j0 + BN - 1 >= wlo;
+    };
+
+    const size_t rowstride = (size_t)a.Hkv * D * 2;
+    const char *kseq = (const char *)a.k + ((size_t)k0 * a.Hkv + c) * D * 2;
+    const char *vseq = (const char *)a.v + ((size_t)k0 * a.Hkv + c) * D * 2;
+    auto issue = [&](int t, char *kdst, char *vdst) {
+        const int j0 = kv_lo + t * BN;
+        copy_tile<D>(kseq + (size_t)j0 * rowstride, kv_hi - j0, rowstride, kdst, wave, lane);
+        copy_tile<D>(vseq + (size_t)j0 * rowstride, kv_hi - j0, rowstride, vdst, wave, lane);
+    };
+
+    // Q^T and dO^T operand fragments: lane (row n, half h2) holds d = 16 ks + 8 h2 .. +8
+    bf16x8 qf[KS], df[KS];
+    {
+        const size_t off = ((size_t)(q0 + (row_ok ? row : 0)) * a.H + head) * D + h2 * 8;
+        const uint16_t *qp = (const uint16_t *)a.q + off;
+        const uint16_t *dp = (const uint16_t *)a.dout + off;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 x = *(const u32x4 *)(qp + ks * 16);
+            u32x4 y = *(const u32x4 *)(dp + ks * 16);
+            if (!row_ok) { x = u32x4{0, 0, 0, 0}; y = u32x4{0, 0, 0, 0}; }
+            qf[ks] = __builtin_bit_cast(bf16x8, x);
+            df[ks] = __builtin_bit_cast(bf16x8, y);
+        }
+    }
+    // lse in log2 units; rows without any allowed key (lse = -inf) and rows
+    // past the end get +inf, which makes every probability 0
+    float lse2 = INFINITY, dvr = 0.f;
+    if (row_ok) {
+        const size_t ri = (size_t)(q0 + row) * a.H + head;
+        const float l = a.lse[ri];
+        lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+        dvr = a.dvec[ri];
+    }
+
+    f32x16 dqa[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dqa[md][v] = 0.f;
+
+    // LDS byte offsets: row-wise operand read of row n, chunk 2 ks + h2; and
+    // the transposing read of rows 16 t4 + 4 h2 + q4 (+8), 4 columns at
+    // md * 32 + 16 ((lane & 31) >> 4) + 4 (l16 & 3)
+    auto koff = [&](int ks) -> uint32_t { return n * ROWB + (((ks * 2 + h2) ^ swz<D>(n)) << 4); };
+    auto toff = [&](int md, int half) -> uint32_t {
+        const int r = h2 * 4 + q4 + half * 8;
+        const int col = md * 32 + ((lane & 31) >> 4) * 16 + (l16 & 3) * 4;
+        return r * ROWB + (((col >> 3) ^ swz<D>(r)) << 4) + (col & 7) * 2;
+    };
+
+    if (ntiles > 0) issue(0, kring, vring);
+    wait_vmem();
+    __syncthreads();
+
+    auto tile = [&](int t, auto BUFC) {
+        constexpr int BUF = decltype(BUFC)::value;
+        const char *kt = kring + BUF * TILEB;
+        const char *vt = vring + BUF * TILEB;
+        if (t + 1 < ntiles) issue(t + 1, kring + (BUF ^ 1) * TILEB, vring + (BUF ^ 1) * TILEB);
+        if (visible(t)) {
+            const int j0 = kv_lo + t * BN;
+            // S^T = K Q^T, dP^T = V dO^T: lane value v of block mb is key
+            // j0 + 32 mb + 8 (v/4) + 4 h2 + v%4 of query row n
+            f32x16 S[2], P[2];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) { S[0][v] = 0.f; S[1][v] = 0.f; P[0][v] = 0.f; P[1][v] = 0.f; }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 k0f = *(const bf16x8 *)(kt + koff(ks));
+                const bf16x8 k1f = *(const bf16x8 *)(kt + koff(ks) + 32 * ROWB);
+                const bf16x8 v0f = *(const bf16x8 *)(vt + koff(ks));
+                const bf16x8 v1f = *(const bf16x8 *)(vt + koff(ks) + 32 * ROWB);
+                S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[ks], S[0], 0, 0, 0);
+                S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[ks], S[1], 0, 0, 0);
+                P[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0f, df[ks], P[0], 0, 0, 0);
+                P[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1f, df[ks], P[1], 0, 0, 0);
+            }
+            if (!(j0 >= flo && j0 + BN - 1 <= fhi)) {
+                // key j is allowed iff (unsigned)(j - lo) <= (unsigned)(hi - lo)
+                const bool none = hi < lo;
+                const uint32_t span = none ? 0u : (uint32_t)(hi - lo);
+                const int jb = none ? 1 : j0 + h2 * 4 - lo;
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const uint32_t d = (uint32_t)(jb + mb * 32 + (v >> 2) * 8 + (v & 3));
+                        S[mb][v] = d > span ? -INFINITY : S[mb][v];
+                    }
+            }
+            // dS^T in bf16, laid out as the B operand of step t4 (keys 16 t4 ..)
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4) {
+                f32x8 x;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int ix = (t4 & 1) * 8 + e;
+                    const float p = __builtin_amdgcn_exp2f(fmaf(S[t4 >> 1][ix], a.scale_log2, -lse2));
+                    x[e] = p * (P[t4 >> 1][ix] - dvr);
+                }
+                const bf16x8 dsb = __builtin_convertvector(x, bf16x8);
+                // dQ^T += K^T dS^T
+#pragma unroll
+                for (int md = 0; md < MD; ++md) {
+                    const bf16x4 ka = lds_read_tr(kt + toff(md, 0) + t4 * 16 * ROWB);
+                    const bf16x4 kb = lds_read_tr(kt + toff(md, 1) + t4 * 16 * ROWB);
+                    const bf16x8 kf = __builtin_shufflevector(ka, kb, 0, 1, 2, 3, 4, 5, 6, 7);
+                    dqa[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, dsb, dqa[md], 0, 0, 0);
+                }
+            }
+        }
+        wait_vmem();
+        __syncthreads();
+    };
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+        tile(t, std::integral_constant<int, 0>{});
+        tile(t + 1, std::integral_constant<int, 1>{});
+    }
+    if (t < ntiles) tile(t, std::integral_constant<int, 0>{});
+
+    // epilogue: lane (row n, half h2) holds dQ^T[32 md + 8 i + 4 h2 + j][row];
+    // rows leave through LDS as whole 16-byte-per-lane rows
+    char *ow = kring + wave * 32 * ROWB;  // chunk XOR (row mod NCH)
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = dqa[md][i * 4 + j] * a.scale;
+            const bf16x4 y = __builtin_convertvector(x, bf16x4);
+            const int phys = (md * 4 + i) ^ (n % NCH);
+            *(u32x2 *)(ow + n * ROWB + phys * 16 + h2 * 8) = __builtin_bit_cast(u32x2, y);
+        }
+    __syncthreads();
+    {
+        constexpr int RPW = 64 / NCH;
+        const int cidx = lane % NCH;
+#pragma unroll
+        for (int u = 0; u < 32 / RPW; ++u) {
+            const int r = u * RPW + lane / NCH;
+            const int orow = i0 + wave * 32 + r;
+            const u32x4 v = *(const u32x4 *)(ow + r * ROWB + ((cidx ^ (r % NCH)) << 4));
+            if (orow < Lq)
+                *(u32x4 *)((uint16_t *)a.dq + ((size_t)(q0 + orow) * a.H + head) * D + cidx * 8) = v;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ B2
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd_dkdv(
+    BwdArgs a, const int4 *__restrict__ items, const int4 *__restrict__ seqinfo, const int32_t *__restrict__ count)
+{
+    constexpr int QT = 64;             // query rows per tile
+    constexpr int KS = D / 16;
+    constexpr int MD = D / 32;
+    constexpr int ROWB = D * 2;
+    constexpr int TILEB = QT * ROWB;
+    // LDS: Q ring [Q0 | Q1], dO ring [O0 | O1], then per slot 64 lse2 and 64 Dv
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TILEB];
+    __shared__ __attribute__((aligned(16))) float s_rows[2][2][QT];
+    char *const qring = (char *)smem;
+    char *const oring = qring + 2 * TILEB;
+
+    int item, c;
+    map_block(blockIdx.x, a.Hkv, item, c);
+    const int n_items = *count;
+    const int4 it = items[item];
+    const int4 si = seqinfo[item];
+    asm volatile("" ::"s"(it.x), "s"(si.x), "s"(n_items));
+    if (item >= n_items) return;
+    const int j0 = it.y, qlo = it.z, qhi = it.w;
+    const int q0 = si.x, Lq = si.y, k0 = si.z, Lk = si.w;
+    const int delta = Lk - Lq;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, h2 = lane >> 5, l16 = lane & 15, q4 = l16 >> 2;
+    // this lane's key (MFMA column) and the wave's 32 keys
+    const int key = j0 + wave * 32 + n;
+    const bool key_ok = key < Lk;
+
+    // K^T and V^T operand fragments (B side): lane (key n, half h2) holds d = 16 ks + 8 h2 .. +8
+    bf16x8 kf[KS], vf[KS];
+    {
+        const size_t off = ((size_t)(k0 + (key_ok ? key : 0)) * a.Hkv + c) * D + h2 * 8;
+        const uint16_t *kp = (const uint16_t *)a.k + off;
+        const uint16_t *vp = (const uint16_t *)a.v + off;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 x = *(const u32x4 *)(kp + ks * 16);
+            u32x4 y = *(const u32x4 *)(vp + ks * 16);
+            if (!key_ok) { x = u32x4{0, 0, 0, 0}; y = u32x4{0, 0, 0, 0}; }
+            kf[ks] = __builtin_bit_cast(bf16x8, x);
+            vf[ks] = __builtin_bit_cast(bf16x8, y);
+        }
+    }
+    f32x16 dka[MD], dva[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { dka[md][v] = 0.f; dva[md][v] = 0.f; }
+
+    // allowed (query i, key j): j - i in [delta - left, delta + right], j < Lk
+    const long long dlo = a.left >= kInfOff ? -(1ll << 40) : (long long)delta - a.left;
+    const long long dhi = a.right >= kInfOff ? (1ll << 40) : (long long)delta + a.right;
+
+    const size_t qstride = (size_t)a.H * D * 2;
+    const int qtiles = (qhi - qlo + QT - 1) / QT;
+    const int total = qtiles * a.g;  // (head of the group, query tile) steps
+    // step s: head c g + s / qtiles, query rows qlo + QT (s % qtiles) ..
+    // step s: copies of its Q / dO tiles into slot `slot`; its per-row lse
+    // (log2 units; +inf for rows past the range or without keys) and Dv are
+    // read into registers here and written to LDS by row_store() at the end
+    // of the current step, so that waiting for them never waits for copies
+    float st_l2 = INFINITY, st_dv = 0.f;
+    auto issue = [&](int s, int slot) {
+        const int h = c * a.g + s / qtiles;
+        const int r0 = qlo + (s % qtiles) * QT;
+        const size_t off = ((size_t)(q0 + r0) * a.H + h) * D * 2;
+        copy_tile<D>((const char *)a.q + off, qhi - r0, qstride, qring + slot * TILEB, wave, lane);
+        copy_tile<D>((const char *)a.dout + off, qhi - r0, qstride, oring + slot * TILEB, wave, lane);
+        st_l2 = INFINITY;
+        st_dv = 0.f;
+        const int r = r0 + tid;
+        if (tid < QT && r < qhi) {
+            const size_t ri = (size_t)(q0 + r) * a.H + h;
+            const float l = a.lse[ri];
+            st_l2 = l == -INFINITY ? INFINITY : l * kLog2e;
+            st_dv = a.dvec[ri];
+        }
+    };
+    auto row_store = [&](int slot) {
+        if (tid < QT) {
+            s_rows[slot][0][tid] = st_l2;
+            s_rows[slot][1][tid] = st_dv;
+        }
+    };
+
+    // LDS offsets: row-wise operand read of query row mb * 32 + n, chunk
+    // 2 ks + h2; transposing read of rows 16 t4 + 4 h2 + q4 (+8)
+    auto roff = [&](int ks) -> uint32_t { return n * ROWB + (((ks * 2 + h2) ^ swz<D>(n)) << 4); };
+    auto toff = [&](int md, int half) -> uint32_t {
+        const int r = h2 * 4 + q4 + half * 8;
+        const int col = md * 32 + ((lane & 31) >> 4) * 16 + (l16 & 3) * 4;
+        return r * ROWB + (((col >> 3) ^ swz<D>(r)) << 4) + (col & 7) * 2;
+    };
+
+    if (total > 0) {
+        issue(0, 0);
+        row_store(0);
+    }
+    wait_vmem();
+    __syncthreads();
+    for (int s = 0; s < total; ++s) {
+        const int slot = s & 1;
+        const bool more = s + 1 < total;
+        if (more) issue(s + 1, slot ^ 1);
+        const char *qt = qring + slot * TILEB;
+        const char *ot = oring + slot * TILEB;
+        const int r0 = qlo + (s % qtiles) * QT;
+#pragma unroll
+        for (int mb = 0; mb < QT / 32; ++mb) {
+            // S = Q K^T, dP = dO V^T for 32 query rows: lane value v is query
+            // r0 + 32 mb + 8 (v/4) + 4 h2 + v%4 of this lane's key
+            f32x16 S, P;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) { S[v] = 0.f; P[v] = 0.f; }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 qa = *(const bf16x8 *)(qt + mb * 32 * ROWB + roff(ks));
+                const bf16x8 oa = *(const bf16x8 *)(ot + mb * 32 * ROWB + roff(ks));
+                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S, 0, 0, 0);
+                P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], P, 0, 0, 0);
+            }
+            // probabilities and dS for this block, then the two products
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int t4 = mb * 2 + half;  // 16-row step of the tile
+                f32x8 pv, dsv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int v = half * 8 + e;
+                    const int qi = 32 * mb + (v >> 2) * 8 + h2 * 4 + (v & 3);  // row within the tile
+                    const float l2 = s_rows[slot][0][qi];
+                    const float dv = s_rows[slot][1][qi];
+                    const long long dd = (long long)key - (r0 + qi);
+                    const bool ok = key_ok && dd >= dlo && dd <= dhi;
+                    const float p = ok ? __builtin_amdgcn_exp2f(fmaf(S[v], a.scale_log2, -l2)) : 0.f;
+                    pv[e] = p;
+                    dsv[e] = p * (P[v] - dv);
+                }
+                const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
+                const bf16x8 db = __builtin_convertvector(dsv, bf16x8);
+#pragma unroll
+                for (int md = 0; md < MD; ++md) {
+                    const bf16x4 oa = lds_read_tr(ot + toff(md, 0) + t4 * 16 * ROWB);
+                    const bf16x4 ob = lds_read_tr(ot + toff(md, 1) + t4 * 16 * ROWB);
+                    const bf16x4 qa = lds_read_tr(qt + toff(md, 0) + t4 * 16 * ROWB);
+                    const bf16x4 qb = lds_read_tr(qt + toff(md, 1) + t4 * 16 * ROWB);
+                    const bf16x8 of = __builtin_shufflevector(oa, ob, 0, 1, 2, 3, 4, 5, 6, 7);
+                    const bf16x8 qf = __builtin_shufflevector(qa, qb, 0, 1, 2, 3, 4, 5, 6, 7);
+                    dva[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, pb, dva[md], 0, 0, 0);
+                    dka[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, db, dka[md], 0, 0, 0);
+                }
+            }
+        }
+        if (more) row_store(slot ^ 1);  // the next step's slot is not read in this step
+        wait_vmem();
+        __syncthreads();
+    }
+
+    // epilogue: lane (key n, half h2) holds d = 32 md + 8 i + 4 h2 .. +4 of
+    // its key's dK^T / dV^T column: 8-byte stores
+    if (key_ok) {
+        const size_t base = ((size_t)(k0 + key) * a.Hkv + c) * D;
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4 x, y;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    x[j] = dka[md][i * 4 + j] * a.scale;
+                    y[j] = dva[md][i * 4 + j];
+                }
+                const int d = md * 32 + i * 8 + h2 * 4;
+                *(u32x2 *)((uint16_t *)a.dk + base + d) = __builtin_bit_cast(u32x2, __builtin_convertvector(x, bf16x4));
+                *(u32x2 *)((uint16_t *)a.dv + base + d) = __builtin_bit_cast(u32x2, __builtin_convertvector(y, bf16x4));
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_backward_bf16(const BwdArgs &a, int head_dim, int total_q, const int4 *q_items,
+                                const int4 *q_seqinfo, const int32_t *q_count, int q_grid,
+                                const int4 *k_items, const int4 *k_seqinfo, const int32_t *k_count,
+                                int k_grid, hipStream_t s)
+{
+    const int rows = total_q * a.H;
+    if (head_dim == 128) {
+        hipLaunchKernelGGL(k_bwd_dot<128>, dim3((rows + 15) / 16), dim3(256), 0, s,
+                           (const uint16_t *)a.dout, (const uint16_t *)a.out, a.dvec, rows);
+        hipLaunchKernelGGL(k_bwd_dq<128>, dim3(q_grid), dim3(256), 0, s, a, q_items, q_seqinfo, q_count);
+        hipLaunchKernelGGL(k_bwd_dkdv<128>, dim3(k_grid), dim3(256), 0, s, a, k_items, k_seqinfo, k_count);
+    } else {
+        hipLaunchKernelGGL(k_bwd_dot<64>, dim3((rows + 31) / 32), dim3(256), 0, s,
+                           (const uint16_t *)a.dout, (const uint16_t *)a.out, a.dvec, rows);
+        hipLaunchKernelGGL(k_bwd_dq<64>, dim3(q_grid), dim3(256), 0, s, a, q_items, q_seqinfo, q_count);
+        hipLaunchKernelGGL(k_bwd_dkdv<64>, dim3(k_grid), dim3(256), 0, s, a, k_items, k_seqinfo, k_count);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace va

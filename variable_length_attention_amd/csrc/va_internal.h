@@ -25,6 +25,8 @@ constexpr int kCostBins = 4096;        // cost classes of the pre-pass ordering
 constexpr int kSortMax = 2048;         // pre-pass sorts up to this many items in LDS
 constexpr int kRankSortMax = 1024;     // ... by ranking (no barriers) up to this many
 constexpr int kPlanSeqs = 2048;        // pre-pass keeps up to this many sequences' lengths in LDS
+constexpr int kBwdKeys = 128;          // backward: key rows per dK/dV workgroup
+constexpr int kBwdQT = 64;             // backward: query rows per dK/dV tile
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -46,7 +48,11 @@ struct AttnArgs {
     float scale, scale_log2;     // scale and scale * log2(e)
 };
 
-enum PlanMode : int32_t { kPlanPrefill = 0, kPlanDecode = 1 };
+// Prefill: items are (sequence, block of bm query rows) with their key range.
+// Decode: (sequence, split of the visible keys).  Backward key blocks:
+// (sequence, block of bm key rows) with the range of query rows that see
+// any of those keys.
+enum PlanMode : int32_t { kPlanPrefill = 0, kPlanDecode = 1, kPlanBwdKeys = 2 };
 
 // How the prefill kernel fetches K/V rows: buffer loads over one
 // sequence's rows (contiguous, every sequence span below 2 GiB), plain
@@ -60,8 +66,8 @@ struct PlanArgs {
     int32_t B, Hkv;
     int32_t left, right;
     int32_t mode;                // PlanMode
-    int32_t bm;                  // prefill: rows per item
-    int32_t bn;                  // prefill: key rows per tile (cost unit)
+    int32_t bm;                  // prefill: query rows per item; backward: key rows per item
+    int32_t bn;                  // prefill: key rows per tile; backward: query rows per tile (cost unit)
     int32_t n_max;               // capacity of the item arrays
     int32_t *count;              // [1] number of items written
     int32_t *seq_off;            // [B+1] first item (prefill) / first split slot (decode)
@@ -70,6 +76,17 @@ struct PlanArgs {
     int4 *items;                 // [n_max] sorted, execution order
     int4 *seqinfo;               // [n_max] per item: (first query row, query rows,
                                  //  first key row (contiguous; 0 paged), key rows)
+};
+
+// Backward (bf16, contiguous K/V).
+struct BwdArgs {
+    const void *q, *k, *v, *dout, *out;
+    const float *lse;            // [T_q, H] from the forward
+    float *dvec;                 // [T_q, H] workspace: sum_d dout * out
+    void *dq, *dk, *dv;
+    int32_t H, Hkv, g;
+    int32_t left, right;         // as in AttnArgs
+    float scale, scale_log2;
 };
 
 // Opt-in device-side argument check (one bit per violated precondition).
@@ -97,6 +114,10 @@ struct CheckArgs {
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_check(const CheckArgs &c, hipStream_t s);
+hipError_t launch_backward_bf16(const BwdArgs &a, int head_dim, int total_q, const int4 *q_items,
+                                const int4 *q_seqinfo, const int32_t *q_count, int q_grid,
+                                const int4 *k_items, const int4 *k_seqinfo, const int32_t *k_count,
+                                int k_grid, hipStream_t s);
 hipError_t launch_plan(const PlanArgs &pa, hipStream_t s);
 hipError_t launch_prefill_bf16(const AttnArgs &a, int head_dim, int mode, const int4 *items,
                                const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);

@@ -129,6 +129,8 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
         if (b < a.B) {
             if (a.mode == kPlanPrefill) {
                 n = (q_len(b) + a.bm - 1) / a.bm;
+            } else if (a.mode == kPlanBwdKeys) {
+                n = (k_len(b) + a.bm - 1) / a.bm;  // every key block, even with no query rows
             } else {
                 int lo, hi;
                 vis_range(b, lo, hi);
@@ -167,6 +169,20 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
             if (Lk > 0) rows_range(i0, i1, Lk - Lq, Lk, a.left, a.right, lo, hi);
             cost = (hi - lo + a.bn - 1) / a.bn;
             return make_int4(b, i0, lo, hi);
+        }
+        if (a.mode == kPlanBwdKeys) {
+            // query rows i that see a key of [j0, j1): i + delta + right >= j0
+            // and i + delta - left <= j1 - 1 (right = 0 when causal)
+            const int Lq = q_len(b), Lk = k_len(b);
+            const int j0 = s * a.bm, j1 = min(Lk, j0 + a.bm);
+            const long long delta = (long long)Lk - Lq;
+            long long qlo = 0, qhi = Lq;
+            if (a.right < kInfOff) qlo = max(qlo, (long long)j0 - delta - a.right);
+            if (a.left < kInfOff) qhi = min(qhi, (long long)j1 - 1 - delta + a.left + 1);
+            qlo = min(qlo, (long long)Lq);
+            if (qhi < qlo) qhi = qlo;
+            cost = (int)((qhi - qlo + a.bn - 1) / a.bn);
+            return make_int4(b, j0, (int)qlo, (int)qhi);
         }
         int lo, hi;
         vis_range(b, lo, hi);
