@@ -23,11 +23,16 @@ SOURCES = ["va_api.cpp", "va_plan.hip", "va_prefill_bf16.hip", "va_prefill_f32.h
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-command-line-argument"]
+# Per-file device options.  The backward's dK/dV kernel keeps its
+# accumulators in AGPRs through inline assembly and needs every other
+# matrix instruction in the VGPR form (the backend otherwise picks the AGPR
+# form for a whole kernel that may use more than 256 registers).
+EXTRA = {"va_backward.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

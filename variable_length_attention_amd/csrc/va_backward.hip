@@ -99,6 +99,29 @@ __device__ __forceinline__ void copy_tile(const char *src, int rows, size_t rows
     }
 }
 
+// acc += A B on the matrix cores with the accumulator held in AGPRs (the
+// dK / dV kernel keeps 256 accumulator registers there and everything else
+// in VGPRs).  Written in assembly because the compiler selects one register
+// form for all of a kernel's matrix instructions.  The leading s_nop covers
+// the two wait states a matrix instruction needs after a VALU write of its
+// A / B operand (the compiler does not see into the block).
+__device__ __forceinline__ void mfma_agpr(f32x16 &acc, bf16x8 a, bf16x8 b)
+{
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last matrix instruction into acc and any other
+// read of it (VALU, LDS or memory instructions read AGPRs only after the
+// matrix pipeline has written them back; 16 passes need 18).
+__device__ __forceinline__ void mfma_agpr_drain(f32x16 &acc)
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc));
+}
+
+// Keeps the computation of x at this point of the instruction stream (an
+// empty volatile statement that reads and writes it; arithmetic without
+// side effects is otherwise free to sink towards its uses).
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
+
 // bf16 pairs of a 32-bit word widened to fp32
 __device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
@@ -335,11 +358,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int MD = D / 32;
     constexpr int ROWB = D * 2;
     constexpr int TILEB = QT * ROWB;
-    // LDS: Q ring [Q0 | Q1], dO ring [O0 | O1], then per slot 64 lse2 and 64 Dv
+    // LDS: Q ring [Q0 | Q1], dO ring [O0 | O1], the block's 128 V rows, then
+    // per slot 64 lse2 and 64 Dv
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TILEB];
+    __shared__ __attribute__((aligned(16))) uint16_t s_v[kBwdKeys * D];
     __shared__ __attribute__((aligned(16))) float s_rows[2][2][QT];
     char *const qring = (char *)smem;
     char *const oring = qring + 2 * TILEB;
+    char *const vt = (char *)s_v;
 
     int item, c;
     map_block(blockIdx.x, a.Hkv, item, c);
@@ -355,34 +381,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, h2 = lane >> 5, l16 = lane & 15, q4 = l16 >> 2;
-    // this lane's key (MFMA column) and the wave's 32 keys
-    const int key = j0 + wave * 32 + n;
-    const bool key_ok = key < Lk;
+    // wave (kh, rh): keys j0 + 64 kh .. +64 (two MFMA column blocks kb), query
+    // rows 32 rh .. +32 of every tile; the two waves of one kh add their
+    // partial dK / dV at the end
+    const int kh = wave & 1, rh = wave >> 1;
+    int keyv[2];
+    bool key_ok[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        keyv[kb] = j0 + kh * 64 + kb * 32 + n;
+        key_ok[kb] = keyv[kb] < Lk;
+    }
 
-    // K^T and V^T operand fragments (B side): lane (key n, half h2) holds d = 16 ks + 8 h2 .. +8
-    bf16x8 kf[KS], vf[KS];
-    {
-        const size_t off = ((size_t)(k0 + (key_ok ? key : 0)) * a.Hkv + c) * D + h2 * 8;
+    // K^T operand fragments (B side) in registers: lane (key n, half h2)
+    // holds d = 16 ks + 8 h2 .. +8; the V rows of the block go to LDS (the
+    // dP products read them from there: registers are short)
+    bf16x8 kf[2][KS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const size_t off = ((size_t)(k0 + (key_ok[kb] ? keyv[kb] : 0)) * a.Hkv + c) * D + h2 * 8;
         const uint16_t *kp = (const uint16_t *)a.k + off;
-        const uint16_t *vp = (const uint16_t *)a.v + off;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 x = *(const u32x4 *)(kp + ks * 16);
-            u32x4 y = *(const u32x4 *)(vp + ks * 16);
-            if (!key_ok) { x = u32x4{0, 0, 0, 0}; y = u32x4{0, 0, 0, 0}; }
-            kf[ks] = __builtin_bit_cast(bf16x8, x);
-            vf[ks] = __builtin_bit_cast(bf16x8, y);
+            if (!key_ok[kb]) x = u32x4{0, 0, 0, 0};
+            kf[kb][ks] = __builtin_bit_cast(bf16x8, x);
         }
     }
-    f32x16 dka[MD], dva[MD];
+    {
+        const size_t kvstride = (size_t)a.Hkv * D * 2;
+        const char *vsrc = (const char *)a.v + ((size_t)(k0 + j0) * a.Hkv + c) * D * 2;
+        copy_tile<D>(vsrc, Lk - j0, kvstride, vt, wave, lane);
+        copy_tile<D>(vsrc + 64 * kvstride, Lk - j0 - 64, kvstride, vt + 64 * ROWB, wave, lane);
+    }
+    f32x16 dka[MD][2], dva[MD][2];
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) { dka[md][v] = 0.f; dva[md][v] = 0.f; }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) { dka[md][kb][v] = 0.f; dva[md][kb][v] = 0.f; }
 
-    // allowed (query i, key j): j - i in [delta - left, delta + right], j < Lk
+    // allowed (query i, key j): j - i in [delta - left, delta + right], j < Lk;
+    // for each of this lane's keys: rows [rlo, rlo + rspan] (none past Lk)
     const long long dlo = a.left >= kInfOff ? -(1ll << 40) : (long long)delta - a.left;
     const long long dhi = a.right >= kInfOff ? (1ll << 40) : (long long)delta + a.right;
+    int rlo[2];
+    uint32_t rspan[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        rlo[kb] = (int)max((long long)keyv[kb] - dhi, -1ll);
+        const int rhi = (int)min((long long)keyv[kb] - dlo, (long long)kMaxSeqlen);
+        rspan[kb] = (uint32_t)(rhi - rlo[kb]);
+        if (!key_ok[kb] || rhi < rlo[kb]) { rlo[kb] = kMaxSeqlen + 1; rspan[kb] = 0; }  // rows < kMaxSeqlen
+    }
 
     const size_t qstride = (size_t)a.H * D * 2;
     const int qtiles = (qhi - qlo + QT - 1) / QT;
@@ -393,12 +445,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // read into registers here and written to LDS by row_store() at the end
     // of the current step, so that waiting for them never waits for copies
     float st_l2 = INFINITY, st_dv = 0.f;
+    auto tile_row = [&](int s) { return qlo + (s % qtiles) * QT; };
+    auto tile_head = [&](int s) { return c * a.g + s / qtiles; };
+    // copies of step s's tiles: KS parts of one 16-byte-per-lane copy each
+    // (Q rows, then dO rows), issued one at a time between the matrix
+    // instructions of the previous step; with no step s the buffers are
+    // empty (nothing is read, the slot gets zeros)
+    constexpr int NCH = D / 8, RPI = 64 / NCH, LPW = 64 / RPI / 4;
+    static_assert(2 * LPW == KS, "one copy part per K step");
+    u32x4 rs_q = {0, 0, 0, 0}, rs_o = {0, 0, 0, 0};
+    int cp_slot = 0;
+    auto copy_setup = [&](int s, int slot) {
+        const int rows = s < total ? min(qhi - tile_row(s), QT) : 0;
+        const size_t off = s < total ? ((size_t)(q0 + tile_row(s)) * a.H + tile_head(s)) * D * 2 : 0;
+        rs_q = rows_rsrc((const char *)a.q + off, rows, qstride);
+        rs_o = rows_rsrc((const char *)a.dout + off, rows, qstride);
+        cp_slot = slot;
+    };
+    auto copy_part = [&](int part) {
+        const int u = part % LPW;
+        const int r = (wave * LPW + u) * RPI + lane / NCH;
+        const int chunk = (lane % NCH) ^ swz<D>(r);
+        char *dst = (part < LPW ? qring : oring) + cp_slot * TILEB + (wave * LPW + u) * 1024;
+        copy16_buffer(part < LPW ? rs_q : rs_o, (uint32_t)(r * qstride) + chunk * 16, lds_addr(dst));
+    };
     auto issue = [&](int s, int slot) {
-        const int h = c * a.g + s / qtiles;
-        const int r0 = qlo + (s % qtiles) * QT;
-        const size_t off = ((size_t)(q0 + r0) * a.H + h) * D * 2;
-        copy_tile<D>((const char *)a.q + off, qhi - r0, qstride, qring + slot * TILEB, wave, lane);
-        copy_tile<D>((const char *)a.dout + off, qhi - r0, qstride, oring + slot * TILEB, wave, lane);
+        const int h = tile_head(s);
+        const int r0 = tile_row(s);
         st_l2 = INFINITY;
         st_dv = 0.f;
         const int r = r0 + tid;
@@ -416,16 +489,180 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     };
 
-    // LDS offsets: row-wise operand read of query row mb * 32 + n, chunk
+    // LDS offsets: row-wise operand read of query row 32 rh + n, chunk
     // 2 ks + h2; transposing read of rows 16 t4 + 4 h2 + q4 (+8)
-    auto roff = [&](int ks) -> uint32_t { return n * ROWB + (((ks * 2 + h2) ^ swz<D>(n)) << 4); };
+    auto roff = [&](int ks) -> uint32_t {
+        const int r = rh * 32 + n;
+        return r * ROWB + (((ks * 2 + h2) ^ swz<D>(r)) << 4);
+    };
     auto toff = [&](int md, int half) -> uint32_t {
         const int r = h2 * 4 + q4 + half * 8;
         const int col = md * 32 + ((lane & 31) >> 4) * 16 + (l16 & 3) * 4;
         return r * ROWB + (((col >> 3) ^ swz<D>(r)) << 4) + (col & 7) * 2;
     };
 
+    // V row-wise operand read of key kh 64 + kb 32 + n, chunk 2 ks + h2
+    auto voff = [&](int kb, int ks) -> uint32_t {
+        const int r = kh * 64 + kb * 32 + n;
+        return r * ROWB + (((ks * 2 + h2) ^ swz<D>(r)) << 4);
+    };
+    // a query tile starting at row r0 needs no mask when every (row, key) of
+    // it is allowed (rows past the range carry lse = +inf and drop out)
+    const bool keys_full = j0 + kBwdKeys <= Lk;
+    auto tile_full = [&](int r0) {
+        return keys_full && (long long)j0 - (r0 + QT - 1) >= dlo && (long long)j0 + kBwdKeys - 1 - r0 <= dhi;
+    };
+
+    // one step: lane value v of block kb is row 32 rh + 8 (v/4) + 4 h2 + v%4
+    // of the tile and key keyv[kb]
+    auto step = [&](int slot, int r0, bool full) {
+        const char *qt = qring + slot * TILEB;
+        const char *ot = oring + slot * TILEB;
+        const float *l2s = s_rows[slot][0];
+        const float *dvs = s_rows[slot][1];
+        // S = Q K^T
+        f32x16 S[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) S[kb][v] = 0.f;
+        // all Q operands first: one LDS latency for the 2 KS products
+        bf16x8 qa[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qa[ks] = *(const bf16x8 *)(qt + roff(ks));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[0][ks], S[0], 0, 0, 0);
+            S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[1][ks], S[1], 0, 0, 0);
+        }
+        if (!full) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int base = r0 + rh * 32 + h2 * 4 - rlo[kb];
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    S[kb][v] = (uint32_t)(base + (v >> 2) * 8 + (v & 3)) <= rspan[kb] ? S[kb][v] : -INFINITY;
+            }
+        }
+        f32x4 l2r[4], dvr[4];
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            l2r[e4] = *(const f32x4 *)(l2s + rh * 32 + e4 * 8 + h2 * 4);
+            dvr[e4] = *(const f32x4 *)(dvs + rh * 32 + e4 * 8 + h2 * 4);
+        }
+        // dP = dO V^T, interleaved with the probabilities (in place in S):
+        // each matrix instruction is followed by 16 / KS exponentials; the
+        // scheduling fences keep that order (one wave per SIMD: the overlap
+        // of matrix and vector work has to come from the instruction order)
+        f32x16 P[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) P[kb][v] = 0.f;
+        auto prob = [&](int idx) {
+            const int kb = idx >> 4, v = idx & 15;
+            float p = __builtin_amdgcn_exp2f(fmaf(S[kb][v], a.scale_log2, -l2r[v >> 2][v & 3]));
+            pin(p);
+            S[kb][v] = p;
+        };
+        bf16x8 oa = *(const bf16x8 *)(ot + roff(0));
+        bf16x8 v0 = *(const bf16x8 *)(vt + voff(0, 0));
+        bf16x8 v1 = *(const bf16x8 *)(vt + voff(1, 0));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 oc = oa, vc0 = v0, vc1 = v1;
+            if (ks + 1 < KS) {
+                oa = *(const bf16x8 *)(ot + roff(ks + 1));
+                v0 = *(const bf16x8 *)(vt + voff(0, ks + 1));
+                v1 = *(const bf16x8 *)(vt + voff(1, ks + 1));
+            }
+            // 32 values over 2 KS matrix instructions
+            constexpr int EPS = 16 / KS;
+            static_assert(2 * KS * EPS == 32, "every probability gets a slot");
+            copy_part(ks);
+            P[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oc, vc0, P[0], 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < EPS; ++e) prob((ks * 2) * EPS + e);
+            __builtin_amdgcn_sched_barrier(0);
+            P[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oc, vc1, P[1], 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < EPS; ++e) prob((ks * 2 + 1) * EPS + e);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // bf16 probabilities: the dV operand
+        bf16x8 pb[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                f32x8 x;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = S[kb][half * 8 + e];
+                pb[kb][half] = __builtin_convertvector(x, bf16x8);
+            }
+        // dV^T += dO^T P over this wave's 32 rows, interleaved with
+        // dS = P (dP - Dv) (in place in P)
+        auto dsm = [&](int idx) {
+            const int kb = idx >> 4, v = idx & 15;
+            float d = S[kb][v] * (P[kb][v] - dvr[v >> 2][v & 3]);
+            pin(d);
+            P[kb][v] = d;
+        };
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int t4 = rh * 2 + half;  // 16-row step of the tile
+#pragma unroll
+            for (int md = 0; md < MD; ++md) {
+                const bf16x4 ta = lds_read_tr(ot + toff(md, 0) + t4 * 16 * ROWB);
+                const bf16x4 tb = lds_read_tr(ot + toff(md, 1) + t4 * 16 * ROWB);
+                const bf16x8 of = __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7);
+                // 32 values over 4 MD matrix instructions
+                constexpr int EPD = 8 / MD;
+                static_assert(4 * MD * EPD == 32, "every dS value gets a slot");
+                const int sl = (half * MD + md) * 2;
+                mfma_agpr(dva[md][0], of, pb[0][half]);
+#pragma unroll
+                for (int e = 0; e < EPD; ++e) dsm(sl * EPD + e);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_agpr(dva[md][1], of, pb[1][half]);
+#pragma unroll
+                for (int e = 0; e < EPD; ++e) dsm((sl + 1) * EPD + e);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        bf16x8 db[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                f32x8 x;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = P[kb][half * 8 + e];
+                db[kb][half] = __builtin_convertvector(x, bf16x8);
+            }
+        // dK^T += Q^T dS
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int t4 = rh * 2 + half;
+            bf16x8 qf[MD];
+#pragma unroll
+            for (int md = 0; md < MD; ++md) {
+                const bf16x4 ta = lds_read_tr(qt + toff(md, 0) + t4 * 16 * ROWB);
+                const bf16x4 tb = lds_read_tr(qt + toff(md, 1) + t4 * 16 * ROWB);
+                qf[md] = __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+#pragma unroll
+            for (int md = 0; md < MD; ++md)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) mfma_agpr(dka[md][kb], qf[md], db[kb][half]);
+        }
+    };
+
     if (total > 0) {
+        copy_setup(0, 0);
+#pragma unroll
+        for (int part = 0; part < KS; ++part) copy_part(part);
         issue(0, 0);
         row_store(0);
     }
@@ -434,80 +671,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int s = 0; s < total; ++s) {
         const int slot = s & 1;
         const bool more = s + 1 < total;
+        copy_setup(s + 1, slot ^ 1);
         if (more) issue(s + 1, slot ^ 1);
-        const char *qt = qring + slot * TILEB;
-        const char *ot = oring + slot * TILEB;
-        const int r0 = qlo + (s % qtiles) * QT;
-#pragma unroll
-        for (int mb = 0; mb < QT / 32; ++mb) {
-            // S = Q K^T, dP = dO V^T for 32 query rows: lane value v is query
-            // r0 + 32 mb + 8 (v/4) + 4 h2 + v%4 of this lane's key
-            f32x16 S, P;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) { S[v] = 0.f; P[v] = 0.f; }
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 qa = *(const bf16x8 *)(qt + mb * 32 * ROWB + roff(ks));
-                const bf16x8 oa = *(const bf16x8 *)(ot + mb * 32 * ROWB + roff(ks));
-                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], S, 0, 0, 0);
-                P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], P, 0, 0, 0);
-            }
-            // probabilities and dS for this block, then the two products
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int t4 = mb * 2 + half;  // 16-row step of the tile
-                f32x8 pv, dsv;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int v = half * 8 + e;
-                    const int qi = 32 * mb + (v >> 2) * 8 + h2 * 4 + (v & 3);  // row within the tile
-                    const float l2 = s_rows[slot][0][qi];
-                    const float dv = s_rows[slot][1][qi];
-                    const long long dd = (long long)key - (r0 + qi);
-                    const bool ok = key_ok && dd >= dlo && dd <= dhi;
-                    const float p = ok ? __builtin_amdgcn_exp2f(fmaf(S[v], a.scale_log2, -l2)) : 0.f;
-                    pv[e] = p;
-                    dsv[e] = p * (P[v] - dv);
-                }
-                const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
-                const bf16x8 db = __builtin_convertvector(dsv, bf16x8);
-#pragma unroll
-                for (int md = 0; md < MD; ++md) {
-                    const bf16x4 oa = lds_read_tr(ot + toff(md, 0) + t4 * 16 * ROWB);
-                    const bf16x4 ob = lds_read_tr(ot + toff(md, 1) + t4 * 16 * ROWB);
-                    const bf16x4 qa = lds_read_tr(qt + toff(md, 0) + t4 * 16 * ROWB);
-                    const bf16x4 qb = lds_read_tr(qt + toff(md, 1) + t4 * 16 * ROWB);
-                    const bf16x8 of = __builtin_shufflevector(oa, ob, 0, 1, 2, 3, 4, 5, 6, 7);
-                    const bf16x8 qf = __builtin_shufflevector(qa, qb, 0, 1, 2, 3, 4, 5, 6, 7);
-                    dva[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, pb, dva[md], 0, 0, 0);
-                    dka[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, db, dka[md], 0, 0, 0);
-                }
-            }
-        }
+        const int r0 = tile_row(s);
+        step(slot, r0, tile_full(r0));
         if (more) row_store(slot ^ 1);  // the next step's slot is not read in this step
         wait_vmem();
         __syncthreads();
     }
 
-    // epilogue: lane (key n, half h2) holds d = 32 md + 8 i + 4 h2 .. +4 of
-    // its key's dK^T / dV^T column: 8-byte stores
-    if (key_ok) {
-        const size_t base = ((size_t)(k0 + key) * a.Hkv + c) * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            mfma_agpr_drain(dka[md][kb]);
+            mfma_agpr_drain(dva[md][kb]);
+        }
+
+    // epilogue: the waves of rows 32..63 hand their dK partials to the waves
+    // of rows 0..31 through LDS (then the reverse for dV); lane (key n, half
+    // h2) holds d = 32 md + 8 i + 4 h2 .. +4 of its keys' dK^T / dV^T columns
+    f32x4 *xch = (f32x4 *)smem + (size_t)kh * (MD * 2 * 4 * 64);  // [md][kb][i][lane]
+    auto put = [&](f32x16 (&acc)[MD][2]) {
 #pragma unroll
         for (int md = 0; md < MD; ++md)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f32x4 x, y;
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    x[j] = dka[md][i * 4 + j] * a.scale;
-                    y[j] = dva[md][i * 4 + j];
+                for (int i = 0; i < 4; ++i)
+                    xch[((md * 2 + kb) * 4 + i) * 64 + lane] =
+                        f32x4{acc[md][kb][i * 4], acc[md][kb][i * 4 + 1], acc[md][kb][i * 4 + 2], acc[md][kb][i * 4 + 3]};
+    };
+    auto finish = [&](f32x16 (&acc)[MD][2], void *dst, float mul) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (!key_ok[kb]) continue;
+            const size_t base = ((size_t)(k0 + keyv[kb]) * a.Hkv + c) * D;
+#pragma unroll
+            for (int md = 0; md < MD; ++md)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 o = xch[((md * 2 + kb) * 4 + i) * 64 + lane];
+                    f32x4 x;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) x[j] = (acc[md][kb][i * 4 + j] + o[j]) * mul;
+                    const int d = md * 32 + i * 8 + h2 * 4;
+                    *(u32x2 *)((uint16_t *)dst + base + d) = __builtin_bit_cast(u32x2, __builtin_convertvector(x, bf16x4));
                 }
-                const int d = md * 32 + i * 8 + h2 * 4;
-                *(u32x2 *)((uint16_t *)a.dk + base + d) = __builtin_bit_cast(u32x2, __builtin_convertvector(x, bf16x4));
-                *(u32x2 *)((uint16_t *)a.dv + base + d) = __builtin_bit_cast(u32x2, __builtin_convertvector(y, bf16x4));
-            }
-    }
+        }
+    };
+    if (rh == 1) put(dka);
+    __syncthreads();
+    if (rh == 0) finish(dka, a.dk, a.scale);
+    __syncthreads();
+    if (rh == 0) put(dva);
+    __syncthreads();
+    if (rh == 1) finish(dva, a.dv, 1.f);
 }
 
 }  // namespace
