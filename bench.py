@@ -12,7 +12,8 @@ TFLOP/s: 4 * head_dim FLOPs per unmasked (query, key) pair per head.
 
 Also reported (same JSON line, key "also"): the full-attention Ulysses-shard
 shape, the sliding-window + sinks MQA shape (bound by HBM) and the paged
-decode shape (bound by HBM), each with its own step time and roofline.
+decode shape (bound by HBM), each with its own step time and roofline; and
+(key "backward") one call of the backward on the main workload.
 
 The roofline figure is for the dominant kernel: its average duration is the
 step time minus the pre-pass time, both measured here with HIP events on
@@ -174,6 +175,42 @@ def time_case(case, steps, warmup, torch):
     return ms_step, ms_plan, path
 
 
+def time_backward(case, steps, warmup, torch):
+    """One call of the backward (pre-passes, dO.O row sums, dQ kernel, dK/dV
+    kernel) on the workload, with out / lse from the forward and a seeded
+    dO, all resident in HBM; returns ms per call."""
+    import variable_length_attention_amd as va
+    q, k, v = _dev(case["q"], torch), _dev(case["k"], torch), _dev(case["v"], torch)
+    cu_q, cu_k = _dev(case["cu_q"], torch), _dev(case["cu_k"], torch)
+    sinks = _dev(case.get("sinks"), torch)
+    win = (case["window_left"], case["window_right"])
+    out = torch.empty_like(q)
+    lse = torch.empty((case["T_q"], case["H"]), dtype=torch.float32, device="cuda")
+    va.varlen_attn_out(out, q, k, v, cu_q, cu_k, case["max_q"], case["max_k"], scale=case["scale"],
+                       causal=case["causal"], window=win, sinks=sinks, lse=lse)
+    g = torch.Generator().manual_seed(case["spec"].seed + 7)
+    dout = torch.randn(tuple(q.shape), generator=g).to(torch.bfloat16).cuda()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    prob = va.make_problem(q, k.shape[1], k.shape[0], case["B"], case["max_q"], case["max_k"], case["scale"],
+                           case["causal"], win)
+    ws = torch.empty(va.bwd_workspace_size(prob), dtype=torch.uint8, device="cuda")
+
+    def step():
+        va.varlen_attn_bwd(dout, q, k, v, out, lse, cu_q, cu_k, case["max_q"], case["max_k"],
+                           scale=case["scale"], causal=case["causal"], window=win, dq=dq, dk=dk, dv=dv,
+                           workspace=ws)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 # ---------------------------------------------------------------- HBM traffic
 def kernel_source_sha(path_name):
     import hashlib
@@ -277,6 +314,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only-main", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--configs", default="2,3,4,5", help="workloads to time (first is the main one)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
@@ -348,6 +386,19 @@ def main():
         "roofline": main["roofline"],
         "tokens_per_s": main["tokens_per_s"],
     }
+    if not args.no_backward and spec0.dtype == "bf16" and not spec0.paged:
+        log(f"backward on {spec0.name}: timing {args.steps} calls after {args.warmup} warm-up")
+        ms_b = time_backward(main_case, args.steps, args.warmup, torch)
+        # 5 matrix products (S, dP, dV, dK, dQ) of 2 * head_dim FLOPs per
+        # unmasked pair and head: 10 * head_dim (the forward's 2.5x)
+        fl_b = 2.5 * flops(main_case)
+        tf_b = fl_b / (ms_b * 1e-3) / 1e12
+        line["backward"] = {"workload": spec0.name, "ms_per_step": ms_b, "tflops": tf_b, "flop": fl_b,
+                            "flop_convention": "10 * head_dim per unmasked (query, key) pair and head",
+                            "roofline": {"bound": "mfma", "achieved": tf_b, "peak": PEAK_BF16_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": tf_b / PEAK_BF16_TFLOPS,
+                                         "scope": "whole backward call", "traffic": None}}
+        log(f"backward: {ms_b:.4f} ms/call, {tf_b:.1f} TFLOP/s")
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a sample of rows")
         line["cpu_baseline"] = cpu_baseline(main_case)
