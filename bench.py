@@ -12,8 +12,10 @@ TFLOP/s: 4 * head_dim FLOPs per unmasked (query, key) pair per head.
 
 Also reported (same JSON line, key "also"): the full-attention Ulysses-shard
 shape, the sliding-window + sinks MQA shape (bound by HBM) and the paged
-decode shape (bound by HBM), each with its own step time and roofline; and
-(key "backward") one call of the backward on the main workload.
+decode shape (bound by HBM), each with its own step time and roofline;
+(key "backward") one call of the backward on the main workload; and (key
+"merge") the log-sum-exp merge of 8 float32 partials of the full-attention
+shard (a ring of 8), bound by HBM.
 
 The roofline figure is for the dominant kernel: its average duration is the
 step time minus the pre-pass time, both measured here with HIP events on
@@ -211,6 +213,37 @@ def time_backward(case, steps, warmup, torch):
     return e0.elapsed_time(e1) / steps
 
 
+MERGE_SHAPE = dict(n=8, rows=32768, H=24, D=128)  # ring of 8 over the full-attention shard
+
+
+def time_merge(steps, warmup, torch):
+    """The log-sum-exp merge of 8 float32 partials (a ring of 8 ranks over
+    the 32768-token, 24-head, d128 full-attention shard) into bf16 out +
+    float32 lse; returns (ms per call, algorithmic bytes)."""
+    import variable_length_attention_amd as va
+    import workloads as W
+    m = W.merge_inputs(MERGE_SHAPE["n"], MERGE_SHAPE["rows"], MERGE_SHAPE["H"], MERGE_SHAPE["D"], "f32", seed=2024)
+    o_parts, lse_parts = _dev(m["o_parts"], torch), _dev(m["lse_parts"], torch)
+    del m
+    n, rows, H, D = (MERGE_SHAPE[k] for k in ("n", "rows", "H", "D"))
+    out = torch.empty((rows, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((rows, H), dtype=torch.float32, device="cuda")
+
+    def step():
+        va.varlen_attn_merge(o_parts, lse_parts, out=out, lse=lse)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    nbytes = float(n * rows * H * (D * 4 + 4) + rows * H * (D * 2 + 4))
+    return e0.elapsed_time(e1) / steps, nbytes
+
+
 # ---------------------------------------------------------------- HBM traffic
 def kernel_source_sha(path_name):
     import hashlib
@@ -315,6 +348,7 @@ def main():
     ap.add_argument("--only-main", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-merge", action="store_true", help="skip the log-sum-exp merge timing")
     ap.add_argument("--configs", default="2,3,4,5", help="workloads to time (first is the main one)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
@@ -399,6 +433,15 @@ def main():
                                          "unit": "TFLOP/s", "frac": tf_b / PEAK_BF16_TFLOPS,
                                          "scope": "whole backward call", "traffic": None}}
         log(f"backward: {ms_b:.4f} ms/call, {tf_b:.1f} TFLOP/s")
+    if not args.no_merge:
+        log("merge of 8 float32 partials (32768 x 24 x 128): timing")
+        ms_m, by_m = time_merge(args.steps, args.warmup, torch)
+        gbs = by_m / (ms_m * 1e-3) / 1e9
+        line["merge"] = {"workload": "ring of 8 float32 partials, 32768 rows x 24 heads x 128 -> bf16",
+                         "ms_per_step": ms_m, "gbs": gbs, "bytes": by_m,
+                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": gbs / PEAK_HBM_GBS, "traffic": None}}
+        log(f"merge: {ms_m:.4f} ms/call, {gbs:.0f} GB/s")
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a sample of rows")
         line["cpu_baseline"] = cpu_baseline(main_case)

@@ -186,6 +186,34 @@ va_status varlen_attn_bwd(const va_problem *p, const void *dout, const void *q, 
                           void *dk, void *dv, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/* Merge of partial attention results computed over disjoint key sets of
+ * the same queries: the local step of ring / context-parallel attention,
+ * where each rank attends its queries to its share of the keys (the joint
+ * K/V that the vllm-omni ulysses.py wrapper hands to its ring path) and the
+ * partials are combined through their log-sum-exp.  For each (row, head),
+ * with parts p = 0 .. n_parts-1 and sigma = sinks[head] (absent: -inf):
+ *   m = max(max_p lse_p, sigma),  s = sum_p exp(lse_p - m) + exp(sigma - m),
+ *   lse = m + log(s),             out = sum_p exp(lse_p - lse) o_p.
+ * The result is the attention over the union of the key sets; a sink is
+ * counted once here, so the partials must be computed without sinks.  A
+ * part with lse_p = -inf contributes nothing; if every part is empty and
+ * there is no sink, out = 0 and lse = -inf (with a sink: out = 0,
+ * lse = sigma).
+ *   o_parts    device [n_parts, rows, num_heads, head_dim], parts_dtype
+ *   lse_parts  device float32 [n_parts, rows, num_heads], natural log
+ *   sinks      device float32 [num_heads] or NULL
+ *   out        device [rows, num_heads, head_dim], out_dtype (bf16: round to
+ *              nearest even), fully overwritten
+ *   lse        device float32 [rows, num_heads] or NULL
+ * n_parts in [1, 4096]; head_dim a multiple of 8 in [8, 1024]; o_parts and
+ * out 16-byte aligned, the float arrays 4-byte aligned; out and lse must not
+ * overlap an input or each other.  Enqueued on `stream`; nothing is
+ * allocated; a failing check returns before any launch. */
+va_status varlen_attn_merge(int32_t n_parts, int32_t rows, int32_t num_heads, int32_t head_dim,
+                            va_dtype parts_dtype, va_dtype out_dtype, const void *o_parts,
+                            const float *lse_parts, const float *sinks, void *out, float *lse,
+                            void *stream);
+
 /* Which kernel family a call with these arguments would use:
  * 0 = prefill tiles, 1 = split-KV decode with combine, 2 = float32 path;
  * -1 if invalid. */

@@ -15,6 +15,9 @@ which holds no attention arithmetic.
   (sequence, head, 64-row) units.
 * ``brute.dense_forward`` -- an independent dense numpy checker for small
   inputs (full score matrix, boolean mask, ``scipy.special.logsumexp``).
+* ``merge`` -- the log-sum-exp merge of partial results over disjoint key
+  sets (the combine step of ring / context-parallel attention that the
+  vllm-omni Ulysses wrapper's ring path needs), written out in float64.
 """
 from __future__ import annotations
 
@@ -170,3 +173,30 @@ def backward(case: dict, dout, out, lse, nthreads: int | None = None):
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
     return dq, dk, dv
+
+
+def merge(o_parts, lse_parts, sinks=None):
+    """Softmax over the union of disjoint key sets from per-set partials.
+
+    o_parts [n, rows, H, D] and lse_parts [n, rows, H] (natural log; -inf for
+    a part with no key) are the attention outputs and log-sum-exps of the
+    same queries over n disjoint key sets; sinks [H] (or None) is the sink
+    logit of each head, counted once.  For each (row, head):
+    lse = log(sum_p exp(lse_p) + exp(sigma)), out = sum_p exp(lse_p - lse) o_p.
+    Rows with nothing (every part empty, no sink) get out = 0, lse = -inf.
+    Returns (out [rows, H, D], lse [rows, H]) in float64."""
+    o = np.asarray(o_parts, dtype=np.float64)
+    lp = np.asarray(lse_parts, dtype=np.float64)
+    n, rows, H = lp.shape
+    terms = lp
+    if sinks is not None:
+        sig = np.broadcast_to(np.asarray(sinks, dtype=np.float64)[None, None, :], (1, rows, H))
+        terms = np.concatenate([lp, sig], axis=0)
+    m = terms.max(axis=0)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    total = np.exp(terms - m_safe[None]).sum(axis=0)
+    lse = np.where(finite, m_safe + np.log(np.where(finite, total, 1.0)), -np.inf)
+    w = np.where(finite[None], np.exp(lp - np.where(finite, lse, 0.0)[None]), 0.0)
+    out = (w[..., None] * o).sum(axis=0)
+    return out, lse

@@ -164,3 +164,28 @@ def test_backward_rejects_before_launching():
     assert _bwd(p, dk=ctypes.c_void_p(A[9].value + 8)) == 6            # not 16-byte aligned
     assert _bwd(p, ws_bytes=64) == 7
     assert _bwd(p, ws=None) == 7
+
+
+def _merge(n=2, rows=10, H=4, D=128, pdt=1, odt=1, o=1 << 20, l=2 << 20, s=None, out=3 << 20, lse=4 << 20):
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return _lib.load().varlen_attn_merge(n, rows, H, D, pdt, odt, vp(o), vp(l), vp(s), vp(out), vp(lse), None)
+
+
+def test_merge_rejects_before_launching():
+    # fake, never dereferenced addresses: every call fails its host checks
+    assert _merge(n=0) == 2
+    assert _merge(n=5000) == 2
+    assert _merge(rows=0) == 2
+    assert _merge(H=0) == 2
+    assert _merge(D=12) == 4
+    assert _merge(D=2048) == 4
+    assert _merge(pdt=2) == 3
+    assert _merge(odt=7) == 3
+    assert _merge(o=None) == 1
+    assert _merge(l=None) == 1
+    assert _merge(out=None) == 1
+    assert _merge(out=(3 << 20) + 8) == 6                                # out not 16-byte aligned
+    assert _merge(l=(2 << 20) + 2) == 6                                   # lse_parts not 4-byte aligned
+    assert _merge(out=(1 << 20) + 256) == 5                               # out inside o_parts
+    assert _merge(lse=(2 << 20) + 4) == 5                                 # lse inside lse_parts
+    assert _merge(lse=(3 << 20) + 64) == 5                                # lse inside out

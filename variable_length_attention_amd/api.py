@@ -13,6 +13,9 @@ request "[varlen_attn for inference] add out variant"):
                      README, PageAttention constraints)
   varlen_attn_fwd    the library-allocating C entry point, results copied
                      into torch tensors (for ABI tests)
+  varlen_attn_bwd    backward (dq, dk, dv) for bf16 contiguous K/V
+  varlen_attn_merge  merge of partial results over disjoint key sets
+                     through their log-sum-exp (ring / context parallel)
 """
 from __future__ import annotations
 
@@ -25,7 +28,7 @@ import torch
 from . import _lib
 
 __all__ = ["varlen_attn", "varlen_attn_out", "varlen_attn_paged", "varlen_attn_fwd", "varlen_attn_bwd",
-           "bwd_workspace_size",
+           "bwd_workspace_size", "varlen_attn_merge",
            "workspace_size", "plan", "kernel_path", "output_shapes", "make_problem"]
 
 _DTYPES = {torch.float32: _lib.VA_F32, torch.bfloat16: _lib.VA_BF16}
@@ -257,3 +260,30 @@ def varlen_attn_bwd(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seq
         _stream(dev))
     _lib.check(st)
     return dq, dk, dv
+
+
+def varlen_attn_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, sinks: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      out_dtype: Optional[torch.dtype] = None, return_lse: bool = True):
+    """Merges n partial results over disjoint key sets: o_parts [n, rows, H, D]
+    (float32 or bfloat16), lse_parts float32 [n, rows, H]; sinks (float32 [H])
+    are counted once here.  Returns out [rows, H, D] (and lse [rows, H])."""
+    _need(o_parts.dim() == 4, "o_parts must be [n_parts, rows, num_heads, head_dim]")
+    n, rows, H, D = o_parts.shape
+    _need(o_parts.dtype in _DTYPES, "o_parts must be float32 or bfloat16")
+    _need(lse_parts.dtype == torch.float32 and tuple(lse_parts.shape) == (n, rows, H),
+          "lse_parts must be float32 [n_parts, rows, num_heads]")
+    _need(sinks is None or (sinks.dtype == torch.float32 and tuple(sinks.shape) == (H,)),
+          "sinks must be float32 [num_heads]")
+    dev = _check_tensors(o_parts, lse_parts, sinks, out, lse)
+    if out is None:
+        out = torch.empty((rows, H, D), dtype=out_dtype or o_parts.dtype, device=dev)
+    _need(tuple(out.shape) == (rows, H, D) and out.dtype in _DTYPES, "out must be [rows, num_heads, head_dim]")
+    if lse is None and return_lse:
+        lse = torch.empty((rows, H), dtype=torch.float32, device=dev)
+    _need(lse is None or (lse.dtype == torch.float32 and tuple(lse.shape) == (rows, H)),
+          "lse must be float32 [rows, num_heads]")
+    _lib.check(_lib.load().varlen_attn_merge(n, rows, H, D, _DTYPES[o_parts.dtype], _DTYPES[out.dtype],
+                                             _ptr(o_parts), _ptr(lse_parts), _ptr(sinks), _ptr(out), _ptr(lse),
+                                             _stream(dev)))
+    return (out, lse) if return_lse else out

@@ -466,6 +466,42 @@ va_status varlen_attn_bwd(const va_problem *p, const void *dout, const void *q, 
 }
 
 
+va_status varlen_attn_merge(int32_t n_parts, int32_t rows, int32_t num_heads, int32_t head_dim,
+                            va_dtype parts_dtype, va_dtype out_dtype, const void *o_parts,
+                            const float *lse_parts, const float *sinks, void *out, float *lse,
+                            void *stream)
+{
+    if (n_parts < 1 || n_parts > 4096) return fail(VA_ERR_SHAPE, "n_parts %d outside [1, 4096]", n_parts);
+    if (rows < 1 || num_heads < 1)
+        return fail(VA_ERR_SHAPE, "rows %d and num_heads %d must be >= 1", rows, num_heads);
+    if (head_dim < 8 || head_dim > 1024 || head_dim % 8 != 0)
+        return fail(VA_ERR_UNSUPPORTED, "head_dim %d is not a multiple of 8 in [8, 1024]", head_dim);
+    if ((parts_dtype != VA_F32 && parts_dtype != VA_BF16) || (out_dtype != VA_F32 && out_dtype != VA_BF16))
+        return fail(VA_ERR_DTYPE, "dtypes must be VA_F32 (0) or VA_BF16 (1)");
+    if (!o_parts || !lse_parts || !out) return fail(VA_ERR_NULL, "o_parts, lse_parts and out must be non-NULL");
+    if (!aligned(o_parts, 16) || !aligned(out, 16))
+        return fail(VA_ERR_ALIGN, "o_parts and out must be 16-byte aligned");
+    if (!aligned(lse_parts, 4) || (sinks && !aligned(sinks, 4)) || (lse && !aligned(lse, 4)))
+        return fail(VA_ERR_ALIGN, "lse_parts, sinks and lse must be 4-byte aligned");
+    const size_t vecs = (size_t)rows * num_heads;
+    const size_t pe = parts_dtype == VA_BF16 ? 2 : 4, oe = out_dtype == VA_BF16 ? 2 : 4;
+    const Range o_r{out, vecs * head_dim * oe}, l_r{lse, lse ? vecs * 4 : 0};
+    const Range ins[] = {{o_parts, (size_t)n_parts * vecs * head_dim * pe},
+                         {lse_parts, (size_t)n_parts * vecs * 4},
+                         {sinks, sinks ? (size_t)num_heads * 4 : 0}};
+    for (const Range &r : ins) {
+        if (overlaps(o_r, r)) return fail(VA_ERR_ALIAS, "out overlaps an input");
+        if (lse && overlaps(l_r, r)) return fail(VA_ERR_ALIAS, "lse overlaps an input");
+    }
+    if (lse && overlaps(o_r, l_r)) return fail(VA_ERR_ALIAS, "out overlaps lse");
+    va::MergeArgs a;
+    a.o_parts = o_parts; a.lse_parts = lse_parts; a.sinks = sinks; a.out = out; a.lse = lse;
+    a.n = n_parts; a.rows = rows; a.H = num_heads; a.D = head_dim;
+    const hipError_t e = va::launch_merge(a, parts_dtype == VA_BF16, out_dtype == VA_BF16, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(VA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return VA_OK;
+}
+
 int varlen_attn_abi_version(void) { return VARLEN_ATTN_ABI_VERSION; }
 
 const char *varlen_attn_last_error(void) { return g_last_error.c_str(); }

@@ -89,6 +89,16 @@ struct BwdArgs {
     float scale, scale_log2;
 };
 
+// Merge of partial results over disjoint key sets.
+struct MergeArgs {
+    const void *o_parts;         // [n, rows, H, D]
+    const float *lse_parts;      // [n, rows, H]
+    const float *sinks;          // [H] or null
+    void *out;                   // [rows, H, D]
+    float *lse;                  // [rows, H] or null
+    int32_t n, rows, H, D;
+};
+
 // Opt-in device-side argument check (one bit per violated precondition).
 enum CheckFlag : uint32_t {
     kChkCuQStart = 1u << 0,   // cu_seqlens_q[0] != 0
@@ -118,6 +128,7 @@ hipError_t launch_backward_bf16(const BwdArgs &a, int head_dim, int total_q, con
                                 const int4 *q_seqinfo, const int32_t *q_count, int q_grid,
                                 const int4 *k_items, const int4 *k_seqinfo, const int32_t *k_count,
                                 int k_grid, hipStream_t s);
+hipError_t launch_merge(const MergeArgs &a, bool part_bf16, bool out_bf16, hipStream_t s);
 hipError_t launch_plan(const PlanArgs &pa, hipStream_t s);
 hipError_t launch_prefill_bf16(const AttnArgs &a, int head_dim, int mode, const int4 *items,
                                const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);

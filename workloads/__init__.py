@@ -34,7 +34,7 @@ import numpy as np
 
 __all__ = [
     "Spec", "CONFIGS", "config", "scaled", "make_case", "f32_to_bf16_bits",
-    "bf16_bits_to_f32", "case_digest", "POISON_BF16", "POISON_F32",
+    "bf16_bits_to_f32", "case_digest", "POISON_BF16", "POISON_F32", "merge_inputs",
 ]
 
 # Finite poison written into cache slots that no sequence owns.  Read by
@@ -254,3 +254,26 @@ def case_digest(case: dict) -> str:
         h.update(key.encode())
         h.update(np.ascontiguousarray(a).tobytes())
     return h.hexdigest()
+
+
+def merge_inputs(n: int, rows: int, H: int, D: int, dtype: str = "f32", seed: int = 2000,
+                 empty_frac: float = 0.0, empty_rows_every: int = 0) -> dict:
+    """Partial results of the same queries over n disjoint key sets, for the
+    log-sum-exp merge: ``o_parts`` [n, rows, H, D] (float32, or bf16 bit
+    patterns when dtype is "bf16") from ``standard_normal``, ``lse_parts``
+    float32 [n, rows, H] = 4 * ``standard_normal``; then a fraction
+    ``empty_frac`` of the (part, row, head) entries gets lse = -inf (a part
+    with no key for that row), and with ``empty_rows_every`` = k every k-th
+    (row, head) vector gets -inf in every part.  Draw order: o, lse, empty
+    mask."""
+    rng = np.random.default_rng(seed)
+    o = rng.standard_normal((n, rows, H, D), dtype=np.float32)
+    lse = (rng.standard_normal((n, rows, H), dtype=np.float32) * np.float32(4.0)).astype(np.float32)
+    if empty_frac > 0:
+        lse[rng.random((n, rows, H)) < empty_frac] = -np.inf
+    if empty_rows_every > 0:
+        flat = lse.reshape(n, rows * H)
+        flat[:, ::empty_rows_every] = -np.inf
+    if dtype == "bf16":
+        o = f32_to_bf16_bits(o)
+    return {"o_parts": o, "lse_parts": lse, "n": n, "rows": rows, "H": H, "D": D, "dtype": dtype}
