@@ -44,6 +44,9 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p)
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// Keeps the computation of x at this point of the instruction stream (an
+// empty volatile statement that reads and writes it).
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 
 // Values of lanes l and l^32 combined (v_permlane32_swap exchanges the two
 // 32-lane halves, no LDS round trip).
@@ -289,6 +292,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
         }
     };
+    // one probability in place (element idx of the tile's 32 per lane),
+    // pinned where it is computed
+    auto prob_elem = [&](f32x16 (&S)[2], int idx, float neg_m, float &rs) {
+        float x = fast_exp2(fmaf(S[idx >> 4][idx & 15], a.scale_log2, neg_m));
+        pin(x);
+        S[idx >> 4][idx & 15] = x;
+        rs += x;
+    };
+    // bf16 operand of PV step t4 from probabilities computed in place
+    auto cvt_step = [&](f32x16 (&S)[2], int t4) -> bf16x8 {
+        f32x8 pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = S[t4 >> 1][(t4 & 1) * 8 + e];
+        return __builtin_convertvector(pv, bf16x8);
+    };
     // probabilities of PV step t4 (keys 16 t4 .. +16) in bf16, laid out as
     // that step's P^T operand
     auto probs = [&](f32x16 (&S)[2], int t4, float neg_m, float &rs) -> bf16x8 {
@@ -350,21 +368,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         constexpr int KEVERY = KS / LPW;
         const u32x4 rs_k = MODE == kLoadBuffer ? tile_rsrc(t + 2, false) : u32x4{0u, 0u, 0u, 0u};
         const u32x4 rs_v = MODE == kLoadBuffer ? tile_rsrc(t + 1, true) : u32x4{0u, 0u, 0u, 0u};
+        // the probabilities of PV steps 0 and 1 (16 per lane) are computed
+        // between the QK^T products of the next tile (independent work), two
+        // per K step; with no current tile they are computed and dropped
+        float rs = 0.f;
+        constexpr int PER_KS = 16 / KS;
+        static_assert(PER_KS * KS == 16, "16 probabilities over the K steps");
         if (vn) {
             qk(Sn, k_next, [&](int ks) {
                 if (ks % KEVERY == KEVERY - 1) issue_u(t + 2, false, k_dst, ks / KEVERY, rs_k);
+#pragma unroll
+                for (int e = 0; e < PER_KS; ++e) prob_elem(Sc, ks * PER_KS + e, neg_m, rs);
+                __builtin_amdgcn_sched_barrier(0);
             });
         } else {
             issue(t + 2, false, k_dst);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) prob_elem(Sc, e, neg_m, rs);
         }
         if (vc) {
             constexpr int VEVERY = 4 / LPW;
             auto vhook = [&](int t4) {
                 if (t4 % VEVERY == VEVERY - 1) issue_u(t + 1, true, v_dst, t4 / VEVERY, rs_v);
             };
-            float rs = 0.f;
-            const bf16x8 p0 = probs(Sc, 0, neg_m, rs);
-            const bf16x8 p1 = probs(Sc, 1, neg_m, rs);
+            const bf16x8 p0 = cvt_step(Sc, 0);
+            const bf16x8 p1 = cvt_step(Sc, 1);
             pv(p0, 0, v_cur);
             vhook(0);
             const bf16x8 p2 = probs(Sc, 2, neg_m, rs);
