@@ -404,6 +404,22 @@ def main():
             main_case = case
         else:
             del case
+    if not args.only_main and W.config(cfgs[0]).dtype == "bf16":
+        # the main workload with float16 inputs (same kernels, f16 matrix instructions)
+        import dataclasses
+        spec16 = dataclasses.replace(W.config(cfgs[0]), dtype="f16", name=W.config(cfgs[0]).name + "_f16")
+        log(f"{spec16.name}: generating input")
+        case16 = W.make_case(spec16)
+        ms16, mp16, _ = time_case(case16, args.steps, args.warmup, torch)
+        fl16 = flops(case16)
+        ach16 = fl16 / (max(ms16 - mp16, 1e-6) * 1e-3) / 1e12
+        results["f16"] = {"workload": spec16.name, "ms_per_step": ms16, "ms_prepass": mp16,
+                          "tflops": fl16 / (ms16 * 1e-3) / 1e12, "flop": fl16, "kernel_path": "prefill16",
+                          "roofline": {"bound": "mfma", "achieved": ach16, "peak": PEAK_BF16_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": ach16 / PEAK_BF16_TFLOPS, "traffic": None}}
+        log(f"{spec16.name}: {ms16:.4f} ms/step, {results['f16']['tflops']:.1f} TFLOP/s")
+        del case16
+        cfgs = cfgs + ["f16"]
     n0 = cfgs[0]
     main = results[n0]
     spec0 = W.config(n0)

@@ -30,8 +30,10 @@
  *   seqused_k     int32 [batch] key count per sequence (paged mode)
  *   sinks         float32 [H] or NULL
  *   lse           float32 [total_q, H] or NULL when not wanted
- *   q, k, v, out share one dtype (VA_F32 or VA_BF16); out is rounded to
- *   nearest-even.
+ *   q, k, v, out share one dtype (VA_F32, VA_BF16 or VA_F16 -- the
+ *   SparseAttnSharedkv README lists BF16 and FP16 inputs); out is rounded to
+ *   nearest-even.  bf16 and fp16 run the same kernels (matrix cores, fp32
+ *   accumulation, probabilities rounded to the input type for P V).
  *
  * Ownership and streams: every pointer handed in is caller-owned device
  * memory (except `va_problem`, which is host memory and only read during the
@@ -84,7 +86,7 @@ typedef enum {
     VA_ERR_DEVICE_CHECK = 9  /* opt-in device-side argument check failed (below)  */
 } va_status;
 
-typedef enum { VA_F32 = 0, VA_BF16 = 1 } va_dtype;
+typedef enum { VA_F32 = 0, VA_BF16 = 1, VA_F16 = 2 } va_dtype;
 
 /* Problem description, host memory.  Field meaning follows the argument list
  * of the out-variant op in the pull request "[varlen_attn for inference] add

@@ -74,6 +74,8 @@ def _load():
             lib.oracle_varlen_fwd_rows.restype = ctypes.c_int
             lib.oracle_varlen_bwd.argtypes = [ctypes.POINTER(_Args)] + [ctypes.c_void_p] * 6 + [ctypes.c_int]
             lib.oracle_varlen_bwd.restype = ctypes.c_int
+            lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+            lib.oracle_half_to_double.restype = ctypes.c_double
             _lib = lib
     return _lib
 
@@ -93,12 +95,15 @@ def _make_args(case: dict, keep: list) -> _Args:
     def c(a, dt):
         if a is None:
             return None
+        a = np.asarray(a)
+        if a.dtype == np.float16:  # binary16 values go over as their bits
+            a = a.view(np.uint16)
         a = np.ascontiguousarray(a, dtype=dt)
         keep.append(a)
         return a
-    elt = np.uint16 if case["dtype"] == "bf16" else np.float32
+    elt = np.uint16 if case["dtype"] in ("bf16", "f16") else np.float32
     a = _Args()
-    a.dtype = 1 if case["dtype"] == "bf16" else 0
+    a.dtype = {"f32": 0, "bf16": 1, "f16": 2}[case["dtype"]]
     a.B, a.H, a.Hkv, a.D = case["B"], case["H"], case["Hkv"], case["D"]
     a.causal = 1 if case["causal"] else 0
     a.wl, a.wr = case["window_left"], case["window_right"]
@@ -200,3 +205,10 @@ def merge(o_parts, lse_parts, sinks=None):
     w = np.where(finite[None], np.exp(lp - np.where(finite, lse, 0.0)[None]), 0.0)
     out = (w[..., None] * o).sum(axis=0)
     return out, lse
+
+
+def half_to_double(bits):
+    """The oracle's binary16 widening (uint16 bit patterns -> float64)."""
+    lib = _load()
+    b = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
+    return np.array([lib.oracle_half_to_double(int(x)) for x in b], dtype=np.float64)

@@ -50,7 +50,7 @@
 #include <string.h>
 
 typedef struct {
-    int32_t dtype;              /* 0: float32, 1: bfloat16 bits            */
+    int32_t dtype;              /* 0: float32, 1: bfloat16 bits, 2: binary16 bits */
     int32_t B, H, Hkv, D;
     int32_t causal, wl, wr;     /* window: -1 = unbounded                  */
     double scale;
@@ -63,10 +63,24 @@ typedef struct {
     const float *sinks;         /* [H] or NULL                             */
 } oracle_args;
 
+/* IEEE 754 binary16 -> double, exact: sign, 5-bit exponent (bias 15),
+ * 10-bit fraction; exponent 0 is subnormal (fraction * 2^-24), 31 is inf/NaN. */
+double oracle_half_to_double(uint16_t h)
+{
+    const int e = (h >> 10) & 0x1f, m = h & 0x3ff;
+    double v;
+    if (e == 0) v = ldexp((double)m, -24);
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexp((double)(m | 0x400), e - 25);
+    return (h & 0x8000) ? -v : v;
+}
+
 static double widen(int dtype, const void *base, size_t idx)
 {
     if (dtype == 0)
         return (double)((const float *)base)[idx];
+    if (dtype == 2)
+        return oracle_half_to_double(((const uint16_t *)base)[idx]);
     uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
@@ -213,7 +227,7 @@ static int check_args(const oracle_args *a)
     if (a->H % a->Hkv != 0) return -1;
     if (!a->q || !a->k || !a->v || !a->cu_q) return -1;
     if (a->block_table ? (!a->seqused_k || a->block_size <= 0) : !a->cu_k) return -1;
-    if (a->dtype != 0 && a->dtype != 1) return -1;
+    if (a->dtype < 0 || a->dtype > 2) return -1;
     return 0;
 }
 

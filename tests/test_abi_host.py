@@ -63,6 +63,7 @@ def _fwd_out(p, q=A[0], k=A[1], v=A[2], cuq=A[3], cuk=A[4], sinks=None, out=A[5]
 @pytest.mark.parametrize("kw,code", [
     (dict(num_heads=6, num_kv_heads=4), 2),        # H % H_kv != 0
     (dict(dtype=7), 3),
+    (dict(dtype=3), 3),
     (dict(head_dim=96), 4),
     (dict(batch=0), 2),
     (dict(total_q=0), 2),                          # empty tensors are not accepted
@@ -157,6 +158,7 @@ def test_backward_rejects_before_launching():
     assert lib.varlen_attn_bwd_workspace_size(ctypes.byref(_prob(dtype=0))) == 0
     assert _bwd(_prob(dtype=0)) == 4                                   # float32: unsupported
     assert _bwd(_prob(head_dim=96)) == 4
+    assert _bwd(_prob(dtype=2)) == 4                                   # float16: the backward is bf16 only
     assert _bwd(p, dout=None) == 1
     assert _bwd(p, lse=None) == 1
     assert _bwd(p, dq=A[1]) == 5                                       # dq aliases q
@@ -181,6 +183,7 @@ def test_merge_rejects_before_launching():
     assert _merge(D=2048) == 4
     assert _merge(pdt=2) == 3
     assert _merge(odt=7) == 3
+    assert _merge(pdt=2) == 3                                             # float16 partials are not taken
     assert _merge(o=None) == 1
     assert _merge(l=None) == 1
     assert _merge(out=None) == 1

@@ -286,6 +286,30 @@ def test_oracle_matches_dense_bruteforce_scaled_configs(n):
     np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-12)
 
 
+def test_half_widening_matches_numpy_on_every_bit_pattern():
+    # binary16 inputs: the oracle's widening against numpy's float16 -> float64
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = oracle.half_to_double(bits)
+    nan = np.isnan(ref)
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    assert np.all(np.isnan(got[nan]))
+
+
+@pytest.mark.parametrize("n", [2, 4, 5])
+def test_oracle_matches_dense_bruteforce_f16(n):
+    # the same workloads in float16 (numpy's round-to-nearest-even cast)
+    spec = W.scaled(W.config(n), B=4 if n != 4 else 2, max_len=200)
+    spec = W.Spec(**{**spec.__dict__, "dtype": "f16", "name": spec.name + "_f16",
+                     **({"H": 8} if n == 4 else {})})
+    case = W.make_case(spec)
+    assert case["q"].dtype == np.float16
+    out, lse = oracle.forward(case)
+    out2, lse2 = brute.dense_forward(case)
+    np.testing.assert_allclose(out, out2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-12)
+
+
 @pytest.mark.parametrize("idx", range(14))
 def test_oracle_matches_dense_bruteforce_sweep(idx):
     case = _sweep_cases()[idx]

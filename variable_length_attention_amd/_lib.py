@@ -18,7 +18,7 @@ STATUS_NAMES = {
     5: "VA_ERR_ALIAS", 6: "VA_ERR_ALIGN", 7: "VA_ERR_WORKSPACE", 8: "VA_ERR_HIP",
     9: "VA_ERR_DEVICE_CHECK",
 }
-VA_F32, VA_BF16 = 0, 1
+VA_F32, VA_BF16, VA_F16 = 0, 1, 2
 
 # every symbol include/varlen_attn.h declares
 EXPORTED = [

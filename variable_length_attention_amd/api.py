@@ -31,7 +31,7 @@ __all__ = ["varlen_attn", "varlen_attn_out", "varlen_attn_paged", "varlen_attn_f
            "bwd_workspace_size", "varlen_attn_merge",
            "workspace_size", "plan", "kernel_path", "output_shapes", "make_problem"]
 
-_DTYPES = {torch.float32: _lib.VA_F32, torch.bfloat16: _lib.VA_BF16}
+_DTYPES = {torch.float32: _lib.VA_F32, torch.bfloat16: _lib.VA_BF16, torch.float16: _lib.VA_F16}
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -56,7 +56,7 @@ def output_shapes(q: torch.Tensor):
 def make_problem(q, num_kv_heads, total_k, batch, max_seqlen_q, max_seqlen_k, scale, causal,
                  window, num_blocks=0, block_size=0, block_table_stride=0) -> _lib.VaProblem:
     _need(q.dim() == 3, "q must be [total_q, num_heads, head_dim]")
-    _need(q.dtype in _DTYPES, f"dtype {q.dtype} not supported (float32 or bfloat16)")
+    _need(q.dtype in _DTYPES, f"dtype {q.dtype} not supported (float32, bfloat16 or float16)")
     p = _lib.VaProblem()
     p.struct_size = ctypes.sizeof(_lib.VaProblem)
     p.dtype = _DTYPES[q.dtype]
@@ -270,7 +270,7 @@ def varlen_attn_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, sinks: 
     are counted once here.  Returns out [rows, H, D] (and lse [rows, H])."""
     _need(o_parts.dim() == 4, "o_parts must be [n_parts, rows, num_heads, head_dim]")
     n, rows, H, D = o_parts.shape
-    _need(o_parts.dtype in _DTYPES, "o_parts must be float32 or bfloat16")
+    _need(o_parts.dtype in (torch.float32, torch.bfloat16), "o_parts must be float32 or bfloat16")
     _need(lse_parts.dtype == torch.float32 and tuple(lse_parts.shape) == (n, rows, H),
           "lse_parts must be float32 [n_parts, rows, num_heads]")
     _need(sinks is None or (sinks.dtype == torch.float32 and tuple(sinks.shape) == (H,)),

@@ -68,8 +68,8 @@ va_status check_problem(const va_problem *p, int paged)
     if (p->struct_size < sizeof(va_problem))
         return fail(VA_ERR_SHAPE, "va_problem.struct_size %u is smaller than %zu", p->struct_size,
                     sizeof(va_problem));
-    if (p->dtype != VA_F32 && p->dtype != VA_BF16)
-        return fail(VA_ERR_DTYPE, "dtype %d is not VA_F32 (0) or VA_BF16 (1)", p->dtype);
+    if (p->dtype != VA_F32 && p->dtype != VA_BF16 && p->dtype != VA_F16)
+        return fail(VA_ERR_DTYPE, "dtype %d is not VA_F32 (0), VA_BF16 (1) or VA_F16 (2)", p->dtype);
     if (p->batch < 1) return fail(VA_ERR_SHAPE, "batch %d < 1", p->batch);
     if (p->total_q < 1) return fail(VA_ERR_SHAPE, "total_q %d < 1 (empty tensors are not accepted)", p->total_q);
     if (!paged && p->total_k < 1)
@@ -192,7 +192,7 @@ va_status check_pointers(const Call &c, const Layout &L)
         (c.lse && !aligned(c.lse, 4)))
         return fail(VA_ERR_ALIGN, "int32 / float32 arrays must be 4-byte aligned");
 
-    const size_t es = p->dtype == VA_BF16 ? 2 : 4;
+    const size_t es = p->dtype == VA_F32 ? 4 : 2;
     const size_t D = (size_t)p->head_dim;
     const size_t kv_rows = c.paged ? (size_t)p->num_blocks * p->block_size : (size_t)p->total_k;
     const Range out{c.out, (size_t)p->total_q * p->num_heads * D * es};
@@ -308,7 +308,7 @@ va_status run(const Call &c, hipStream_t s)
     if (device_check_enabled() && (st = device_check(c, L, s))) return st;
     if (log_enabled())
         fprintf(stderr, "[varlen_attn] path=%s D=%d paged=%d B=%d H=%d Hkv=%d total_q=%d grid=%lld ws=%zu\n",
-                L.path == kPathPrefill ? "prefill_bf16" : L.path == kPathDecode ? "decode_bf16" : "f32",
+                L.path == kPathPrefill ? "prefill16" : L.path == kPathDecode ? "decode16" : "f32",
                 c.p->head_dim, c.paged, a.B, a.H, a.Hkv, c.p->total_q, L.grid, L.total);
     hipError_t e = va::launch_plan(pa, s);
     if (e == hipSuccess) {
@@ -316,7 +316,8 @@ va_status run(const Call &c, hipStream_t s)
         {
             const size_t span = (size_t)c.p->max_seqlen_k * c.p->num_kv_heads * c.p->head_dim * 2;
             const int mode = c.paged ? va::kLoadPaged : (span < ((size_t)1 << 31) ? va::kLoadBuffer : va::kLoadGlobal);
-            e = va::launch_prefill_bf16(a, c.p->head_dim, mode, pa.items, pa.seqinfo, pa.count, (int)L.grid, s);
+            e = va::launch_prefill16(a, c.p->dtype == VA_F16, c.p->head_dim, mode, pa.items, pa.seqinfo, pa.count,
+                                     (int)L.grid, s);
         }
         else if (L.path == kPathF32)
             e = va::launch_prefill_f32(a, c.p->head_dim, c.paged, pa.items, pa.seqinfo, pa.count, (int)L.grid, s);
@@ -324,8 +325,10 @@ va_status run(const Call &c, hipStream_t s)
             char *ws = (char *)c.ws;
             float *po = (float *)(ws + L.off_part_o);
             float2 *pml = (float2 *)(ws + L.off_part_ml);
-            e = va::launch_decode_bf16(a, c.p->head_dim, c.paged, pa.items, pa.seqinfo, pa.count, (int)L.grid, po, pml, s);
-            if (e == hipSuccess) e = va::launch_decode_combine(a, c.p->head_dim, pa.seq_off, po, pml, s);
+            const bool f16 = c.p->dtype == VA_F16;
+            e = va::launch_decode16(a, f16, c.p->head_dim, c.paged, pa.items, pa.seqinfo, pa.count, (int)L.grid, po,
+                                    pml, s);
+            if (e == hipSuccess) e = va::launch_decode_combine(a, f16, c.p->head_dim, pa.seq_off, po, pml, s);
         }
     }
     if (e != hipSuccess) return fail(VA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -555,7 +558,7 @@ va_status varlen_attn_fwd(const va_problem *p, const void *q, const void *k, con
     Layout L;
     if ((st = make_layout(p, 0, L))) return st;
     hipStream_t s = (hipStream_t)stream;
-    const size_t es = p->dtype == VA_BF16 ? 2 : 4;
+    const size_t es = p->dtype == VA_F32 ? 4 : 2;
     const size_t out_bytes = (size_t)p->total_q * p->num_heads * p->head_dim * es;
     const size_t lse_bytes = (size_t)p->total_q * p->num_heads * 4;
     void *o = nullptr, *l = nullptr, *w = nullptr;

@@ -37,19 +37,54 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p)
-{
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4 *)((__attribute__((address_space(3))) uint16_t *)(p)));
-}
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
 
-template <int D, bool PAGED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_decode_bf16(AttnArgs a, const int4 *__restrict__ items,
+// The 16-bit input type's 16x16x32 matrix instruction and transposing LDS
+// read (bf16 and fp16 share the data layout and the fp32 accumulation).
+template <typename T>
+struct Elt;
+template <>
+struct Elt<__bf16> {
+    typedef bf16x8 v8;
+    typedef bf16x4 v4;
+    static __device__ __forceinline__ v4 read_tr(const uint16_t *p)
+    {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4 *)((__attribute__((address_space(3))) uint16_t *)(p)));
+    }
+    static __device__ __forceinline__ f32x4 mfma(v8 a, v8 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Elt<_Float16> {
+    typedef f16x8 v8;
+    typedef f16x4 v4;
+    static __device__ __forceinline__ v4 read_tr(const uint16_t *p)
+    {
+        return __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                                          (lds_fp16x4 *)((__attribute__((address_space(3))) uint16_t *)(p))));
+    }
+    static __device__ __forceinline__ f32x4 mfma(v8 a, v8 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <typename T, int D, bool PAGED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_decode16(AttnArgs a, const int4 *__restrict__ items,
                                                       const int4 *__restrict__ seqinfo,
                                                       const int32_t *__restrict__ count,
                                                       float *__restrict__ part_o,
                                                       float2 *__restrict__ part_ml)
 {
+    using E = Elt<T>;
+    typedef typename E::v8 v8;
+    typedef typename E::v4 v4;
     constexpr int CH = kDecChunk;        // keys per wave step
     constexpr int NCH = D / 8;           // 16-byte chunks per row
     constexpr int KS = D / 32;           // QK^T k-steps
@@ -89,14 +124,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         flo = l1; fhi = h0;
     }
 
-    bf16x8 qf[KS];
+    v8 qf[KS];
     {
         const uint16_t *qp = (const uint16_t *)a.q + ((size_t)(q0 + (row_ok ? qi : 0)) * a.H + (row_ok ? head : 0)) * D + kq * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 x = *(const u32x4 *)(qp + ks * 32);
             if (!row_ok) x = u32x4{0, 0, 0, 0};
-            qf[ks] = __builtin_bit_cast(bf16x8, x);
+            qf[ks] = __builtin_bit_cast(v8, x);
         }
     }
     f32x4 o[MD];
@@ -150,7 +185,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint32_t voff0 = (lane / NCH) * (uint32_t)rowstride + (lane % NCH) * 16;
 
     for (int j0 = kv_lo + wave * CH; j0 < kv_hi; j0 += 4 * CH) {
-        bf16x8 kf[NKB][KS];
+        v8 kf[NKB][KS];
         u32x4 vr[VL];
         const int cc = lane % NCH;
         if constexpr (AM == 0) {
@@ -171,7 +206,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    kf[kb][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                    kf[kb][ks] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(
                         rk, koff0 + (uint32_t)(kb * 16 * rowstride) + ks * 64, 0, 0));
 #pragma unroll
             for (int u = 0; u < VL; ++u)
@@ -182,7 +217,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int kb = 0; kb < NKB; ++kb) {
                 const uint16_t *kp = kbase + row_off(j0 + kb * 16 + n) + kq * 8;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(kp + ks * 32));
+                for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = __builtin_bit_cast(v8, *(const u32x4 *)(kp + ks * 32));
             }
             // V rows of the chunk, 16-byte chunk `cc` of row r
 #pragma unroll
@@ -199,7 +234,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][ks], qf[ks], s[kb], 0, 0, 0);
+                s[kb] = E::mfma(kf[kb][ks], qf[ks], s[kb]);
         }
         // stage V: chunk index XOR 2 (row mod NCH/2) spreads the 16 rows of
         // one transposing read over all banks
@@ -260,7 +295,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 pv[e] = s[2 * t][e];
                 pv[4 + e] = s[2 * t + 1][e];
             }
-            const bf16x8 pf = __builtin_convertvector(pv, bf16x8);
+            const v8 pf = __builtin_convertvector(pv, v8);
             const int rA = 32 * t + kq * 4 + (l16 >> 2);
             const int rB = rA + 16;
 #pragma unroll
@@ -268,10 +303,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const int col = md * 16 + (l16 & 3) * 4;
                 const int chA = (col >> 3) ^ ((rA % (NCH / 2)) << 1);
                 const int chB = (col >> 3) ^ ((rB % (NCH / 2)) << 1);
-                const bf16x4 va = lds_read_tr(sv + rA * D + (chA << 3) + (col & 7));
-                const bf16x4 vb = lds_read_tr(sv + rB * D + (chB << 3) + (col & 7));
-                const bf16x8 vf = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[md], 0, 0, 0);
+                const v4 va = E::read_tr(sv + rA * D + (chA << 3) + (col & 7));
+                const v4 vb = E::read_tr(sv + rB * D + (chB << 3) + (col & 7));
+                const v8 vf = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+                o[md] = E::mfma(vf, pf, o[md]);
             }
         }
         __builtin_amdgcn_wave_barrier();
@@ -322,7 +357,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void k3_combine(AttnArgs a, const int32_t *__restrict__ seq_off,
                                                   const float *__restrict__ part_o,
                                                   const float2 *__restrict__ part_ml)
@@ -360,7 +395,7 @@ __global__ __launch_bounds__(256) void k3_combine(AttnArgs a, const int32_t *__r
 #pragma unroll
     for (int i = 0; i < DPT; i += 4) {
         const f32x4 x = {acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv};
-        const bf16x4 y = __builtin_convertvector(x, bf16x4);
+        const auto y = __builtin_convertvector(x, typename Elt<T>::v4);
         *(u32x2 *)(op + i) = __builtin_bit_cast(u32x2, y);
     }
     if ((threadIdx.x & 15) == 0 && a.lse)
@@ -369,27 +404,35 @@ __global__ __launch_bounds__(256) void k3_combine(AttnArgs a, const int32_t *__r
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const AttnArgs &a, int head_dim, bool paged, const int4 *items,
-                              const int4 *seqinfo, const int32_t *count, int grid, float *part_o,
-                              float2 *part_ml, hipStream_t s)
+hipError_t launch_decode16(const AttnArgs &a, bool f16, int head_dim, bool paged, const int4 *items,
+                           const int4 *seqinfo, const int32_t *count, int grid, float *part_o,
+                           float2 *part_ml, hipStream_t s)
 {
     const dim3 g(grid), blk(256);
-    if (head_dim == 128) {
-        if (paged) hipLaunchKernelGGL((k2_decode_bf16<128, true>), g, blk, 0, s, a, items, seqinfo, count, part_o, part_ml);
-        else hipLaunchKernelGGL((k2_decode_bf16<128, false>), g, blk, 0, s, a, items, seqinfo, count, part_o, part_ml);
+#define VA_LAUNCH(TT, DD, PP) \
+    hipLaunchKernelGGL((k2_decode16<TT, DD, PP>), g, blk, 0, s, a, items, seqinfo, count, part_o, part_ml)
+    if (f16) {
+        if (head_dim == 128) { if (paged) VA_LAUNCH(_Float16, 128, true); else VA_LAUNCH(_Float16, 128, false); }
+        else { if (paged) VA_LAUNCH(_Float16, 64, true); else VA_LAUNCH(_Float16, 64, false); }
     } else {
-        if (paged) hipLaunchKernelGGL((k2_decode_bf16<64, true>), g, blk, 0, s, a, items, seqinfo, count, part_o, part_ml);
-        else hipLaunchKernelGGL((k2_decode_bf16<64, false>), g, blk, 0, s, a, items, seqinfo, count, part_o, part_ml);
+        if (head_dim == 128) { if (paged) VA_LAUNCH(__bf16, 128, true); else VA_LAUNCH(__bf16, 128, false); }
+        else { if (paged) VA_LAUNCH(__bf16, 64, true); else VA_LAUNCH(__bf16, 64, false); }
     }
+#undef VA_LAUNCH
     return hipGetLastError();
 }
 
-hipError_t launch_decode_combine(const AttnArgs &a, int head_dim, const int32_t *seq_off,
+hipError_t launch_decode_combine(const AttnArgs &a, bool f16, int head_dim, const int32_t *seq_off,
                                  const float *part_o, const float2 *part_ml, hipStream_t s)
 {
     const dim3 g(a.B * a.Hkv), blk(256);
-    if (head_dim == 128) hipLaunchKernelGGL((k3_combine<128>), g, blk, 0, s, a, seq_off, part_o, part_ml);
-    else hipLaunchKernelGGL((k3_combine<64>), g, blk, 0, s, a, seq_off, part_o, part_ml);
+    if (f16) {
+        if (head_dim == 128) hipLaunchKernelGGL((k3_combine<_Float16, 128>), g, blk, 0, s, a, seq_off, part_o, part_ml);
+        else hipLaunchKernelGGL((k3_combine<_Float16, 64>), g, blk, 0, s, a, seq_off, part_o, part_ml);
+    } else {
+        if (head_dim == 128) hipLaunchKernelGGL((k3_combine<__bf16, 128>), g, blk, 0, s, a, seq_off, part_o, part_ml);
+        else hipLaunchKernelGGL((k3_combine<__bf16, 64>), g, blk, 0, s, a, seq_off, part_o, part_ml);
+    }
     return hipGetLastError();
 }
 

@@ -130,14 +130,14 @@ hipError_t launch_backward_bf16(const BwdArgs &a, int head_dim, int total_q, con
                                 int k_grid, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, bool part_bf16, bool out_bf16, hipStream_t s);
 hipError_t launch_plan(const PlanArgs &pa, hipStream_t s);
-hipError_t launch_prefill_bf16(const AttnArgs &a, int head_dim, int mode, const int4 *items,
-                               const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);
+hipError_t launch_prefill16(const AttnArgs &a, bool f16, int head_dim, int mode, const int4 *items,
+                            const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);
 hipError_t launch_prefill_f32(const AttnArgs &a, int head_dim, bool paged, const int4 *items,
                               const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);
-hipError_t launch_decode_bf16(const AttnArgs &a, int head_dim, bool paged, const int4 *items,
-                              const int4 *seqinfo, const int32_t *count, int grid, float *part_o,
-                              float2 *part_ml, hipStream_t s);
-hipError_t launch_decode_combine(const AttnArgs &a, int head_dim, const int32_t *seq_off,
+hipError_t launch_decode16(const AttnArgs &a, bool f16, int head_dim, bool paged, const int4 *items,
+                           const int4 *seqinfo, const int32_t *count, int grid, float *part_o,
+                           float2 *part_ml, hipStream_t s);
+hipError_t launch_decode_combine(const AttnArgs &a, bool f16, int head_dim, const int32_t *seq_off,
                                  const float *part_o, const float2 *part_ml, hipStream_t s);
 
 // ---------------------------------------------------------------- device helpers

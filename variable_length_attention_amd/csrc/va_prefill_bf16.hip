@@ -1,9 +1,10 @@
-// bf16 prefill forward on gfx950 matrix cores.
+// bf16 / fp16 prefill forward on gfx950 matrix cores (one kernel template
+// over the 16-bit input type).
 //
 // One workgroup = 4 waves = 128 query rows of one head (32 rows per wave);
 // key/value tiles of 64 rows are staged in LDS (double buffered, one barrier
 // per tile) and shared by the 4 waves.  Per wave and tile:
-//   S^T = K * Q^T      8 (D=128) x 2 MFMA 32x32x16 bf16, fp32 accumulate.
+//   S^T = K * Q^T      8 (D=128) x 2 MFMA 32x32x16 bf16 / f16, fp32 accumulate.
 //                      With keys on the MFMA M side, each lane ends up owning
 //                      one query row: the row max needs one cross-lane step
 //                      (lanes l and l^32) and the row sum none until the end.
@@ -37,11 +38,43 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p)
-{
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4 *)((__attribute__((address_space(3))) uint16_t *)(p)));
-}
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
+
+// The 16-bit input type's matrix instruction and transposing LDS read
+// (bf16 and fp16 share the data layout and the fp32 accumulation).
+template <typename T>
+struct Elt;
+template <>
+struct Elt<__bf16> {
+    typedef bf16x8 v8;
+    typedef bf16x4 v4;
+    static __device__ __forceinline__ v4 read_tr(const uint16_t *p)
+    {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4 *)((__attribute__((address_space(3))) uint16_t *)(p)));
+    }
+    static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Elt<_Float16> {
+    typedef f16x8 v8;
+    typedef f16x4 v4;
+    static __device__ __forceinline__ v4 read_tr(const uint16_t *p)
+    {
+        return __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                                          (lds_fp16x4 *)((__attribute__((address_space(3))) uint16_t *)(p))));
+    }
+    static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // Keeps the computation of x at this point of the instruction stream (an
@@ -105,10 +138,13 @@ __device__ __forceinline__ void wait_vmem_keep()
 }
 __device__ __forceinline__ void wait_vmem() { wait_vmem_keep<0>(); }
 
-template <int D, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k1_prefill_bf16(
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k1_prefill16(
     AttnArgs a, const int4 *__restrict__ items, const int4 *__restrict__ seqinfo, const int32_t *__restrict__ count)
 {
+    using E = Elt<T>;
+    typedef typename E::v8 v8;
+    typedef typename E::v4 v4;
     constexpr int BN = kBN;
     constexpr int NCH = D / 8;         // 16-byte chunks per row
     constexpr int NSEG = NCH / 4;      // 64-byte segments per row
@@ -212,7 +248,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
 
     // Q^T operand fragments: lane (row n, half h2) holds d = 16 ks + 8 h2 .. +8
-    bf16x8 qf[KS];
+    v8 qf[KS];
     {
         const uint16_t *qp = (const uint16_t *)a.q + ((size_t)(q0 + (row_ok ? row : 0)) * a.H + head) * D + h2 * 8;
 #pragma unroll
@@ -220,7 +256,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // unconditional load (rows past the end read row 0), then zeroed
             u32x4 x = *(const u32x4 *)(qp + ks * 16);
             if (!row_ok) x = u32x4{0, 0, 0, 0};
-            qf[ks] = __builtin_bit_cast(bf16x8, x);
+            qf[ks] = __builtin_bit_cast(v8, x);
         }
     }
 
@@ -246,10 +282,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int v = 0; v < 16; ++v) { S[0][v] = 0.f; S[1][v] = 0.f; }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 kf0 = *(const bf16x8 *)(kt + koff(ks));
-            const bf16x8 kf1 = *(const bf16x8 *)(kt + koff(ks) + 32 * ROWB);
-            S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[ks], S[0], 0, 0, 0);
-            S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[ks], S[1], 0, 0, 0);
+            const v8 kf0 = *(const v8 *)(kt + koff(ks));
+            const v8 kf1 = *(const v8 *)(kt + koff(ks) + 32 * ROWB);
+            S[0] = E::mfma(kf0, qf[ks], S[0]);
+            S[1] = E::mfma(kf1, qf[ks], S[1]);
             hook(ks);
         }
     };
@@ -301,15 +337,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         rs += x;
     };
     // bf16 operand of PV step t4 from probabilities computed in place
-    auto cvt_step = [&](f32x16 (&S)[2], int t4) -> bf16x8 {
+    auto cvt_step = [&](f32x16 (&S)[2], int t4) -> v8 {
         f32x8 pv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pv[e] = S[t4 >> 1][(t4 & 1) * 8 + e];
-        return __builtin_convertvector(pv, bf16x8);
+        return __builtin_convertvector(pv, v8);
     };
     // probabilities of PV step t4 (keys 16 t4 .. +16) in bf16, laid out as
     // that step's P^T operand
-    auto probs = [&](f32x16 (&S)[2], int t4, float neg_m, float &rs) -> bf16x8 {
+    auto probs = [&](f32x16 (&S)[2], int t4, float neg_m, float &rs) -> v8 {
         f32x8 pv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -317,16 +353,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             pv[e] = x;
             rs += x;
         }
-        return __builtin_convertvector(pv, bf16x8);
+        return __builtin_convertvector(pv, v8);
     };
     // O^T += V^T P^T for one step of 16 keys
-    auto pv = [&](const bf16x8 &P, int t4, const char *vt) {
+    auto pv = [&](const v8 &P, int t4, const char *vt) {
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
-            const bf16x4 va = lds_read_tr((const uint16_t *)(vt + voff(md) + t4 * 16 * ROWB));
-            const bf16x4 vb = lds_read_tr((const uint16_t *)(vt + voff(md) + (t4 * 16 + 8) * ROWB));
-            const bf16x8 vf = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-            o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P, o[md], 0, 0, 0);
+            const v4 va = E::read_tr((const uint16_t *)(vt + voff(md) + t4 * 16 * ROWB));
+            const v4 vb = E::read_tr((const uint16_t *)(vt + voff(md) + (t4 * 16 + 8) * ROWB));
+            const v8 vf = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+            o[md] = E::mfma(vf, P, o[md]);
         }
     };
 
@@ -391,14 +427,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             auto vhook = [&](int t4) {
                 if (t4 % VEVERY == VEVERY - 1) issue_u(t + 1, true, v_dst, t4 / VEVERY, rs_v);
             };
-            const bf16x8 p0 = cvt_step(Sc, 0);
-            const bf16x8 p1 = cvt_step(Sc, 1);
+            const v8 p0 = cvt_step(Sc, 0);
+            const v8 p1 = cvt_step(Sc, 1);
             pv(p0, 0, v_cur);
             vhook(0);
-            const bf16x8 p2 = probs(Sc, 2, neg_m, rs);
+            const v8 p2 = probs(Sc, 2, neg_m, rs);
             pv(p1, 1, v_cur);
             vhook(1);
-            const bf16x8 p3 = probs(Sc, 3, neg_m, rs);
+            const v8 p3 = probs(Sc, 3, neg_m, rs);
             pv(p2, 2, v_cur);
             vhook(2);
             pv(p3, 3, v_cur);
@@ -434,7 +470,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             f32x4 x;
 #pragma unroll
             for (int j = 0; j < 4; ++j) x[j] = o[md][i * 4 + j] * inv;
-            const bf16x4 y = __builtin_convertvector(x, bf16x4);
+            const v4 y = __builtin_convertvector(x, v4);
             const int phys = (md * 4 + i) ^ (n % NCH);
             *(u32x2 *)(ow + n * ROWB + phys * 16 + h2 * 8) = __builtin_bit_cast(u32x2, y);
         }
@@ -458,20 +494,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const AttnArgs &a, int head_dim, int mode, const int4 *items,
-                               const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s)
+hipError_t launch_prefill16(const AttnArgs &a, bool f16, int head_dim, int mode, const int4 *items,
+                            const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s)
 {
     const dim3 g(grid), blk(256);
-#define VA_LAUNCH(DD, MM) hipLaunchKernelGGL((k1_prefill_bf16<DD, MM>), g, blk, 0, s, a, items, seqinfo, count)
-    if (head_dim == 128) {
-        if (mode == kLoadBuffer) VA_LAUNCH(128, kLoadBuffer);
-        else if (mode == kLoadGlobal) VA_LAUNCH(128, kLoadGlobal);
-        else VA_LAUNCH(128, kLoadPaged);
+#define VA_LAUNCH(TT, DD, MM) hipLaunchKernelGGL((k1_prefill16<TT, DD, MM>), g, blk, 0, s, a, items, seqinfo, count)
+#define VA_MODES(TT, DD)                                   \
+    do {                                                   \
+        if (mode == kLoadBuffer) VA_LAUNCH(TT, DD, kLoadBuffer); \
+        else if (mode == kLoadGlobal) VA_LAUNCH(TT, DD, kLoadGlobal); \
+        else VA_LAUNCH(TT, DD, kLoadPaged);                \
+    } while (0)
+    if (f16) {
+        if (head_dim == 128) VA_MODES(_Float16, 128);
+        else VA_MODES(_Float16, 64);
     } else {
-        if (mode == kLoadBuffer) VA_LAUNCH(64, kLoadBuffer);
-        else if (mode == kLoadGlobal) VA_LAUNCH(64, kLoadGlobal);
-        else VA_LAUNCH(64, kLoadPaged);
+        if (head_dim == 128) VA_MODES(__bf16, 128);
+        else VA_MODES(__bf16, 64);
     }
+#undef VA_MODES
 #undef VA_LAUNCH
     return hipGetLastError();
 }

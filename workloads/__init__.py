@@ -16,6 +16,9 @@ Layouts follow the statement of the problem on the pages:
 * per-head fp32 sink logits ``sinks[H]`` (same README, parameter table row
   ``sinks``; its usage example draws one value per query head).
 
+float16 ("f16") data is numpy's round-to-nearest-even cast of the same
+float32 draws, carried as numpy float16 arrays.
+
 Recipe (all configurations): ``rng = numpy.random.default_rng(seed)`` and,
 in this order, (1) lengths, (2) ``q`` of shape ``[T_q, H, D]`` from
 ``standard_normal(float32)``, (3) per sequence in packing order ``k_b`` then
@@ -142,7 +145,11 @@ def _draw_lengths(spec: Spec, rng: np.random.Generator):
 
 
 def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
-    return f32_to_bf16_bits(x) if dtype == "bf16" else np.ascontiguousarray(x, np.float32)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "f16":
+        return np.ascontiguousarray(x, np.float32).astype(np.float16)  # round to nearest even
+    return np.ascontiguousarray(x, np.float32)
 
 
 def make_case(spec: Spec, *, lens_q=None, lens_k=None, poison: bool = True) -> dict:
@@ -165,7 +172,7 @@ def make_case(spec: Spec, *, lens_q=None, lens_k=None, poison: bool = True) -> d
     cu_k[1:] = np.cumsum(dk)
 
     q = _cast(rng.standard_normal((T_q, H, D), dtype=np.float32), spec.dtype)
-    elt = np.uint16 if spec.dtype == "bf16" else np.float32
+    elt = {"bf16": np.uint16, "f16": np.float16}.get(spec.dtype, np.float32)
     case = dict(spec=spec, B=B, H=H, Hkv=Hkv, D=D, dtype=spec.dtype,
                 scale=spec.softmax_scale, causal=bool(spec.causal),
                 window_left=int(spec.window[0]), window_right=int(spec.window[1]),
@@ -191,7 +198,7 @@ def make_case(spec: Spec, *, lens_q=None, lens_k=None, poison: bool = True) -> d
     nblk = [(int(x) + bs - 1) // bs for x in dk]
     n_used = int(sum(nblk))
     W = max(max(nblk) if nblk else 1, 1)
-    poison_val = POISON_BF16 if spec.dtype == "bf16" else np.float32(POISON_F32)
+    poison_val = {"bf16": POISON_BF16, "f16": np.float16(POISON_F32)}.get(spec.dtype, np.float32(POISON_F32))
     # one spare physical block at the end holds only poison
     k_cache = np.empty((n_used + 1, bs, Hkv, D), dtype=elt)
     v_cache = np.empty((n_used + 1, bs, Hkv, D), dtype=elt)
