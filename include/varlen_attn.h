@@ -71,7 +71,9 @@
 extern "C" {
 #endif
 
-#define VARLEN_ATTN_ABI_VERSION 1
+/* 1: forward, plan, backward.  2: adds VA_F16, va_problem.alibi_slopes and
+ * varlen_attn_merge (version 1 structs are still accepted). */
+#define VARLEN_ATTN_ABI_VERSION 2
 
 typedef enum {
     VA_OK = 0,
@@ -110,6 +112,17 @@ typedef struct {
     int32_t num_blocks;       /* paged: blocks in the cache                        */
     int32_t block_size;       /* paged: tokens per block, multiple of 16, <= 1024  */
     int32_t block_table_stride; /* paged: int32 entries per block_table row        */
+    /* Fields below were appended in ABI version 2; a caller whose struct_size
+     * ends before a field gets its default (NULL). */
+    const float *alibi_slopes;  /* device float32 [H] or NULL: the score of query
+                                 * i and key j of head h gets
+                                 * - alibi_slopes[h] * |i + Lk - Lq - j|
+                                 * (distance to the query's end-aligned position,
+                                 * added after the scale; sinks unaffected).  The
+                                 * pages list alibi_slopes in the op schema of the
+                                 * pull request "[varlen_attn for inference] add
+                                 * out variant" without its formula; this is the
+                                 * reading taken.  Forward only.                  */
 } va_problem;
 
 /* Bytes of device workspace `varlen_attn_fwd_out` (paged = 0) or

@@ -45,7 +45,7 @@ class _Args(ctypes.Structure):
         ("cu_q", ctypes.c_void_p), ("cu_k", ctypes.c_void_p),
         ("seqused_k", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
         ("bt_stride", ctypes.c_int32), ("block_size", ctypes.c_int32),
-        ("sinks", ctypes.c_void_p),
+        ("sinks", ctypes.c_void_p), ("alibi", ctypes.c_void_p),
     ]
 
 
@@ -123,6 +123,7 @@ def _make_args(case: dict, keep: list) -> _Args:
         a.v = _ptr(c(case["v"], elt))
         a.cu_k = _ptr(c(case["cu_k"], np.int32))
     a.sinks = _ptr(c(case.get("sinks"), np.float32))
+    a.alibi = _ptr(c(case.get("alibi"), np.float32))
     return a
 
 

@@ -59,6 +59,7 @@ def dense_forward(case, return_probs=False):
     lse = np.full((case["T_q"], H), -np.inf)
     probs = {}
     sinks = case.get("sinks")
+    alibi = case.get("alibi")
     for b in range(case["B"]):
         s, e = int(case["cu_q"][b]), int(case["cu_q"][b + 1])
         Lq = e - s
@@ -68,6 +69,9 @@ def dense_forward(case, return_probs=False):
         for h in range(H):
             c = h // g
             S = (q_all[s:e, h, :] @ k[:, c, :].T) * case["scale"]
+            if alibi is not None:
+                pos = np.arange(Lq)[:, None] + (Lk - Lq)
+                S = S - float(alibi[h]) * np.abs(pos - np.arange(Lk)[None, :])
             S = np.where(ok, S, -np.inf)
             V = v[:, c, :]
             if sinks is not None:

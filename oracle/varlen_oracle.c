@@ -61,6 +61,8 @@ typedef struct {
     const int32_t *block_table; /* [B, bt_stride], NULL = contiguous mode  */
     int32_t bt_stride, block_size;
     const float *sinks;         /* [H] or NULL                             */
+    const float *alibi;         /* [H] slopes or NULL: score of (i, j) gets
+                                 * - slope_h * |i + Lk - Lq - j|         */
 } oracle_args;
 
 /* IEEE 754 binary16 -> double, exact: sign, 5-bit exponent (bias 15),
@@ -105,6 +107,14 @@ static size_t kv_offset(const oracle_args *a, int b, int j, int c)
     return (row * a->Hkv + c) * (size_t)a->D;
 }
 
+/* ALiBi term of query i, key j (0 without slopes) */
+static double alibi_bias(const oracle_args *a, int h, long i, long j, long delta)
+{
+    if (!a->alibi) return 0.0;
+    const long dist = i + delta - j;
+    return -(double)a->alibi[h] * (double)(dist < 0 ? -dist : dist);
+}
+
 static int is_allowed(const oracle_args *a, long i, long j, long delta)
 {
     long p = i + delta;
@@ -133,7 +143,7 @@ static void one_row(const oracle_args *a, int b, int i, int h, double *scores,
         double dot = 0.0;
         for (int d = 0; d < D; ++d)
             dot += widen(a->dtype, a->q, qoff + d) * widen(a->dtype, a->k, koff + d);
-        scores[j] = dot * a->scale;
+        scores[j] = dot * a->scale + alibi_bias(a, h, i, j, delta);
         if (scores[j] > m) m = scores[j];
     }
     if (a->sinks && (double)a->sinks[h] > m) m = (double)a->sinks[h];
@@ -325,7 +335,7 @@ static void bwd_unit(const bwd_pool_t *p, int b, int c)
                     s += widen(a->dtype, a->q, qoff + d) * widen(a->dtype, a->k, koff + d);
                     dp += p->dout[qoff + d] * widen(a->dtype, a->v, koff + d);
                 }
-                s *= a->scale;
+                s = s * a->scale + alibi_bias(a, h, i, j, delta);
                 const double pr = exp(s - l);
                 const double ds = pr * (dp - dv_row);
                 for (int d = 0; d < D; ++d) {

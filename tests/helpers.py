@@ -31,20 +31,22 @@ def run_case(case, torch, *, out=None, workspace=None, return_lse=True):
     q = dev(case["q"], torch)
     cu_q = dev(case["cu_q"], torch)
     sinks = dev(case.get("sinks"), torch)
+    alibi = dev(case.get("alibi"), torch)
     win = (case["window_left"], case["window_right"])
     if case.get("paged"):
         kc, vc = dev(case["k_cache"], torch), dev(case["v_cache"], torch)
         bt, su = dev(case["block_table"], torch), dev(case["seqused_k"], torch)
         o, lse = va.varlen_attn_paged(q, kc, vc, bt, cu_q, su, case["max_q"], case["max_k"],
                                       scale=case["scale"], causal=case["causal"], window=win,
-                                      sinks=sinks, out=out, return_lse=True, workspace=workspace)
+                                      sinks=sinks, out=out, return_lse=True, workspace=workspace,
+                                      alibi_slopes=alibi)
     else:
         k, v, cu_k = dev(case["k"], torch), dev(case["v"], torch), dev(case["cu_k"], torch)
         if out is None:
             out = torch.empty_like(q)
         lse = va.varlen_attn_out(out, q, k, v, cu_q, cu_k, case["max_q"], case["max_k"],
                                  scale=case["scale"], causal=case["causal"], window=win,
-                                 sinks=sinks, return_lse=True, workspace=workspace)
+                                 sinks=sinks, return_lse=True, workspace=workspace, alibi_slopes=alibi)
         o = out
     torch.cuda.synchronize()
     return o, lse

@@ -28,12 +28,37 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.varlen_attn_abi_version() == 1
+    assert lib.varlen_attn_abi_version() == 2
 
 
-def test_problem_struct_size_matches_header():
-    # 17 four-byte fields
-    assert ctypes.sizeof(_lib.VaProblem) == 17 * 4
+def test_problem_struct_matches_header(tmp_path):
+    # the ctypes mirror against the header itself, compiled by the host C compiler
+    import subprocess
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "varlen_attn.h"\n'
+                   'int main(void) { printf("%zu %zu %zu\\n", sizeof(va_problem), '
+                   'offsetof(va_problem, block_table_stride), offsetof(va_problem, alibi_slopes)); return 0; }\n')
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-I", inc, str(src), "-o", str(exe)], check=True)
+    size, bts, alibi = map(int, subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split())
+    assert ctypes.sizeof(_lib.VaProblem) == size
+    assert _lib.VaProblem.block_table_stride.offset == bts
+    assert _lib.VaProblem.alibi_slopes.offset == alibi
+
+
+def test_version_one_problem_struct_is_accepted():
+    # a caller built against version 1 (struct ends after block_table_stride)
+    # (host checks only: the size queries launch nothing)
+    lib = _lib.load()
+    p = _prob()
+    p.alibi_slopes = 0x1234
+    assert lib.varlen_attn_bwd_workspace_size(ctypes.byref(p)) == 0     # slopes: backward refuses
+    p.struct_size = _lib.VaProblem.block_table_stride.offset + 4
+    assert lib.varlen_attn_bwd_workspace_size(ctypes.byref(p)) > 0      # beyond the struct: not read
+    assert lib.varlen_attn_workspace_size(ctypes.byref(p), 0) > 0
+    p.struct_size -= 4
+    assert lib.varlen_attn_workspace_size(ctypes.byref(p), 0) == 0      # shorter than version 1
 
 
 def _prob(**kw):

@@ -39,6 +39,7 @@ class VaProblem(ctypes.Structure):
         ("scale", ctypes.c_float), ("causal", ctypes.c_int32), ("window_left", ctypes.c_int32),
         ("window_right", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
         ("block_size", ctypes.c_int32), ("block_table_stride", ctypes.c_int32),
+        ("alibi_slopes", ctypes.c_void_p),
     ]
 
 

@@ -54,7 +54,7 @@ def output_shapes(q: torch.Tensor):
 
 
 def make_problem(q, num_kv_heads, total_k, batch, max_seqlen_q, max_seqlen_k, scale, causal,
-                 window, num_blocks=0, block_size=0, block_table_stride=0) -> _lib.VaProblem:
+                 window, num_blocks=0, block_size=0, block_table_stride=0, alibi_slopes=None) -> _lib.VaProblem:
     _need(q.dim() == 3, "q must be [total_q, num_heads, head_dim]")
     _need(q.dtype in _DTYPES, f"dtype {q.dtype} not supported (float32, bfloat16 or float16)")
     p = _lib.VaProblem()
@@ -69,6 +69,10 @@ def make_problem(q, num_kv_heads, total_k, batch, max_seqlen_q, max_seqlen_k, sc
     p.causal = 1 if causal else 0
     p.window_left, p.window_right = int(window[0]), int(window[1])
     p.num_blocks, p.block_size, p.block_table_stride = int(num_blocks), int(block_size), int(block_table_stride)
+    if alibi_slopes is not None:
+        _need(alibi_slopes.dtype == torch.float32 and alibi_slopes.numel() == q.shape[1] and
+              alibi_slopes.is_cuda and alibi_slopes.is_contiguous(), "alibi_slopes must be float32 [num_heads] on the GPU")
+        p.alibi_slopes = alibi_slopes.data_ptr()
     return p
 
 
@@ -105,16 +109,17 @@ def _workspace(problem, paged, dev, workspace):
 def varlen_attn_out(out: torch.Tensor, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
                     max_seqlen_k: int, *, scale: Optional[float] = None, causal: bool = False,
                     window: Tuple[int, int] = (-1, -1), sinks=None, lse=None,
-                    return_lse: bool = False, workspace=None):
+                    return_lse: bool = False, workspace=None, alibi_slopes=None):
     """Writes attention over contiguous packed K/V into ``out``; returns the
-    float32 LSE when ``return_lse`` (or an ``lse`` buffer is given), else None."""
+    float32 LSE when ``return_lse`` (or an ``lse`` buffer is given), else None.
+    ``alibi_slopes`` (float32 [num_heads]) adds -slope * |i + Lk - Lq - j|."""
     dev = _check_tensors(out, q, k, v, cu_seqlens_q, cu_seqlens_k, sinks, lse, workspace)
     _need(k.dim() == 3 and v.shape == k.shape, "k and v must be [total_k, num_kv_heads, head_dim]")
     _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32, "cu_seqlens must be int32")
     _need(out.dtype == q.dtype and k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v, out must share a dtype")
     _need(out.shape == q.shape, "out must have q's shape")
     p = make_problem(q, k.shape[1], k.shape[0], cu_seqlens_q.numel() - 1, max_seqlen_q, max_seqlen_k,
-                     scale, causal, window)
+                     scale, causal, window, alibi_slopes=alibi_slopes)
     if return_lse and lse is None:
         lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=dev)
     if sinks is not None:
@@ -129,19 +134,19 @@ def varlen_attn_out(out: torch.Tensor, q, k, v, cu_seqlens_q, cu_seqlens_k, max_
 
 def varlen_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, *,
                 scale: Optional[float] = None, causal: bool = False,
-                window: Tuple[int, int] = (-1, -1), sinks=None, return_lse: bool = False):
+                window: Tuple[int, int] = (-1, -1), sinks=None, return_lse: bool = False, alibi_slopes=None):
     """Allocating form: returns out, or (out, lse) when ``return_lse``."""
     out = torch.empty_like(q)
     lse = varlen_attn_out(out, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                           scale=scale, causal=causal, window=window, sinks=sinks,
-                          return_lse=return_lse)
+                          return_lse=return_lse, alibi_slopes=alibi_slopes)
     return (out, lse) if return_lse else out
 
 
 def varlen_attn_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, max_seqlen_q: int,
                       max_seqlen_k: int, *, scale: Optional[float] = None, causal: bool = False,
                       window: Tuple[int, int] = (-1, -1), sinks=None, out=None, lse=None,
-                      return_lse: bool = False, workspace=None):
+                      return_lse: bool = False, workspace=None, alibi_slopes=None):
     """Paged K/V: caches [num_blocks, block_size, num_kv_heads, head_dim],
     block_table int32 [batch, stride], seqused_k int32 [batch]."""
     dev = _check_tensors(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, sinks, out, lse,
@@ -151,7 +156,8 @@ def varlen_attn_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k,
     _need(block_table.dtype == torch.int32 and block_table.dim() == 2, "block_table must be int32 [batch, stride]")
     _need(seqused_k.dtype == torch.int32 and cu_seqlens_q.dtype == torch.int32, "seqused_k / cu_seqlens_q must be int32")
     p = make_problem(q, k_cache.shape[2], 0, cu_seqlens_q.numel() - 1, max_seqlen_q, max_seqlen_k, scale,
-                     causal, window, k_cache.shape[0], k_cache.shape[1], block_table.shape[1])
+                     causal, window, k_cache.shape[0], k_cache.shape[1], block_table.shape[1],
+                     alibi_slopes=alibi_slopes)
     if out is None:
         out = torch.empty_like(q)
     if return_lse and lse is None:

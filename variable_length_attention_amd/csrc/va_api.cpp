@@ -10,6 +10,7 @@
 #include "va_internal.h"
 
 #include <cmath>
+#include <cstddef>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -61,13 +62,21 @@ struct Layout {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Size of the version-1 va_problem (fields up to block_table_stride); later
+// fields take their defaults when struct_size ends before them.
+constexpr size_t kProblemV1 = offsetof(va_problem, block_table_stride) + sizeof(int32_t);
+const float *alibi_of(const va_problem *p)
+{
+    return p->struct_size >= offsetof(va_problem, alibi_slopes) + sizeof(p->alibi_slopes) ? p->alibi_slopes
+                                                                                          : nullptr;
+}
+
 // Validation of the problem description alone (no pointers).
 va_status check_problem(const va_problem *p, int paged)
 {
     if (!p) return fail(VA_ERR_NULL, "problem descriptor is NULL");
-    if (p->struct_size < sizeof(va_problem))
-        return fail(VA_ERR_SHAPE, "va_problem.struct_size %u is smaller than %zu", p->struct_size,
-                    sizeof(va_problem));
+    if (p->struct_size < kProblemV1)
+        return fail(VA_ERR_SHAPE, "va_problem.struct_size %u is smaller than %zu", p->struct_size, kProblemV1);
     if (p->dtype != VA_F32 && p->dtype != VA_BF16 && p->dtype != VA_F16)
         return fail(VA_ERR_DTYPE, "dtype %d is not VA_F32 (0), VA_BF16 (1) or VA_F16 (2)", p->dtype);
     if (p->batch < 1) return fail(VA_ERR_SHAPE, "batch %d < 1", p->batch);
@@ -189,7 +198,7 @@ va_status check_pointers(const Call &c, const Layout &L)
         return fail(VA_ERR_ALIGN, "q, k, v, out and workspace must be 16-byte aligned");
     if (!aligned(c.cu_q, 4) || (c.cu_k && !aligned(c.cu_k, 4)) || (c.seqused_k && !aligned(c.seqused_k, 4)) ||
         (c.block_table && !aligned(c.block_table, 4)) || (c.sinks && !aligned(c.sinks, 4)) ||
-        (c.lse && !aligned(c.lse, 4)))
+        (c.lse && !aligned(c.lse, 4)) || (alibi_of(p) && !aligned(alibi_of(p), 4)))
         return fail(VA_ERR_ALIGN, "int32 / float32 arrays must be 4-byte aligned");
 
     const size_t es = p->dtype == VA_F32 ? 4 : 2;
@@ -206,6 +215,7 @@ va_status check_pointers(const Call &c, const Layout &L)
         {c.seqused_k, c.seqused_k ? 4 * (size_t)p->batch : 0},
         {c.block_table, c.block_table ? 4 * (size_t)p->batch * p->block_table_stride : 0},
         {c.sinks, c.sinks ? 4 * (size_t)p->num_heads : 0},
+        {alibi_of(p), alibi_of(p) ? 4 * (size_t)p->num_heads : 0},
         {c.ws, c.ws_bytes},
     };
     for (const Range &r : ins) {
@@ -224,6 +234,7 @@ va::AttnArgs make_args(const Call &c)
     a.out = c.out; a.lse = c.lse;
     a.cu_q = c.cu_q; a.cu_k = c.cu_k; a.seqused_k = c.seqused_k; a.block_table = c.block_table;
     a.sinks = c.sinks;
+    a.alibi = alibi_of(p);
     a.B = p->batch; a.H = p->num_heads; a.Hkv = p->num_kv_heads; a.g = p->num_heads / p->num_kv_heads;
     a.bt_stride = c.paged ? p->block_table_stride : 0;
     a.block_size = c.paged ? p->block_size : 1;
@@ -316,8 +327,8 @@ va_status run(const Call &c, hipStream_t s)
         {
             const size_t span = (size_t)c.p->max_seqlen_k * c.p->num_kv_heads * c.p->head_dim * 2;
             const int mode = c.paged ? va::kLoadPaged : (span < ((size_t)1 << 31) ? va::kLoadBuffer : va::kLoadGlobal);
-            e = va::launch_prefill16(a, c.p->dtype == VA_F16, c.p->head_dim, mode, pa.items, pa.seqinfo, pa.count,
-                                     (int)L.grid, s);
+            e = va::launch_prefill16(a, c.p->dtype == VA_F16, a.alibi != nullptr, c.p->head_dim, mode, pa.items,
+                                     pa.seqinfo, pa.count, (int)L.grid, s);
         }
         else if (L.path == kPathF32)
             e = va::launch_prefill_f32(a, c.p->head_dim, c.paged, pa.items, pa.seqinfo, pa.count, (int)L.grid, s);
@@ -366,6 +377,7 @@ va_status bwd_layout(const va_problem *p, BwdLayout &L)
     va_status st = check_problem(p, 0);
     if (st) return st;
     if (p->dtype != VA_BF16) return fail(VA_ERR_UNSUPPORTED, "the backward takes bf16 inputs");
+    if (alibi_of(p)) return fail(VA_ERR_UNSUPPORTED, "the backward does not take alibi_slopes");
     const long long nq = ((long long)p->total_q + (long long)p->batch * (va::kBM - 1)) / va::kBM;
     const long long nk = ((long long)p->total_k + (long long)p->batch * (va::kBwdKeys - 1)) / va::kBwdKeys;
     const long long gq = nq * p->num_heads, gk = nk * p->num_kv_heads;

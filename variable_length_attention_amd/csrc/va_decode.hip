@@ -115,6 +115,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int qi = n / a.g, head = c * a.g + n % a.g;
     int lo = 1, hi = 0;
     if (row_ok) row_bounds(qi, delta, Lk, a.left, a.right, lo, hi);
+    // ALiBi: - slope * |qi + delta - j| in log2 units (0 without slopes,
+    // which leaves every score unchanged)
+    const float sl2 = (a.alibi && row_ok) ? a.alibi[head] * kLog2e : 0.f;
+    const int pos = qi + delta;
     // keys every packed row sees: rows are ordered by query index
     int flo = 0x7fffffff, fhi = -1;
     if (rows > 0) {
@@ -250,7 +254,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    s[kb][v] *= a.scale_log2;
+                    const int j = j0 + kb * 16 + kq * 4 + v;
+                    s[kb][v] = fmaf(-sl2, fabsf((float)(pos - j)), s[kb][v] * a.scale_log2);
                     mx = fmaxf(mx, s[kb][v]);
                 }
         } else {
@@ -259,7 +264,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int j = j0 + kb * 16 + kq * 4 + v;
-                    const float x = (j >= lo && j <= hi) ? s[kb][v] * a.scale_log2 : -INFINITY;
+                    const float x = (j >= lo && j <= hi) ? fmaf(-sl2, fabsf((float)(pos - j)), s[kb][v] * a.scale_log2)
+                                                         : -INFINITY;
                     s[kb][v] = x;
                     mx = fmaxf(mx, x);
                 }

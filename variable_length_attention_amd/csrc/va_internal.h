@@ -41,6 +41,7 @@ struct AttnArgs {
     const int32_t *seqused_k;    // [B]   paged mode
     const int32_t *block_table;  // [B, bt_stride] paged mode
     const float *sinks;          // [H] or null
+    const float *alibi;          // [H] slopes or null
     int32_t B, H, Hkv, g;
     int32_t bt_stride, block_size;
     int32_t bs_shift;            // log2(block_size) when a power of two, else -1
@@ -130,7 +131,7 @@ hipError_t launch_backward_bf16(const BwdArgs &a, int head_dim, int total_q, con
                                 int k_grid, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, bool part_bf16, bool out_bf16, hipStream_t s);
 hipError_t launch_plan(const PlanArgs &pa, hipStream_t s);
-hipError_t launch_prefill16(const AttnArgs &a, bool f16, int head_dim, int mode, const int4 *items,
+hipError_t launch_prefill16(const AttnArgs &a, bool f16, bool alibi, int head_dim, int mode, const int4 *items,
                             const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);
 hipError_t launch_prefill_f32(const AttnArgs &a, int head_dim, bool paged, const int4 *items,
                               const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);

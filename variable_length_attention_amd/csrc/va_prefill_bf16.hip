@@ -138,7 +138,7 @@ __device__ __forceinline__ void wait_vmem_keep()
 }
 __device__ __forceinline__ void wait_vmem() { wait_vmem_keep<0>(); }
 
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, bool ALIBI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k1_prefill16(
     AttnArgs a, const int4 *__restrict__ items, const int4 *__restrict__ seqinfo, const int32_t *__restrict__ count)
 {
@@ -181,6 +181,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool row_ok = row < Lq;
     int lo = 1, hi = 0;
     if (row_ok) row_bounds(row, delta, Lk, a.left, a.right, lo, hi);
+    // ALiBi in raw-score units (the scores are scaled after the max):
+    // - (slope / scale) * |row + delta - j|
+    float alibi_r = 0.f;
+    if constexpr (ALIBI) alibi_r = a.alibi[head] / a.scale;
+    const int pos = row + delta;
 
     // keys this wave can see (wlo..whi) and keys all its rows see (flo..fhi)
     int wlo = 1, whi = 0, flo = 0x7fffffff, fhi = -1;
@@ -293,6 +298,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // tile raises it by more than the slack (raw scores; scale > 0)
     auto row_max = [&](f32x16 (&S)[2], int t) {
         const int j0 = kv_lo + t * BN;
+        if constexpr (ALIBI) {
+            // lane value v of block mb is key j0 + 32 mb + 8 (v/4) + 4 h2 + v%4
+            const float base = (float)(pos - j0 - 4 * h2);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    S[mb][v] = fmaf(-alibi_r, fabsf(base - (float)(32 * mb + 8 * (v >> 2) + (v & 3))), S[mb][v]);
+        }
         float mx = -INFINITY;
         if (j0 >= flo && j0 + BN - 1 <= fhi) {
 #pragma unroll
@@ -494,24 +508,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 }  // namespace
 
-hipError_t launch_prefill16(const AttnArgs &a, bool f16, int head_dim, int mode, const int4 *items,
+hipError_t launch_prefill16(const AttnArgs &a, bool f16, bool alibi, int head_dim, int mode, const int4 *items,
                             const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s)
 {
     const dim3 g(grid), blk(256);
-#define VA_LAUNCH(TT, DD, MM) hipLaunchKernelGGL((k1_prefill16<TT, DD, MM>), g, blk, 0, s, a, items, seqinfo, count)
-#define VA_MODES(TT, DD)                                   \
-    do {                                                   \
-        if (mode == kLoadBuffer) VA_LAUNCH(TT, DD, kLoadBuffer); \
-        else if (mode == kLoadGlobal) VA_LAUNCH(TT, DD, kLoadGlobal); \
-        else VA_LAUNCH(TT, DD, kLoadPaged);                \
+#define VA_LAUNCH(TT, DD, MM, AA) \
+    hipLaunchKernelGGL((k1_prefill16<TT, DD, MM, AA>), g, blk, 0, s, a, items, seqinfo, count)
+#define VA_MODES(TT, DD, AA)                                          \
+    do {                                                              \
+        if (mode == kLoadBuffer) VA_LAUNCH(TT, DD, kLoadBuffer, AA);  \
+        else if (mode == kLoadGlobal) VA_LAUNCH(TT, DD, kLoadGlobal, AA); \
+        else VA_LAUNCH(TT, DD, kLoadPaged, AA);                       \
+    } while (0)
+#define VA_DIMS(TT, AA)                          \
+    do {                                         \
+        if (head_dim == 128) VA_MODES(TT, 128, AA); \
+        else VA_MODES(TT, 64, AA);               \
     } while (0)
     if (f16) {
-        if (head_dim == 128) VA_MODES(_Float16, 128);
-        else VA_MODES(_Float16, 64);
+        if (alibi) VA_DIMS(_Float16, true);
+        else VA_DIMS(_Float16, false);
     } else {
-        if (head_dim == 128) VA_MODES(__bf16, 128);
-        else VA_MODES(__bf16, 64);
+        if (alibi) VA_DIMS(__bf16, true);
+        else VA_DIMS(__bf16, false);
     }
+#undef VA_DIMS
 #undef VA_MODES
 #undef VA_LAUNCH
     return hipGetLastError();

@@ -39,6 +39,10 @@ __global__ __launch_bounds__(256) void k1_prefill_f32(AttnArgs a, const int4 *__
     const bool row_ok = row < Lq;
     int lo = 1, hi = 0;
     if (row_ok) row_bounds(row, Lk - Lq, Lk, a.left, a.right, lo, hi);
+    // ALiBi: - slope * |row + Lk - Lq - j| in log2 units (0 without slopes,
+    // which leaves every score unchanged)
+    const float sl2 = a.alibi ? a.alibi[head] * kLog2e : 0.f;
+    const int pos = row + Lk - Lq;
 
     // lane `part` owns float4 chunks part, part+4, part+8, ...
     float4 qv[NC4], ov[NC4];
@@ -87,7 +91,7 @@ __global__ __launch_bounds__(256) void k1_prefill_f32(AttnArgs a, const int4 *__
             d += __shfl_xor(d, 1);
             d += __shfl_xor(d, 2);
             const int j = j0 + jj;
-            const float x = (j >= lo && j <= hi) ? d * a.scale_log2 : -INFINITY;
+            const float x = (j >= lo && j <= hi) ? fmaf(-sl2, fabsf((float)(pos - j)), d * a.scale_log2) : -INFINITY;
             sc[jj] = x;
             mx = fmaxf(mx, x);
         }
