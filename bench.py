@@ -15,7 +15,8 @@ shape, the sliding-window + sinks MQA shape (bound by HBM) and the paged
 decode shape (bound by HBM), each with its own step time and roofline;
 (key "backward") one call of the backward on the main workload; and (key
 "merge") the log-sum-exp merge of 8 float32 partials of the full-attention
-shard (a ring of 8), bound by HBM.
+shard (a ring of 8), bound by HBM; and (key "sparse") sliding-window +
+sparse compressed attention over shared K/V.
 
 The roofline figure is for the dominant kernel: its average duration is the
 step time minus the pre-pass time, both measured here with HIP events on
@@ -244,6 +245,70 @@ def time_merge(steps, warmup, torch):
     return e0.elapsed_time(e1) / steps, nbytes
 
 
+SPARSE_SHAPE = dict(lens_q=[1024] * 4, seqused_kv=[8192] * 4, H=64, Hkv=1, D=128, window=(127, 0), topk=512,
+                    cmp_ratio=4, ori_bs=128, cmp_bs=128, seed=4600)
+
+
+def sparse_work(sc):
+    """(FLOPs, algorithmic bytes) of sliding-window + sparse compressed
+    attention: 4 * D FLOPs per (token, head, valid key); bytes = q, out, lse,
+    the indices, block tables and each sequence's distinct original rows in
+    some window and distinct selected compressed rows (read once)."""
+    cu = sc["cu_q"]
+    left, right = sc["window"]
+    g = sc["H"] // sc["Hkv"]
+    keys, rows = 0, 0
+    for b in range(sc["B"]):
+        S2, Lq = int(sc["seqused_kv"][b]), int(cu[b + 1] - cu[b])
+        if Lq == 0:
+            continue
+        S3 = S2 // sc["cmp_ratio"]
+        p = np.arange(Lq) + S2 - Lq
+        lo, hi = np.maximum(0, p - left), np.minimum(S2 - 1, p + right)
+        nwin = np.maximum(0, hi - lo + 1)
+        idx = sc["indices"][cu[b]:cu[b + 1]] if sc["topk"] else np.zeros((Lq, sc["Hkv"], 0), np.int32)
+        ok = (idx >= 0) & (idx < S3)
+        keys += int(nwin.sum()) * sc["Hkv"] + int(ok.sum())
+        seen = np.zeros(S2, bool)
+        for a_, z in zip(lo, hi):
+            if z >= a_:
+                seen[a_:z + 1] = True
+        rows += int(seen.sum()) * sc["Hkv"] + sum(len(np.unique(idx[:, c][ok[:, c]])) for c in range(sc["Hkv"]))
+    D, es = sc["D"], 2
+    fl = 4.0 * D * g * keys
+    by = (2.0 * sc["T"] * sc["H"] * D * es + 4.0 * sc["T"] * sc["H"] + 4.0 * sc["indices"].size
+          + 4.0 * (sc["ori_table"].size + sc["cmp_table"].size) + rows * D * es)
+    return fl, by
+
+
+def time_sparse(steps, warmup, torch):
+    """Sliding-window + sparse compressed attention over shared K/V on
+    SPARSE_SHAPE; returns (ms per call, FLOPs, algorithmic bytes)."""
+    import variable_length_attention_amd as va
+    import workloads as W
+    sc = W.sparse_case(**SPARSE_SHAPE)
+    args = [_dev(sc[k], torch) for k in ("q", "ori_kv", "ori_table", "seqused_kv", "cmp_kv", "cmp_table",
+                                          "indices", "cu_q")]
+    sinks = _dev(sc["sinks"], torch)
+    out = torch.empty_like(args[0])
+    lse = torch.empty((sc["T"], sc["H"]), dtype=torch.float32, device="cuda")
+
+    def step():
+        va.varlen_attn_sparse_sharedkv(*args, sc["max_seqlen_kv"], scale=sc["scale"], window=sc["window"],
+                                       cmp_ratio=sc["cmp_ratio"], sinks=sinks, out=out, lse=lse)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    fl, by = sparse_work(sc)
+    return e0.elapsed_time(e1) / steps, fl, by
+
+
 # ---------------------------------------------------------------- HBM traffic
 def kernel_source_sha(path_name):
     import hashlib
@@ -349,6 +414,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-merge", action="store_true", help="skip the log-sum-exp merge timing")
+    ap.add_argument("--no-sparse", action="store_true", help="skip the sparse shared-KV attention timing")
     ap.add_argument("--configs", default="2,3,4,5", help="workloads to time (first is the main one)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
@@ -458,6 +524,20 @@ def main():
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                       "frac": gbs / PEAK_HBM_GBS, "traffic": None}}
         log(f"merge: {ms_m:.4f} ms/call, {gbs:.0f} GB/s")
+    if not args.no_sparse:
+        log("sparse shared-KV attention (4 x 1024 tokens over 8192 keys, 64/1 heads, window 128 + 512 selected)")
+        ms_s, fl_s, by_s = time_sparse(args.steps, args.warmup, torch)
+        tf_s, gb_s = fl_s / (ms_s * 1e-3) / 1e12, by_s / (ms_s * 1e-3) / 1e9
+        hbm = (fl_s / by_s) < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+        line["sparse"] = {
+            "workload": "sliding window (127, 0) + 512 selected of 4x compressed keys, shared K/V, "
+                        "4 x 1024 tokens over 8192 keys, 64 heads / 1 kv head, d128, bf16",
+            "ms_per_step": ms_s, "tflops": tf_s, "gbs": gb_s, "flop": fl_s, "bytes": by_s,
+            "roofline": ({"bound": "hbm", "achieved": gb_s, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": gb_s / PEAK_HBM_GBS, "traffic": None} if hbm else
+                         {"bound": "mfma", "achieved": tf_s, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": tf_s / PEAK_BF16_TFLOPS, "traffic": None})}
+        log(f"sparse: {ms_s:.4f} ms/call, {tf_s:.1f} TFLOP/s, {gb_s:.0f} GB/s (algorithmic)")
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a sample of rows")
         line["cpu_baseline"] = cpu_baseline(main_case)

@@ -71,8 +71,9 @@
 extern "C" {
 #endif
 
-/* 1: forward, plan, backward.  2: adds VA_F16, va_problem.alibi_slopes and
- * varlen_attn_merge (version 1 structs are still accepted). */
+/* 1: forward, plan, backward.  2: adds VA_F16, va_problem.alibi_slopes,
+ * varlen_attn_merge and varlen_attn_sparse_sharedkv (version 1 structs are
+ * still accepted). */
 #define VARLEN_ATTN_ABI_VERSION 2
 
 typedef enum {
@@ -228,6 +229,56 @@ va_status varlen_attn_merge(int32_t n_parts, int32_t rows, int32_t num_heads, in
                             va_dtype parts_dtype, va_dtype out_dtype, const void *o_parts,
                             const float *lse_parts, const float *sinks, void *out, float *lse,
                             void *stream);
+
+/* Sliding-window + sparse compressed attention over shared K/V: the third
+ * scenario of the SparseAttnSharedkv README (ori_kv, cmp_kv and
+ * cmp_sparse_indices given; K~ = V~ in its formula: one tensor row serves as
+ * key and value).  For token t (row i of sequence b, Lq_b rows, S2_b =
+ * seqused_kv[b] original keys) and each query head h of kv head c:
+ *   window keys:   original positions j in [p - window_left, p + window_right]
+ *                  and [0, S2_b), p = i + S2_b - Lq_b (aligned to the end),
+ *                  read from ori_kv through ori_block_table;
+ *   selected keys: compressed positions cmp_sparse_indices[t][c][0 .. topk-1]
+ *                  read from cmp_kv through cmp_block_table; an index outside
+ *                  [0, S2_b / cmp_ratio) selects nothing; a repeated index
+ *                  is attended as often as it appears;
+ *   out[t][h] = sum_j w_j kv_j,  w = softmax over the window and selected keys
+ *               of scale <q[t][h], kv_j>, with sinks[h] as an extra logit;
+ *   lse[t][h] = natural log of that softmax's denominator.
+ * The README leaves the compression operator and its mask mode 3 undefined;
+ * here the compressed rows are given and every selected row is visible.
+ *   q, out            [total_q, H, D] dtype (VA_BF16 / VA_F16), TND
+ *   ori_kv            [ori_num_blocks, ori_block_size, H_kv, D], PA_ND
+ *   cmp_kv            [cmp_num_blocks, cmp_block_size, H_kv, D], PA_ND
+ *   ori_block_table   int32 [batch, ori_block_table_stride]
+ *   cmp_block_table   int32 [batch, cmp_block_table_stride]
+ *   seqused_kv        int32 [batch], <= max_seqlen_kv
+ *   cmp_sparse_indices int32 [total_q, H_kv, topk] (NULL iff topk = 0)
+ *   cu_seqlens_q      int32 [batch + 1]; sinks float32 [H] or NULL;
+ *   lse               float32 [total_q, H] or NULL
+ * Limits: D in {64, 128}; H / H_kv <= 64; bounded window (both sides >= 0)
+ * with window_left + window_right + 1 + topk <= 1536; cmp_ratio >= 1.  Same
+ * ownership, stream, alignment and aliasing rules as the forward; nothing
+ * is allocated and no workspace is needed. */
+typedef struct {
+    uint32_t struct_size;       /* sizeof(va_sparse_problem)                    */
+    int32_t dtype;              /* VA_BF16 or VA_F16                            */
+    int32_t batch, total_q;     /* B >= 1, rows of q (>= 1)                     */
+    int32_t num_heads, num_kv_heads, head_dim;
+    int32_t max_seqlen_kv;      /* host bound of every seqused_kv[b]            */
+    float scale;                /* > 0                                          */
+    int32_t window_left, window_right;
+    int32_t topk;               /* selected compressed keys per (token, kv head) */
+    int32_t cmp_ratio;          /* compressed keys of sequence b: S2_b / ratio  */
+    int32_t ori_num_blocks, ori_block_size, ori_block_table_stride;
+    int32_t cmp_num_blocks, cmp_block_size, cmp_block_table_stride;
+} va_sparse_problem;
+
+va_status varlen_attn_sparse_sharedkv(const va_sparse_problem *p, const void *q, const void *ori_kv,
+                                      const int32_t *ori_block_table, const int32_t *seqused_kv,
+                                      const void *cmp_kv, const int32_t *cmp_block_table,
+                                      const int32_t *cmp_sparse_indices, const int32_t *cu_seqlens_q,
+                                      const float *sinks, void *out, float *lse, void *stream);
 
 /* Which kernel family a call with these arguments would use:
  * 0 = prefill tiles, 1 = split-KV decode with combine, 2 = float32 path;

@@ -18,6 +18,9 @@ which holds no attention arithmetic.
 * ``merge`` -- the log-sum-exp merge of partial results over disjoint key
   sets (the combine step of ring / context-parallel attention that the
   vllm-omni Ulysses wrapper's ring path needs), written out in float64.
+* ``sparse_sharedkv`` -- sliding-window + sparse compressed attention over
+  shared K/V (the SparseAttnSharedkv README's third scenario), written out
+  in float64 token by token.
 """
 from __future__ import annotations
 
@@ -213,3 +216,61 @@ def half_to_double(bits):
     lib = _load()
     b = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
     return np.array([lib.oracle_half_to_double(int(x)) for x in b], dtype=np.float64)
+
+
+def _widen16(a, dtype):
+    a = np.asarray(a)
+    if dtype == "bf16":
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)  # float16 values
+
+
+def sparse_sharedkv(case, tokens=None):
+    """Attention of each query token over its sliding window of original
+    keys plus the compressed keys its indices select (one softmax, sinks as
+    extra logits; each key row is also its value row).  SparseAttnSharedkv
+    README, formula section (K~ = V~ from ori_kv, cmp_kv and the indices) and
+    its third scenario.  Readings: the window is [p - left, p + right] with
+    p = i + S2_b - Lq_b; an index outside [0, S2_b / cmp_ratio) selects
+    nothing; a repeated index is attended as often as it appears.
+    Returns (out [n, H, D], lse [n, H]) in float64 for the given tokens (all
+    tokens by default)."""
+    cu_q = np.asarray(case["cu_q"], np.int64)
+    T, H, Hkv, D = case["T"], case["H"], case["Hkv"], case["D"]
+    g = H // Hkv
+    toks = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    left, right = case["window"]
+    out = np.zeros((len(toks), H, D))
+    lse = np.full((len(toks), H), -np.inf)
+
+    def rows(cache, table, bs, b, positions, c):
+        positions = np.asarray(positions, np.int64)
+        phys = np.asarray(table)[b, positions // bs].astype(np.int64)
+        return _widen16(np.asarray(cache)[phys, positions % bs, c], case["dtype"])
+
+    for n, t in enumerate(toks):
+        b = int(np.searchsorted(cu_q, t, side="right") - 1)
+        i = t - cu_q[b]
+        Lq = cu_q[b + 1] - cu_q[b]
+        S2 = int(case["seqused_kv"][b])
+        S3 = S2 // case["cmp_ratio"]
+        p = i + S2 - Lq
+        win = np.arange(max(0, p - left), min(S2 - 1, p + right) + 1)
+        for c in range(Hkv):
+            sel = np.asarray(case["indices"][t, c], np.int64)
+            sel = sel[(sel >= 0) & (sel < S3)]
+            kv = np.concatenate([rows(case["ori_kv"], case["ori_table"], case["ori_kv"].shape[1], b, win, c),
+                                 rows(case["cmp_kv"], case["cmp_table"], case["cmp_kv"].shape[1], b, sel, c)])
+            heads = np.arange(c * g, (c + 1) * g)
+            qv = _widen16(np.asarray(case["q"])[t, heads], case["dtype"])
+            logits = case["scale"] * (qv @ kv.T)                        # [g, keys]
+            if case.get("sinks") is not None:
+                logits = np.concatenate([logits, np.asarray(case["sinks"], np.float64)[heads][:, None]], axis=1)
+            if logits.shape[1] == 0:
+                continue
+            m = logits.max(axis=1, keepdims=True)
+            w = np.exp(logits - m)
+            z = w.sum(axis=1, keepdims=True)
+            lse[n, heads] = (m + np.log(z))[:, 0]
+            out[n, heads] = (w[:, : kv.shape[0]] / z) @ kv
+    return out, lse

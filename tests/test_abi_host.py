@@ -217,3 +217,38 @@ def test_merge_rejects_before_launching():
     assert _merge(out=(1 << 20) + 256) == 5                               # out inside o_parts
     assert _merge(lse=(2 << 20) + 4) == 5                                 # lse inside lse_parts
     assert _merge(lse=(3 << 20) + 64) == 5                                # lse inside out
+
+
+def _sparse(**kw):
+    p = _lib.VaSparseProblem()
+    p.struct_size = ctypes.sizeof(_lib.VaSparseProblem)
+    d = dict(dtype=1, batch=2, total_q=10, num_heads=64, num_kv_heads=1, head_dim=128, max_seqlen_kv=4096,
+             scale=0.088, window_left=127, window_right=0, topk=512, cmp_ratio=4, ori_num_blocks=64,
+             ori_block_size=128, ori_block_table_stride=32, cmp_num_blocks=16, cmp_block_size=128,
+             cmp_block_table_stride=8)
+    ptrs = dict(q=A[0], ori=A[1], ot=A[2], su=A[3], cmp=A[4], ct=A[5], idx=A[6], cuq=A[7], sinks=None,
+                out=A[8], lse=A[9])
+    for k, v in kw.items():
+        (ptrs if k in ptrs else d)[k] = v
+    for k, v in d.items():
+        setattr(p, k, v)
+    return _lib.load().varlen_attn_sparse_sharedkv(ctypes.byref(p), ptrs["q"], ptrs["ori"], ptrs["ot"], ptrs["su"],
+                                                   ptrs["cmp"], ptrs["ct"], ptrs["idx"], ptrs["cuq"], ptrs["sinks"],
+                                                   ptrs["out"], ptrs["lse"], None)
+
+
+def test_sparse_rejects_before_launching():
+    # fake, never dereferenced addresses: each call fails one host check
+    assert _sparse(dtype=0) == 3                      # float32 not taken
+    assert _sparse(num_heads=128) == 4                # 128 query heads per kv head
+    assert _sparse(head_dim=96) == 4
+    assert _sparse(window_left=-1) == 4               # unbounded window
+    assert _sparse(topk=1500) == 4                    # window + topk beyond 1536 keys
+    assert _sparse(cmp_ratio=0) == 2
+    assert _sparse(ori_block_table_stride=31) == 2    # 4096 / 128 = 32 needed
+    assert _sparse(cmp_block_table_stride=7) == 2     # 1024 / 128 = 8 needed
+    assert _sparse(idx=None) == 1                     # topk > 0 needs indices
+    assert _sparse(q=ctypes.c_void_p(A[0].value + 8)) == 6
+    assert _sparse(out=A[1]) == 5                     # out aliases the original cache
+    assert _sparse(lse=ctypes.c_void_p(A[8].value + 64)) == 5  # lse inside out
+    assert _sparse(scale=0.0) == 4

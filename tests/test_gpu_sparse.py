@@ -1,0 +1,98 @@
+"""Parity of sliding-window + sparse compressed attention over shared K/V
+(through the C ABI) with the fp64 oracle.
+
+Tolerances are the forward's for each dtype (bf16: 2e-2 on O, 1e-3 on LSE;
+f16: 5e-3, 1e-3): the kernel computes scores and the softmax the same way
+(fp32 accumulation, probabilities rounded to the input type for P V).
+Rows with no key and no sink must give O = 0 and LSE = -inf.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from helpers import TOL, announce, dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the GPU tests need an MI355X")
+    import variable_length_attention_amd._lib as L
+    L.load()
+    yield
+
+
+def _run(sc):
+    import variable_length_attention_amd as va
+    idx = dev(sc["indices"], torch) if sc["topk"] > 0 else None
+    out, lse = va.varlen_attn_sparse_sharedkv(
+        dev(sc["q"], torch), dev(sc["ori_kv"], torch), dev(sc["ori_table"], torch), dev(sc["seqused_kv"], torch),
+        dev(sc["cmp_kv"], torch), dev(sc["cmp_table"], torch), idx, dev(sc["cu_q"], torch),
+        sc["max_seqlen_kv"], scale=sc["scale"], window=sc["window"], cmp_ratio=sc["cmp_ratio"],
+        sinks=dev(sc["sinks"], torch), return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _compare(sc, out, lse, ref_o, ref_l, what):
+    tol_o, tol_l = TOL[sc["dtype"]]
+    out, lse = np.asarray(out), np.asarray(lse)
+    assert np.all(np.isfinite(out)), f"{what}: non-finite output"
+    np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(ref_l), err_msg=f"{what}: -inf LSE rows")
+    fin = np.isfinite(ref_l)
+    e_o = float(np.max(np.abs(out - ref_o))) if out.size else 0.0
+    e_l = float(np.max(np.abs(lse[fin] - ref_l[fin]))) if fin.any() else 0.0
+    assert e_o <= tol_o, f"{what}: max |O - ref| = {e_o:.3e}"
+    assert e_l <= tol_l, f"{what}: max |LSE - ref| = {e_l:.3e}"
+    announce(f"sparse {what}: O error {e_o:.2e}, LSE error {e_l:.2e}")
+
+
+CASES = {
+    # the README example's structure at a small size: 64 heads over one kv head,
+    # window (127, 0), 512 shared indices into a 4x compressed cache, sinks
+    "readme_shape_shared_indices": dict(lens_q=[128, 128], seqused_kv=[4096, 4096], H=64, Hkv=1, D=128,
+                                        window=(127, 0), topk=512, cmp_ratio=4, shared_indices=True),
+    "per_token_indices_invalid_f16_gqa": dict(lens_q=[70, 33], seqused_kv=[900, 400], H=16, Hkv=2, D=128,
+                                              dtype="f16", window=(31, 5), topk=100, cmp_ratio=4,
+                                              invalid_frac=0.15, ori_bs=48, cmp_bs=16),
+    "ragged_empty_and_keyless_no_sinks": dict(lens_q=[1, 0, 37, 5, 90], seqused_kv=[1, 50, 0, 20, 700], H=8,
+                                              Hkv=1, D=128, window=(63, 0), topk=40, cmp_ratio=2, sinks=False,
+                                              ori_bs=16, cmp_bs=32),
+    "d64_two_sided_window": dict(lens_q=[64, 65], seqused_kv=[300, 129], H=32, Hkv=4, D=64, window=(20, 20),
+                                 topk=64, cmp_ratio=3, invalid_frac=0.05, ori_bs=64, cmp_bs=64),
+    "window_only_short_history": dict(lens_q=[16, 40], seqused_kv=[10, 40], H=64, Hkv=1, D=128,
+                                      window=(127, 0), topk=0, cmp_ratio=4),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_sparse_matches_oracle(name):
+    sc = W.sparse_case(**CASES[name], seed=4500 + len(name))
+    announce(f"sparse {name}")
+    out, lse = _run(sc)
+    ref_o, ref_l = oracle.sparse_sharedkv(sc)
+    _compare(sc, to_f64(out), to_f64(lse), ref_o, ref_l, name)
+
+
+# benchmark workload: 4 sequences of 1024 query tokens over 8192 original
+# keys each, 64 heads / 1 kv head, d128, window (127, 0), 512 indices per
+# token into a 4x compressed cache, 128-token blocks, sinks
+BENCH = dict(lens_q=[1024] * 4, seqused_kv=[8192] * 4, H=64, Hkv=1, D=128, window=(127, 0), topk=512,
+             cmp_ratio=4, ori_bs=128, cmp_bs=128, seed=4600)
+
+
+def test_sparse_benchmark_size_sampled():
+    sc = W.sparse_case(**BENCH)
+    announce("sparse benchmark size: running")
+    out, lse = _run(sc)
+    rng = np.random.default_rng(3)
+    toks = np.unique(np.concatenate([rng.integers(0, sc["T"], 96), [0, 1023, 1024, sc["T"] - 1]]))
+    ref_o, ref_l = oracle.sparse_sharedkv(sc, tokens=toks)
+    ti = torch.from_numpy(toks).cuda()
+    _compare(sc, to_f64(out[ti]), to_f64(lse[ti]), ref_o, ref_l, "benchmark size sampled")
+    assert bool(torch.isfinite(out).all())

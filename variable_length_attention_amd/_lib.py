@@ -25,7 +25,7 @@ EXPORTED = [
     "varlen_attn_workspace_size", "varlen_attn_fwd_out", "varlen_attn_fwd",
     "varlen_attn_fwd_paged", "varlen_attn_free", "varlen_attn_plan", "varlen_attn_path",
     "varlen_attn_last_error", "varlen_attn_abi_version", "varlen_attn_bwd_workspace_size",
-    "varlen_attn_bwd", "varlen_attn_merge",
+    "varlen_attn_bwd", "varlen_attn_merge", "varlen_attn_sparse_sharedkv",
 ]
 
 
@@ -41,6 +41,16 @@ class VaProblem(ctypes.Structure):
         ("block_size", ctypes.c_int32), ("block_table_stride", ctypes.c_int32),
         ("alibi_slopes", ctypes.c_void_p),
     ]
+
+
+class VaSparseProblem(ctypes.Structure):
+    """Mirror of ``va_sparse_problem`` in include/varlen_attn.h."""
+    _fields_ = [(name, ctypes.c_uint32 if name == "struct_size" else
+                 ctypes.c_float if name == "scale" else ctypes.c_int32) for name in (
+        "struct_size", "dtype", "batch", "total_q", "num_heads", "num_kv_heads", "head_dim",
+        "max_seqlen_kv", "scale", "window_left", "window_right", "topk", "cmp_ratio",
+        "ori_num_blocks", "ori_block_size", "ori_block_table_stride",
+        "cmp_num_blocks", "cmp_block_size", "cmp_block_table_stride")]
 
 
 _lock = threading.Lock()
@@ -85,6 +95,8 @@ def load():
         i32 = ctypes.c_int32
         lib.varlen_attn_merge.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp]
         lib.varlen_attn_merge.restype = ctypes.c_int
+        lib.varlen_attn_sparse_sharedkv.argtypes = [ctypes.POINTER(VaSparseProblem)] + [vp] * 12
+        lib.varlen_attn_sparse_sharedkv.restype = ctypes.c_int
         lib.varlen_attn_abi_version.argtypes = []
         lib.varlen_attn_abi_version.restype = ctypes.c_int
         _lib = lib

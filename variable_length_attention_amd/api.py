@@ -16,6 +16,9 @@ request "[varlen_attn for inference] add out variant"):
   varlen_attn_bwd    backward (dq, dk, dv) for bf16 contiguous K/V
   varlen_attn_merge  merge of partial results over disjoint key sets
                      through their log-sum-exp (ring / context parallel)
+  varlen_attn_sparse_sharedkv
+                     sliding-window + sparse compressed attention over shared
+                     K/V (SparseAttnSharedkv README, third scenario)
 """
 from __future__ import annotations
 
@@ -28,7 +31,7 @@ import torch
 from . import _lib
 
 __all__ = ["varlen_attn", "varlen_attn_out", "varlen_attn_paged", "varlen_attn_fwd", "varlen_attn_bwd",
-           "bwd_workspace_size", "varlen_attn_merge",
+           "bwd_workspace_size", "varlen_attn_merge", "varlen_attn_sparse_sharedkv",
            "workspace_size", "plan", "kernel_path", "output_shapes", "make_problem"]
 
 _DTYPES = {torch.float32: _lib.VA_F32, torch.bfloat16: _lib.VA_BF16, torch.float16: _lib.VA_F16}
@@ -293,3 +296,51 @@ def varlen_attn_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, sinks: 
                                              _ptr(o_parts), _ptr(lse_parts), _ptr(sinks), _ptr(out), _ptr(lse),
                                              _stream(dev)))
     return (out, lse) if return_lse else out
+
+
+def varlen_attn_sparse_sharedkv(q, ori_kv, ori_block_table, seqused_kv, cmp_kv, cmp_block_table,
+                                cmp_sparse_indices, cu_seqlens_q, max_seqlen_kv: int, *,
+                                scale: Optional[float] = None, window: Tuple[int, int] = (127, 0),
+                                cmp_ratio: int = 4, sinks=None, out=None, lse=None, return_lse: bool = False):
+    """Sliding-window + sparse compressed attention over shared K/V.
+    q [total_q, H, D] bf16 / f16; ori_kv / cmp_kv paged caches
+    [blocks, block_size, H_kv, D]; block tables int32 [batch, stride];
+    seqused_kv int32 [batch]; cmp_sparse_indices int32 [total_q, H_kv, topk]
+    (or None for none); cu_seqlens_q int32 [batch + 1]."""
+    dev = _check_tensors(q, ori_kv, ori_block_table, seqused_kv, cmp_kv, cmp_block_table, cmp_sparse_indices,
+                         cu_seqlens_q, sinks, out, lse)
+    _need(q.dim() == 3 and q.dtype in (torch.bfloat16, torch.float16), "q must be bf16 / f16 [total_q, H, D]")
+    _need(ori_kv.dim() == 4 and cmp_kv.dim() == 4 and ori_kv.dtype == q.dtype and cmp_kv.dtype == q.dtype,
+          "caches must be [blocks, block_size, num_kv_heads, head_dim] in q's dtype")
+    _need(ori_kv.shape[2] == cmp_kv.shape[2] and ori_kv.shape[3] == q.shape[2] and cmp_kv.shape[3] == q.shape[2],
+          "caches must share num_kv_heads and q's head_dim")
+    for name, t in (("ori_block_table", ori_block_table), ("cmp_block_table", cmp_block_table),
+                    ("seqused_kv", seqused_kv), ("cu_seqlens_q", cu_seqlens_q)):
+        _need(t.dtype == torch.int32, f"{name} must be int32")
+    topk = 0 if cmp_sparse_indices is None else int(cmp_sparse_indices.shape[-1])
+    if cmp_sparse_indices is not None:
+        _need(cmp_sparse_indices.dtype == torch.int32 and cmp_sparse_indices.dim() == 3 and
+              tuple(cmp_sparse_indices.shape[:2]) == (q.shape[0], ori_kv.shape[2]),
+              "cmp_sparse_indices must be int32 [total_q, num_kv_heads, topk]")
+    p = _lib.VaSparseProblem()
+    p.struct_size = ctypes.sizeof(_lib.VaSparseProblem)
+    p.dtype = _DTYPES[q.dtype]
+    p.batch, p.total_q = cu_seqlens_q.numel() - 1, int(q.shape[0])
+    p.num_heads, p.num_kv_heads, p.head_dim = int(q.shape[1]), int(ori_kv.shape[2]), int(q.shape[2])
+    p.max_seqlen_kv = int(max_seqlen_kv)
+    p.scale = float(1.0 / math.sqrt(q.shape[2]) if scale is None else scale)
+    p.window_left, p.window_right = int(window[0]), int(window[1])
+    p.topk, p.cmp_ratio = topk, int(cmp_ratio)
+    p.ori_num_blocks, p.ori_block_size, p.ori_block_table_stride = (int(ori_kv.shape[0]), int(ori_kv.shape[1]),
+                                                                    int(ori_block_table.shape[1]))
+    p.cmp_num_blocks, p.cmp_block_size, p.cmp_block_table_stride = (int(cmp_kv.shape[0]), int(cmp_kv.shape[1]),
+                                                                    int(cmp_block_table.shape[1]))
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=dev)
+    _lib.check(_lib.load().varlen_attn_sparse_sharedkv(
+        ctypes.byref(p), _ptr(q), _ptr(ori_kv), _ptr(ori_block_table), _ptr(seqused_kv), _ptr(cmp_kv),
+        _ptr(cmp_block_table), _ptr(cmp_sparse_indices), _ptr(cu_seqlens_q), _ptr(sinks), _ptr(out), _ptr(lse),
+        _stream(dev)))
+    return (out, lse) if (return_lse or lse is not None) else out

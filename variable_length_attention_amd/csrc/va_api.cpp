@@ -9,6 +9,7 @@
 #include "../../include/varlen_attn.h"
 #include "va_internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstddef>
 #include <cstdarg>
@@ -513,6 +514,88 @@ va_status varlen_attn_merge(int32_t n_parts, int32_t rows, int32_t num_heads, in
     a.o_parts = o_parts; a.lse_parts = lse_parts; a.sinks = sinks; a.out = out; a.lse = lse;
     a.n = n_parts; a.rows = rows; a.H = num_heads; a.D = head_dim;
     const hipError_t e = va::launch_merge(a, parts_dtype == VA_BF16, out_dtype == VA_BF16, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(VA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return VA_OK;
+}
+
+va_status varlen_attn_sparse_sharedkv(const va_sparse_problem *p, const void *q, const void *ori_kv,
+                                      const int32_t *ori_block_table, const int32_t *seqused_kv,
+                                      const void *cmp_kv, const int32_t *cmp_block_table,
+                                      const int32_t *cmp_sparse_indices, const int32_t *cu_seqlens_q,
+                                      const float *sinks, void *out, float *lse, void *stream)
+{
+    if (!p) return fail(VA_ERR_NULL, "problem descriptor is NULL");
+    if (p->struct_size < sizeof(va_sparse_problem))
+        return fail(VA_ERR_SHAPE, "va_sparse_problem.struct_size %u is smaller than %zu", p->struct_size,
+                    sizeof(va_sparse_problem));
+    if (p->dtype != VA_BF16 && p->dtype != VA_F16)
+        return fail(VA_ERR_DTYPE, "dtype %d is not VA_BF16 (1) or VA_F16 (2)", p->dtype);
+    if (p->batch < 1 || p->total_q < 1) return fail(VA_ERR_SHAPE, "batch and total_q must be >= 1");
+    if (p->num_heads < 1 || p->num_kv_heads < 1 || p->num_heads % p->num_kv_heads != 0)
+        return fail(VA_ERR_SHAPE, "num_heads %d must be a positive multiple of num_kv_heads %d", p->num_heads,
+                    p->num_kv_heads);
+    if (p->num_heads / p->num_kv_heads > 64)
+        return fail(VA_ERR_UNSUPPORTED, "more than 64 query heads per kv head");
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return fail(VA_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", p->head_dim);
+    if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return fail(VA_ERR_UNSUPPORTED, "scale must be finite and > 0");
+    if (p->window_left < 0 || p->window_right < 0 || p->topk < 0 ||
+        (long long)p->window_left + p->window_right + 1 + p->topk > va::kSpListMax)
+        return fail(VA_ERR_UNSUPPORTED, "window (%d, %d) must be bounded and window + topk %d at most %d keys",
+                    p->window_left, p->window_right, p->topk, va::kSpListMax);
+    if (p->cmp_ratio < 1) return fail(VA_ERR_SHAPE, "cmp_ratio %d < 1", p->cmp_ratio);
+    if (p->max_seqlen_kv < 0 || p->max_seqlen_kv > va::kMaxSeqlen)
+        return fail(VA_ERR_SHAPE, "max_seqlen_kv %d outside [0, %d]", p->max_seqlen_kv, va::kMaxSeqlen);
+    if (p->ori_num_blocks < 1 || p->ori_block_size < 1 || p->cmp_num_blocks < 1 || p->cmp_block_size < 1)
+        return fail(VA_ERR_SHAPE, "block counts and sizes must be >= 1");
+    const long long ori_need = ((long long)p->max_seqlen_kv + p->ori_block_size - 1) / p->ori_block_size;
+    const long long cmp_need = ((long long)(p->max_seqlen_kv / p->cmp_ratio) + p->cmp_block_size - 1) / p->cmp_block_size;
+    if (p->ori_block_table_stride < ori_need || p->cmp_block_table_stride < cmp_need)
+        return fail(VA_ERR_SHAPE, "block table strides (%d, %d) below (%lld, %lld) blocks", p->ori_block_table_stride,
+                    p->cmp_block_table_stride, ori_need, cmp_need);
+    if (!q || !ori_kv || !ori_block_table || !seqused_kv || !cmp_kv || !cmp_block_table || !cu_seqlens_q || !out ||
+        (p->topk > 0 && !cmp_sparse_indices))
+        return fail(VA_ERR_NULL, "a required pointer is NULL");
+    const void *al16[] = {q, ori_kv, cmp_kv, out};
+    for (const void *ptr : al16)
+        if (!aligned(ptr, 16)) return fail(VA_ERR_ALIGN, "q, ori_kv, cmp_kv and out must be 16-byte aligned");
+    const void *al4[] = {ori_block_table, seqused_kv, cmp_block_table, cmp_sparse_indices, cu_seqlens_q, sinks, lse};
+    for (const void *ptr : al4)
+        if (ptr && !aligned(ptr, 4)) return fail(VA_ERR_ALIGN, "int32 / float32 arrays must be 4-byte aligned");
+    const size_t D = (size_t)p->head_dim, H = (size_t)p->num_heads, Hkv = (size_t)p->num_kv_heads;
+    const size_t T = (size_t)p->total_q;
+    const Range o_r{out, T * H * D * 2}, l_r{lse, lse ? T * H * 4 : 0};
+    const Range ins[] = {
+        {q, T * H * D * 2},
+        {ori_kv, (size_t)p->ori_num_blocks * p->ori_block_size * Hkv * D * 2},
+        {cmp_kv, (size_t)p->cmp_num_blocks * p->cmp_block_size * Hkv * D * 2},
+        {ori_block_table, 4 * (size_t)p->batch * p->ori_block_table_stride},
+        {cmp_block_table, 4 * (size_t)p->batch * p->cmp_block_table_stride},
+        {seqused_kv, 4 * (size_t)p->batch},
+        {cmp_sparse_indices, cmp_sparse_indices ? 4 * T * Hkv * p->topk : 0},
+        {cu_seqlens_q, 4 * ((size_t)p->batch + 1)},
+        {sinks, sinks ? 4 * H : 0},
+    };
+    for (const Range &r : ins) {
+        if (overlaps(o_r, r)) return fail(VA_ERR_ALIAS, "out overlaps an input");
+        if (overlaps(l_r, r)) return fail(VA_ERR_ALIAS, "lse overlaps an input");
+    }
+    if (overlaps(o_r, l_r)) return fail(VA_ERR_ALIAS, "out overlaps lse");
+    va::SparseArgs a;
+    a.q = q; a.ori_kv = ori_kv; a.ori_table = ori_block_table; a.seqused_kv = seqused_kv;
+    a.cmp_kv = cmp_kv; a.cmp_table = cmp_block_table; a.indices = cmp_sparse_indices; a.cu_q = cu_seqlens_q;
+    a.sinks = sinks; a.out = out; a.lse = lse;
+    a.B = p->batch; a.T = p->total_q; a.H = p->num_heads; a.Hkv = p->num_kv_heads;
+    a.g = p->num_heads / p->num_kv_heads; a.topk = p->topk;
+    a.ori_bs = p->ori_block_size; a.ori_stride = p->ori_block_table_stride;
+    a.cmp_bs = p->cmp_block_size; a.cmp_stride = p->cmp_block_table_stride; a.cmp_ratio = p->cmp_ratio;
+    a.left = p->window_left; a.right = p->window_right;
+    a.scale_log2 = p->scale * va::kLog2e;
+    // tokens per workgroup: about 1536 workgroups (4 per CU of 2 waves each,
+    // 1.5 rounds), at least 1 and at most kSpTokMax tokens each
+    const long long units = (long long)p->total_q * p->num_kv_heads;
+    a.tok_per_wg = (int)std::min<long long>(va::kSpTokMax, std::max<long long>(1, (units + 1535) / 1536));
+    const hipError_t e = va::launch_sparse16(a, p->dtype == VA_F16, p->head_dim, (hipStream_t)stream);
     if (e != hipSuccess) return fail(VA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return VA_OK;
 }

@@ -90,6 +90,29 @@ struct BwdArgs {
     float scale, scale_log2;
 };
 
+// Sliding-window + sparse compressed attention over shared K/V (the
+// third scenario of the SparseAttnSharedkv README).
+constexpr int kSpTokMax = 16;    // tokens per workgroup, at most
+constexpr int kSpListMax = 1536; // window + selected keys per token, at most (LDS: 4 workgroups per CU)
+struct SparseArgs {
+    const void *q;                   // [T_q, H, D]
+    const void *ori_kv;              // [ori_blocks, ori_bs, Hkv, D], K = V
+    const int32_t *ori_table;        // [B, ori_stride]
+    const int32_t *seqused_kv;       // [B] original keys per sequence
+    const void *cmp_kv;              // [cmp_blocks, cmp_bs, Hkv, D], K = V
+    const int32_t *cmp_table;        // [B, cmp_stride]
+    const int32_t *indices;          // [T_q, Hkv, topk] compressed positions
+    const int32_t *cu_q;             // [B + 1]
+    const float *sinks;              // [H] or null
+    void *out;                       // [T_q, H, D]
+    float *lse;                      // [T_q, H] or null
+    int32_t B, T, H, Hkv, g, topk;
+    int32_t tok_per_wg;              // consecutive tokens per workgroup
+    int32_t ori_bs, ori_stride, cmp_bs, cmp_stride, cmp_ratio;
+    int32_t left, right;             // window on the original keys (kInfOff = unbounded)
+    float scale_log2;
+};
+
 // Merge of partial results over disjoint key sets.
 struct MergeArgs {
     const void *o_parts;         // [n, rows, H, D]
@@ -130,6 +153,7 @@ hipError_t launch_backward_bf16(const BwdArgs &a, int head_dim, int total_q, con
                                 const int4 *k_items, const int4 *k_seqinfo, const int32_t *k_count,
                                 int k_grid, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, bool part_bf16, bool out_bf16, hipStream_t s);
+hipError_t launch_sparse16(const SparseArgs &a, bool f16, int head_dim, hipStream_t s);
 hipError_t launch_plan(const PlanArgs &pa, hipStream_t s);
 hipError_t launch_prefill16(const AttnArgs &a, bool f16, bool alibi, int head_dim, int mode, const int4 *items,
                             const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);

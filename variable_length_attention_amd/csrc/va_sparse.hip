@@ -1,0 +1,329 @@
+// Sliding-window + sparse compressed attention over shared K/V on gfx950
+// matrix cores (the third scenario of the SparseAttnSharedkv README: q
+// attends to the original keys in its sliding window and to the compressed
+// keys its sparse indices select, in one softmax, with per-head sinks; the
+// same tensor rows serve as keys and values).
+//
+// Per token t of sequence b, kv head c, the key list is
+//   window:   original positions [p - left, p + right] within [0, S2_b),
+//             p = i + S2_b - Lq_b (aligned to the end of the keys),
+//   selected: compressed positions cmp_sparse_indices[t, c, 0 .. topk-1],
+//             those outside [0, S2_b / cmp_ratio) select nothing;
+// and for each of the g query heads h of c
+//   O[t, h] = softmax_j(scale <q[t, h], kv_j>, sink_h) . kv_j.
+//
+// One workgroup = 2 waves = up to 64 query heads of one kv head (heads on
+// the MFMA N side: each lane owns one head), a few consecutive tokens in
+// turn (chosen by the host so that the grid fills the chip).
+// For each token the physical rows of its key list go to LDS, then 64-row
+// tiles are gathered global -> LDS (double buffered, one barrier per tile).
+// A tile is read row-wise as the K operand (S^T = K Q^T, keys on M) and
+// through the transposing LDS read as the V^T operand (O^T += V^T P^T):
+// one XOR swizzle of the 16-byte chunks serves both without bank
+// conflicts.  Keys that select nothing carry a -inf bias.
+#include "va_internal.h"
+
+namespace va {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
+
+template <typename T>
+struct Elt;
+template <>
+struct Elt<__bf16> {
+    typedef bf16x8 v8;
+    typedef bf16x4 v4;
+    static __device__ __forceinline__ v4 read_tr(const char *p)
+    {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)((__attribute__((address_space(3))) char *)(p)));
+    }
+    static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Elt<_Float16> {
+    typedef f16x8 v8;
+    typedef f16x4 v4;
+    static __device__ __forceinline__ v4 read_tr(const char *p)
+    {
+        return __builtin_bit_cast(
+            v4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)((__attribute__((address_space(3))) char *)(p))));
+    }
+    static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// Physical 16-byte chunk of logical chunk c in LDS row r is c ^ swz(r): the
+// rows of a row-wise operand read and the 4 rows x 4 chunks of a
+// transposing read land on distinct chunks (D = 128; D = 64 per pair of
+// rows sharing a 256-byte bank line).
+template <int D>
+__device__ __forceinline__ int swz(int r)
+{
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// 16 bytes per lane, global -> LDS (lane i writes LDS bytes [lds + 16 i, +16));
+// no register results, M0 carries the LDS address.  Ordered by the kernel's
+// own vector-memory wait and barrier before a slot is read.
+__device__ __forceinline__ void copy16_global(const void *src, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)(p);
+}
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ float halves_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void k5_sparse16(SparseArgs a)
+{
+    using E = Elt<T>;
+    typedef typename E::v8 v8;
+    typedef typename E::v4 v4;
+    constexpr int BN = 64;             // keys per tile
+    constexpr int NCH = D / 8;         // 16-byte chunks per row
+    constexpr int KS = D / 16;         // QK^T k-steps
+    constexpr int MD = D / 32;         // 32-wide blocks of the head dimension
+    constexpr int RPI = 64 / NCH;      // rows one 64-lane copy fills
+    constexpr int LPW = BN / RPI / 2;  // copies per wave per tile (2 waves)
+    constexpr int ROWB = D * 2;
+    constexpr int TILEB = BN * ROWB;
+    __shared__ __attribute__((aligned(16))) char s_tile[2 * TILEB];
+    __shared__ int s_list[kSpListMax];     // physical row of each key, -1: selects nothing
+    __shared__ __attribute__((aligned(16))) float s_bias[2][BN];
+
+    const int c = blockIdx.y;
+    const int t0 = blockIdx.x * a.tok_per_wg;
+    const int t_end = min(a.T, t0 + a.tok_per_wg);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, h2 = lane >> 5, l16 = lane & 15, q4 = l16 >> 2;
+    const int hrow = wave * 32 + n;           // head of the group this lane owns
+    const bool head_ok = hrow < a.g;
+    const int head = c * a.g + (head_ok ? hrow : 0);
+
+    // sequence of the first token: the last b with cu_q[b] <= t0
+    int b = 0;
+    {
+        int lo_b = 0, hi_b = a.B - 1;
+        while (lo_b < hi_b) {
+            const int mid = (lo_b + hi_b + 1) >> 1;
+            if (a.cu_q[mid] <= t0) lo_b = mid;
+            else hi_b = mid - 1;
+        }
+        b = lo_b;
+    }
+
+    // LDS offsets: row-wise K operand read of key row 32 mb + n, chunk
+    // 2 ks + h2; transposing V^T read of rows 16 t4 + 4 h2 + q4 (+8)
+    auto koff = [&](int mb, int ks) -> uint32_t {
+        const int r = mb * 32 + n;
+        return r * ROWB + (((ks * 2 + h2) ^ swz<D>(r)) << 4);
+    };
+    auto toff = [&](int md, int half) -> uint32_t {
+        const int r = h2 * 4 + q4 + half * 8;
+        const int col = md * 32 + ((lane & 31) >> 4) * 16 + (l16 & 3) * 4;
+        return r * ROWB + (((col >> 3) ^ swz<D>(r)) << 4) + (col & 7) * 2;
+    };
+    const float sink2 = (a.sinks && head_ok) ? a.sinks[head] * kLog2e : -INFINITY;
+
+    for (int t = t0; t < t_end; ++t) {
+        while (a.cu_q[b + 1] <= t) ++b;  // empty sequences are stepped over
+        const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
+        const int i = t - q0;
+        const int S2 = a.seqused_kv[b];
+        const int S3 = S2 / a.cmp_ratio;
+        const int p = i + S2 - Lq;
+        const int win_lo = a.left >= kInfOff ? 0 : max(0, p - a.left);
+        const int win_hi = a.right >= kInfOff ? S2 - 1 : min(S2 - 1, p + a.right);
+        const int nwin = max(0, win_hi - win_lo + 1);
+        const int L = nwin + a.topk;                 // <= kSpListMax (checked on the host)
+        const int ntiles = (L + BN - 1) / BN;
+
+        // physical rows of the key list
+        for (int kk = tid; kk < L; kk += 128) {
+            int row;
+            if (kk < nwin) {
+                const int pos = win_lo + kk;
+                row = a.ori_table[(size_t)b * a.ori_stride + pos / a.ori_bs] * a.ori_bs + pos % a.ori_bs;
+            } else {
+                const int idx = a.indices[((size_t)t * a.Hkv + c) * a.topk + (kk - nwin)];
+                row = (idx >= 0 && idx < S3)
+                          ? a.cmp_table[(size_t)b * a.cmp_stride + idx / a.cmp_bs] * a.cmp_bs + idx % a.cmp_bs
+                          : -1;
+            }
+            s_list[kk] = row;
+        }
+        // Q^T operand fragments: lane (head n, half h2) holds d = 16 ks + 8 h2 .. +8
+        v8 qf[KS];
+        {
+            const uint16_t *qp = (const uint16_t *)a.q + ((size_t)t * a.H + head) * D + h2 * 8;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 x = *(const u32x4 *)(qp + ks * 16);
+                if (!head_ok) x = u32x4{0, 0, 0, 0};
+                qf[ks] = __builtin_bit_cast(v8, x);
+            }
+        }
+        __syncthreads();  // the list is complete
+
+        // tile tau's rows into slot; the bias of each key goes with it
+        auto issue = [&](int tau, int slot) {
+#pragma unroll
+            for (int u = 0; u < LPW; ++u) {
+                const int r = (wave * LPW + u) * RPI + lane / NCH;
+                const int kk = tau * BN + r;
+                const int row = kk < L ? s_list[kk] : -1;
+                const char *base = (const char *)(kk < nwin ? a.ori_kv : a.cmp_kv);
+                const int chunk = (lane % NCH) ^ swz<D>(r);
+                // a key that selects nothing re-reads row 0 of the original
+                // cache (finite data under a -inf bias)
+                const size_t off = ((size_t)(row >= 0 ? row : 0) * a.Hkv + c) * ROWB + chunk * 16;
+                copy16_global((row >= 0 ? base : (const char *)a.ori_kv) + off,
+                              lds_addr(s_tile + slot * TILEB + (wave * LPW + u) * 1024));
+                if (lane % NCH == 0) s_bias[slot][r] = row >= 0 ? 0.f : -INFINITY;
+            }
+        };
+
+        f32x16 o[MD];
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[md][v] = 0.f;
+        float m_run = sink2, l_run = (sink2 != -INFINITY && h2 == 0) ? 1.f : 0.f;
+
+        if (ntiles > 0) issue(0, 0);
+        wait_vmem();
+        __syncthreads();
+        for (int tau = 0; tau < ntiles; ++tau) {
+            const int slot = tau & 1;
+            if (tau + 1 < ntiles) issue(tau + 1, slot ^ 1);
+            const char *kt = s_tile + slot * TILEB;
+            // S^T = K Q^T: lane value v of block mb is key 32 mb + 8 (v/4) + 4 h2 + v%4
+            f32x16 S[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) S[mb][v] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    S[mb] = E::mfma(*(const v8 *)(kt + koff(mb, ks)), qf[ks], S[mb]);
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const f32x4 bias = *(const f32x4 *)&s_bias[slot][mb * 32 + e4 * 8 + h2 * 4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = S[mb][e4 * 4 + e] * a.scale_log2 + bias[e];
+                        S[mb][e4 * 4 + e] = x;
+                        mx = fmaxf(mx, x);
+                    }
+                }
+            mx = halves_max(mx);
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // m_run = -inf -> 0
+            l_run *= alpha;
+#pragma unroll
+            for (int md = 0; md < MD; ++md)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
+            m_run = m_new;
+            float rs = 0.f;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float pr = __builtin_amdgcn_exp2f(S[mb][v] - m_use);
+                    S[mb][v] = pr;
+                    rs += pr;
+                }
+            l_run += rs;
+            // O^T += V^T P^T, 16 keys per step
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4) {
+                f32x8 pv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pv[e] = S[t4 >> 1][(t4 & 1) * 8 + e];
+                const v8 pb = __builtin_convertvector(pv, v8);
+#pragma unroll
+                for (int md = 0; md < MD; ++md) {
+                    const v4 va = E::read_tr(kt + toff(md, 0) + t4 * 16 * ROWB);
+                    const v4 vb = E::read_tr(kt + toff(md, 1) + t4 * 16 * ROWB);
+                    o[md] = E::mfma(__builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[md]);
+                }
+            }
+            wait_vmem();
+            __syncthreads();
+        }
+
+        // epilogue: lane (head n, half h2) holds O^T[32 md + 8 i + 4 h2 + j]
+        const float l = halves_sum(l_run);
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        if (head_ok) {
+            uint16_t *op = (uint16_t *)a.out + ((size_t)t * a.H + head) * D;
+#pragma unroll
+            for (int md = 0; md < MD; ++md)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    f32x4 x;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) x[j] = o[md][ii * 4 + j] * inv;
+                    *(u32x2 *)(op + md * 32 + ii * 8 + h2 * 4) =
+                        __builtin_bit_cast(u32x2, __builtin_convertvector(x, v4));
+                }
+            if (a.lse && h2 == 0)
+                a.lse[(size_t)t * a.H + head] = l > 0.f ? (m_run + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_sparse16(const SparseArgs &a, bool f16, int head_dim, hipStream_t s)
+{
+    const dim3 g((a.T + a.tok_per_wg - 1) / a.tok_per_wg, a.Hkv), blk(128);
+    if (f16) {
+        if (head_dim == 128) hipLaunchKernelGGL((k5_sparse16<_Float16, 128>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((k5_sparse16<_Float16, 64>), g, blk, 0, s, a);
+    } else {
+        if (head_dim == 128) hipLaunchKernelGGL((k5_sparse16<__bf16, 128>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((k5_sparse16<__bf16, 64>), g, blk, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace va

@@ -37,7 +37,7 @@ import numpy as np
 
 __all__ = [
     "Spec", "CONFIGS", "config", "scaled", "make_case", "f32_to_bf16_bits",
-    "bf16_bits_to_f32", "case_digest", "POISON_BF16", "POISON_F32", "merge_inputs",
+    "bf16_bits_to_f32", "case_digest", "POISON_BF16", "POISON_F32", "merge_inputs", "sparse_case",
 ]
 
 # Finite poison written into cache slots that no sequence owns.  Read by
@@ -284,3 +284,81 @@ def merge_inputs(n: int, rows: int, H: int, D: int, dtype: str = "f32", seed: in
     if dtype == "bf16":
         o = f32_to_bf16_bits(o)
     return {"o_parts": o, "lse_parts": lse, "n": n, "rows": rows, "H": H, "D": D, "dtype": dtype}
+
+
+def _paged(rng, rows_per_seq, bs, Hkv, D, dtype, poison_val):
+    """Logical rows of each sequence placed in a block-permuted cache with one
+    spare all-poison block; returns (cache, block_table)."""
+    nblk = [(r.shape[0] + bs - 1) // bs for r in rows_per_seq]
+    n_used = int(sum(nblk))
+    W = max(max(nblk) if nblk else 1, 1)
+    elt = {"bf16": np.uint16, "f16": np.float16}[dtype]
+    cache = np.empty((n_used + 1, bs, Hkv, D), dtype=elt)
+    cache[...] = poison_val
+    perm = rng.permutation(n_used).astype(np.int32)
+    table = np.full((len(rows_per_seq), W), n_used, dtype=np.int32)
+    off = 0
+    for b, rows in enumerate(rows_per_seq):
+        for t in range(nblk[b]):
+            phys = int(perm[off + t])
+            table[b, t] = phys
+            r0, r1 = t * bs, min(rows.shape[0], (t + 1) * bs)
+            cache[phys, : r1 - r0] = rows[r0:r1]
+        off += nblk[b]
+    return cache, table
+
+
+def sparse_case(lens_q, seqused_kv, *, H=64, Hkv=1, D=128, dtype="bf16", window=(127, 0), topk=512,
+                cmp_ratio=4, ori_bs=128, cmp_bs=128, sinks=True, seed=4000, invalid_frac=0.0,
+                shared_indices=False, scale=None) -> dict:
+    """Inputs of sliding-window + sparse compressed attention over shared K/V
+    (the SparseAttnSharedkv README's third scenario, its shapes: TND q,
+    PA_ND caches through permuted block tables, int32 indices [T, H_kv, topk]).
+
+    Draw order from ``default_rng(seed)``: q [T, H, D]; per sequence the
+    original rows [S2_b, H_kv, D] then the compressed rows [S2_b / ratio,
+    H_kv, D] (standard normal, cast to ``dtype``); sinks [H]; the two block
+    permutations; the indices (uniform in [0, S3_b), drawn per token or once
+    per sequence when ``shared_indices``, as in the README example); then a
+    fraction ``invalid_frac`` of the indices replaced by out-of-range values
+    (-1 or S3_b + k)."""
+    rng = np.random.default_rng(seed)
+    lens_q = np.asarray(lens_q, np.int64)
+    S2 = np.asarray(seqused_kv, np.int64)
+    B = len(lens_q)
+    cu_q = np.zeros(B + 1, np.int32)
+    cu_q[1:] = np.cumsum(lens_q)
+    T = int(cu_q[-1])
+    q = _cast(rng.standard_normal((T, H, D), dtype=np.float32), dtype)
+    ori_rows, cmp_rows = [], []
+    for b in range(B):
+        ori_rows.append(_cast(rng.standard_normal((int(S2[b]), Hkv, D), dtype=np.float32), dtype))
+        cmp_rows.append(_cast(rng.standard_normal((int(S2[b]) // cmp_ratio, Hkv, D), dtype=np.float32), dtype))
+    sk = rng.standard_normal(H, dtype=np.float32) if sinks else None
+    poison = POISON_BF16 if dtype == "bf16" else np.float16(POISON_F32)
+    ori_kv, ori_table = _paged(rng, ori_rows, ori_bs, Hkv, D, dtype, poison)
+    cmp_kv, cmp_table = _paged(rng, cmp_rows, cmp_bs, Hkv, D, dtype, poison)
+    idx = np.zeros((T, Hkv, topk), np.int32)
+    for b in range(B):
+        S3 = int(S2[b]) // cmp_ratio
+        s, e = int(cu_q[b]), int(cu_q[b + 1])
+        if e == s or topk == 0:
+            continue
+        hi = max(S3, 1)
+        if shared_indices:
+            idx[s:e] = rng.integers(0, hi, (1, Hkv, topk))
+        else:
+            idx[s:e] = rng.integers(0, hi, (e - s, Hkv, topk))
+        if S3 == 0:
+            idx[s:e] = -1
+    if invalid_frac > 0 and topk > 0:
+        bad = rng.random(idx.shape) < invalid_frac
+        alt = rng.integers(0, 2, idx.shape)
+        seq_of = np.repeat(np.arange(B), lens_q)
+        s3 = (S2 // cmp_ratio)[seq_of][:, None, None]
+        idx = np.where(bad, np.where(alt == 0, -1, s3 + rng.integers(0, 5, idx.shape)), idx).astype(np.int32)
+    return dict(B=B, T=T, H=H, Hkv=Hkv, D=D, dtype=dtype, cu_q=cu_q, seqused_kv=S2.astype(np.int32),
+                q=q, ori_kv=ori_kv, ori_table=ori_table, cmp_kv=cmp_kv, cmp_table=cmp_table, indices=idx,
+                sinks=sk, window=tuple(window), topk=topk, cmp_ratio=cmp_ratio,
+                scale=(1.0 / math.sqrt(D)) if scale is None else scale,
+                max_seqlen_kv=int(S2.max()) if B else 0)
