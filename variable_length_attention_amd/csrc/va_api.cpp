@@ -591,10 +591,10 @@ va_status varlen_attn_sparse_sharedkv(const va_sparse_problem *p, const void *q,
     a.cmp_bs = p->cmp_block_size; a.cmp_stride = p->cmp_block_table_stride; a.cmp_ratio = p->cmp_ratio;
     a.left = p->window_left; a.right = p->window_right;
     a.scale_log2 = p->scale * va::kLog2e;
-    // tokens per workgroup: about 1536 workgroups (4 per CU of 2 waves each,
-    // 1.5 rounds), at least 1 and at most kSpTokMax tokens each
+    // tokens per workgroup: the fewest that keep the grid within whole rounds
+    // of 1024 workgroups (4 per CU of 2 waves each), 1 to kSpTokMax each
     const long long units = (long long)p->total_q * p->num_kv_heads;
-    a.tok_per_wg = (int)std::min<long long>(va::kSpTokMax, std::max<long long>(1, (units + 1535) / 1536));
+    a.tok_per_wg = (int)std::min<long long>(va::kSpTokMax, std::max<long long>(1, (units + 1023) / 1024));
     const hipError_t e = va::launch_sparse16(a, p->dtype == VA_F16, p->head_dim, (hipStream_t)stream);
     if (e != hipSuccess) return fail(VA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return VA_OK;

@@ -93,7 +93,7 @@ struct BwdArgs {
 // Sliding-window + sparse compressed attention over shared K/V (the
 // third scenario of the SparseAttnSharedkv README).
 constexpr int kSpTokMax = 16;    // tokens per workgroup, at most
-constexpr int kSpListMax = 1536; // window + selected keys per token, at most (LDS: 4 workgroups per CU)
+constexpr int kSpListMax = 1536; // window + selected keys per token, at most (a multiple of 128 and of the 64-key tile)
 struct SparseArgs {
     const void *q;                   // [T_q, H, D]
     const void *ori_kv;              // [ori_blocks, ori_bs, Hkv, D], K = V

@@ -119,8 +119,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int ROWB = D * 2;
     constexpr int TILEB = BN * ROWB;
     __shared__ __attribute__((aligned(16))) char s_tile[2 * TILEB];
-    __shared__ int s_list[kSpListMax];     // physical row of each key, -1: selects nothing
-    __shared__ __attribute__((aligned(16))) float s_bias[2][BN];
+    __shared__ __attribute__((aligned(16))) int s_list[kSpListMax];  // physical row per key, -1: none
 
     const int c = blockIdx.y;
     const int t0 = blockIdx.x * a.tok_per_wg;
@@ -170,19 +169,43 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int L = nwin + a.topk;                 // <= kSpListMax (checked on the host)
         const int ntiles = (L + BN - 1) / BN;
 
-        // physical rows of the key list
-        for (int kk = tid; kk < L; kk += 128) {
-            int row;
-            if (kk < nwin) {
-                const int pos = win_lo + kk;
-                row = a.ori_table[(size_t)b * a.ori_stride + pos / a.ori_bs] * a.ori_bs + pos % a.ori_bs;
-            } else {
+        // physical rows of the key list, in two rounds of independent loads
+        // (the indices, then the block-table entries they name): thread tid
+        // takes keys tid, tid + 128, ...
+        constexpr int KPT = kSpListMax / 128;
+        static_assert(kSpListMax % 128 == 0, "whole rounds of 128 keys");
+        int pos[KPT];   // position within its cache, -1: selects nothing
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            const int kk = tid + 128 * k;
+            pos[k] = -1;
+            if (kk < nwin) pos[k] = win_lo + kk;
+            else if (kk < L) {
                 const int idx = a.indices[((size_t)t * a.Hkv + c) * a.topk + (kk - nwin)];
-                row = (idx >= 0 && idx < S3)
-                          ? a.cmp_table[(size_t)b * a.cmp_stride + idx / a.cmp_bs] * a.cmp_bs + idx % a.cmp_bs
-                          : -1;
+                pos[k] = (idx >= 0 && idx < S3) ? idx : -1;
             }
-            s_list[kk] = row;
+        }
+        int blk[KPT];
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            const int kk = tid + 128 * k;
+            blk[k] = 0;
+            if (pos[k] >= 0)
+                blk[k] = kk < nwin ? a.ori_table[(size_t)b * a.ori_stride + pos[k] / a.ori_bs]
+                                   : a.cmp_table[(size_t)b * a.cmp_stride + pos[k] / a.cmp_bs];
+        }
+        // entries up to the end of the last tile (-1 past L); whether any
+        // key of the token selects nothing decides if its tiles are masked
+        bool none_here = false;
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            const int kk = tid + 128 * k;
+            if (kk < ntiles * BN) {
+                const int bs = kk < nwin ? a.ori_bs : a.cmp_bs;
+                const int row = pos[k] >= 0 ? blk[k] * bs + pos[k] % bs : -1;
+                s_list[kk] = row;
+                none_here |= row < 0;
+            }
         }
         // Q^T operand fragments: lane (head n, half h2) holds d = 16 ks + 8 h2 .. +8
         v8 qf[KS];
@@ -195,15 +218,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 qf[ks] = __builtin_bit_cast(v8, x);
             }
         }
-        __syncthreads();  // the list is complete
+        const bool masked = __syncthreads_or(none_here);  // the list is complete
 
-        // tile tau's rows into slot; the bias of each key goes with it
+        // tile tau's rows into slot
         auto issue = [&](int tau, int slot) {
 #pragma unroll
             for (int u = 0; u < LPW; ++u) {
                 const int r = (wave * LPW + u) * RPI + lane / NCH;
                 const int kk = tau * BN + r;
-                const int row = kk < L ? s_list[kk] : -1;
+                const int row = s_list[kk];
                 const char *base = (const char *)(kk < nwin ? a.ori_kv : a.cmp_kv);
                 const int chunk = (lane % NCH) ^ swz<D>(r);
                 // a key that selects nothing re-reads row 0 of the original
@@ -211,7 +234,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const size_t off = ((size_t)(row >= 0 ? row : 0) * a.Hkv + c) * ROWB + chunk * 16;
                 copy16_global((row >= 0 ? base : (const char *)a.ori_kv) + off,
                               lds_addr(s_tile + slot * TILEB + (wave * LPW + u) * 1024));
-                if (lane % NCH == 0) s_bias[slot][r] = row >= 0 ? 0.f : -INFINITY;
             }
         };
 
@@ -243,25 +265,39 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const f32x4 bias = *(const f32x4 *)&s_bias[slot][mb * 32 + e4 * 8 + h2 * 4];
+                for (int v = 0; v < 16; ++v) S[mb][v] *= a.scale_log2;
+            if (masked) {
+                // keys that select nothing (list entry -1) drop out
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float x = S[mb][e4 * 4 + e] * a.scale_log2 + bias[e];
-                        S[mb][e4 * 4 + e] = x;
-                        mx = fmaxf(mx, x);
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4) {
+                        const int4 row = *(const int4 *)&s_list[tau * BN + mb * 32 + e4 * 8 + h2 * 4];
+                        S[mb][e4 * 4 + 0] = row.x < 0 ? -INFINITY : S[mb][e4 * 4 + 0];
+                        S[mb][e4 * 4 + 1] = row.y < 0 ? -INFINITY : S[mb][e4 * 4 + 1];
+                        S[mb][e4 * 4 + 2] = row.z < 0 ? -INFINITY : S[mb][e4 * 4 + 2];
+                        S[mb][e4 * 4 + 3] = row.w < 0 ? -INFINITY : S[mb][e4 * 4 + 3];
                     }
-                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[mb][v]);
+            // the running max moves only when a tile raises it by more than
+            // 2^8 (log2 units) for some head: until then the probabilities
+            // stay below 2^8 and the O / l rescale is skipped
             mx = halves_max(mx);
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // m_run = -inf -> 0
-            l_run *= alpha;
+            if (__ballot(mx > m_run + 8.f) != 0ull) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
 #pragma unroll
-            for (int md = 0; md < MD; ++md)
+                for (int md = 0; md < MD; ++md)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
-            m_run = m_new;
+                    for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;
             float rs = 0.f;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
