@@ -15,8 +15,9 @@ shape, the sliding-window + sinks MQA shape (bound by HBM) and the paged
 decode shape (bound by HBM), each with its own step time and roofline;
 (key "backward") one call of the backward on the main workload; and (key
 "merge") the log-sum-exp merge of 8 float32 partials of the full-attention
-shard (a ring of 8), bound by HBM; and (key "sparse") sliding-window +
-sparse compressed attention over shared K/V.
+shard (a ring of 8), bound by HBM; and (keys "sparse", "sparse_d512")
+sliding-window + sparse compressed attention over shared K/V at head sizes
+128 and 512.
 
 The roofline figure is for the dominant kernel: its average duration is the
 step time minus the pre-pass time, both measured here with HIP events on
@@ -247,6 +248,8 @@ def time_merge(steps, warmup, torch):
 
 SPARSE_SHAPE = dict(lens_q=[1024] * 4, seqused_kv=[8192] * 4, H=64, Hkv=1, D=128, window=(127, 0), topk=512,
                     cmp_ratio=4, ori_bs=128, cmp_bs=128, seed=4600)
+# the same at the Ascend operator's own head size
+SPARSE_SHAPE_D512 = dict(SPARSE_SHAPE, D=512, seed=4601)
 
 
 def sparse_work(sc):
@@ -281,12 +284,12 @@ def sparse_work(sc):
     return fl, by
 
 
-def time_sparse(steps, warmup, torch):
+def time_sparse(steps, warmup, torch, shape=SPARSE_SHAPE):
     """Sliding-window + sparse compressed attention over shared K/V on
-    SPARSE_SHAPE; returns (ms per call, FLOPs, algorithmic bytes)."""
+    shape; returns (ms per call, FLOPs, algorithmic bytes)."""
     import variable_length_attention_amd as va
     import workloads as W
-    sc = W.sparse_case(**SPARSE_SHAPE)
+    sc = W.sparse_case(**shape)
     args = [_dev(sc[k], torch) for k in ("q", "ori_kv", "ori_table", "seqused_kv", "cmp_kv", "cmp_table",
                                           "indices", "cu_q")]
     sinks = _dev(sc["sinks"], torch)
@@ -525,19 +528,22 @@ def main():
                                       "frac": gbs / PEAK_HBM_GBS, "traffic": None}}
         log(f"merge: {ms_m:.4f} ms/call, {gbs:.0f} GB/s")
     if not args.no_sparse:
-        log("sparse shared-KV attention (4 x 1024 tokens over 8192 keys, 64/1 heads, window 128 + 512 selected)")
-        ms_s, fl_s, by_s = time_sparse(args.steps, args.warmup, torch)
-        tf_s, gb_s = fl_s / (ms_s * 1e-3) / 1e12, by_s / (ms_s * 1e-3) / 1e9
-        hbm = (fl_s / by_s) < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-        line["sparse"] = {
-            "workload": "sliding window (127, 0) + 512 selected of 4x compressed keys, shared K/V, "
-                        "4 x 1024 tokens over 8192 keys, 64 heads / 1 kv head, d128, bf16",
-            "ms_per_step": ms_s, "tflops": tf_s, "gbs": gb_s, "flop": fl_s, "bytes": by_s,
-            "roofline": ({"bound": "hbm", "achieved": gb_s, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                          "frac": gb_s / PEAK_HBM_GBS, "traffic": None} if hbm else
-                         {"bound": "mfma", "achieved": tf_s, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                          "frac": tf_s / PEAK_BF16_TFLOPS, "traffic": None})}
-        log(f"sparse: {ms_s:.4f} ms/call, {tf_s:.1f} TFLOP/s, {gb_s:.0f} GB/s (algorithmic)")
+        for key, shape in (("sparse", SPARSE_SHAPE), ("sparse_d512", SPARSE_SHAPE_D512)):
+            D = shape["D"]
+            log(f"sparse shared-KV attention (4 x 1024 tokens over 8192 keys, 64/1 heads, d{D}, "
+                "window 128 + 512 selected)")
+            ms_s, fl_s, by_s = time_sparse(args.steps, args.warmup, torch, shape)
+            tf_s, gb_s = fl_s / (ms_s * 1e-3) / 1e12, by_s / (ms_s * 1e-3) / 1e9
+            hbm = (fl_s / by_s) < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+            line[key] = {
+                "workload": "sliding window (127, 0) + 512 selected of 4x compressed keys, shared K/V, "
+                            f"4 x 1024 tokens over 8192 keys, 64 heads / 1 kv head, d{D}, bf16",
+                "ms_per_step": ms_s, "tflops": tf_s, "gbs": gb_s, "flop": fl_s, "bytes": by_s,
+                "roofline": ({"bound": "hbm", "achieved": gb_s, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": gb_s / PEAK_HBM_GBS, "traffic": None} if hbm else
+                             {"bound": "mfma", "achieved": tf_s, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                              "frac": tf_s / PEAK_BF16_TFLOPS, "traffic": None})}
+            log(f"{key}: {ms_s:.4f} ms/call, {tf_s:.1f} TFLOP/s, {gb_s:.0f} GB/s (algorithmic)")
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a sample of rows")
         line["cpu_baseline"] = cpu_baseline(main_case)

@@ -256,7 +256,8 @@ va_status varlen_attn_merge(int32_t n_parts, int32_t rows, int32_t num_heads, in
  *   cmp_sparse_indices int32 [total_q, H_kv, topk] (NULL iff topk = 0)
  *   cu_seqlens_q      int32 [batch + 1]; sinks float32 [H] or NULL;
  *   lse               float32 [total_q, H] or NULL
- * Limits: D in {64, 128}; H / H_kv <= 64; bounded window (both sides >= 0)
+ * Limits: D in {64, 128, 512} (512 is the README's head size); H / H_kv <= 64;
+ * bounded window (both sides >= 0)
  * with window_left + window_right + 1 + topk <= 1536; cmp_ratio >= 1.  Same
  * ownership, stream, alignment and aliasing rules as the forward; nothing
  * is allocated and no workspace is needed. */

@@ -242,6 +242,7 @@ def test_sparse_rejects_before_launching():
     assert _sparse(dtype=0) == 3                      # float32 not taken
     assert _sparse(num_heads=128) == 4                # 128 query heads per kv head
     assert _sparse(head_dim=96) == 4
+    assert _sparse(head_dim=256) == 4
     assert _sparse(window_left=-1) == 4               # unbounded window
     assert _sparse(topk=1500) == 4                    # window + topk beyond 1536 keys
     assert _sparse(cmp_ratio=0) == 2

@@ -67,6 +67,13 @@ CASES = {
                                  topk=64, cmp_ratio=3, invalid_frac=0.05, ori_bs=64, cmp_bs=64),
     "window_only_short_history": dict(lens_q=[16, 40], seqused_kv=[10, 40], H=64, Hkv=1, D=128,
                                       window=(127, 0), topk=0, cmp_ratio=4),
+    # the README's head size: 64 heads over one kv head of 512, window (127, 0),
+    # 512 indices per token, 128-token blocks, sinks
+    "readme_config_d512": dict(lens_q=[64, 37], seqused_kv=[3000, 2100], H=64, Hkv=1, D=512,
+                               window=(127, 0), topk=512, cmp_ratio=4, ori_bs=128, cmp_bs=128),
+    "d512_f16_ragged_invalid_gqa_no_sinks": dict(lens_q=[5, 0, 40, 1], seqused_kv=[300, 7, 90, 1], H=24, Hkv=2,
+                                                 D=512, dtype="f16", window=(20, 3), topk=50, cmp_ratio=2,
+                                                 invalid_frac=0.2, sinks=False, ori_bs=32, cmp_bs=16),
 }
 
 
@@ -79,16 +86,17 @@ def test_sparse_matches_oracle(name):
     _compare(sc, to_f64(out), to_f64(lse), ref_o, ref_l, name)
 
 
-# benchmark workload: 4 sequences of 1024 query tokens over 8192 original
-# keys each, 64 heads / 1 kv head, d128, window (127, 0), 512 indices per
-# token into a 4x compressed cache, 128-token blocks, sinks
+# benchmark workloads: 4 sequences of 1024 query tokens over 8192 original
+# keys each, 64 heads / 1 kv head, d128 and d512, window (127, 0), 512
+# indices per token into a 4x compressed cache, 128-token blocks, sinks
 BENCH = dict(lens_q=[1024] * 4, seqused_kv=[8192] * 4, H=64, Hkv=1, D=128, window=(127, 0), topk=512,
              cmp_ratio=4, ori_bs=128, cmp_bs=128, seed=4600)
 
 
-def test_sparse_benchmark_size_sampled():
-    sc = W.sparse_case(**BENCH)
-    announce("sparse benchmark size: running")
+@pytest.mark.parametrize("D", [128, 512])
+def test_sparse_benchmark_size_sampled(D):
+    sc = W.sparse_case(**dict(BENCH, D=D, seed=4600 if D == 128 else 4601))
+    announce(f"sparse benchmark size d{D}: running")
     out, lse = _run(sc)
     rng = np.random.default_rng(3)
     toks = np.unique(np.concatenate([rng.integers(0, sc["T"], 96), [0, 1023, 1024, sc["T"] - 1]]))

@@ -27,9 +27,9 @@ def _forward_case(sc, window, causal):
                 num_blocks=sc["ori_kv"].shape[0], sinks=sc["sinks"])
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_no_selection_is_window_attention(dtype):
-    sc = W.sparse_case([5, 0, 9, 1], [40, 3, 200, 130], H=8, Hkv=2, D=64, dtype=dtype, window=(17, 3),
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f16", 64), ("bf16", 512)])
+def test_no_selection_is_window_attention(dtype, D):
+    sc = W.sparse_case([5, 0, 9, 1], [40, 3, 200, 130], H=8, Hkv=2, D=D, dtype=dtype, window=(17, 3),
                        topk=0, ori_bs=32, cmp_bs=16, seed=4100)
     got_o, got_l = oracle.sparse_sharedkv(sc)
     ref_o, ref_l = oracle.forward(_forward_case(sc, (17, 3), causal=False))

@@ -23,11 +23,13 @@ SOURCES = ["va_api.cpp", "va_plan.hip", "va_prefill_bf16.hip", "va_prefill_f32.h
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-command-line-argument"]
-# Per-file device options.  The backward's dK/dV kernel keeps its
-# accumulators in AGPRs through inline assembly and needs every other
-# matrix instruction in the VGPR form (the backend otherwise picks the AGPR
-# form for a whole kernel that may use more than 256 registers).
-EXTRA = {"va_backward.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=1"]}
+# Per-file device options.  The backward's dK/dV kernel and the d512 sparse
+# shared-KV kernel keep their accumulators in AGPRs through inline assembly
+# and need every other matrix instruction in the VGPR form (the backend
+# otherwise picks the AGPR form for a whole kernel that may use more than
+# 256 registers).
+EXTRA = {"va_backward.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=1"],
+         "va_sparse.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

@@ -536,8 +536,8 @@ va_status varlen_attn_sparse_sharedkv(const va_sparse_problem *p, const void *q,
                     p->num_kv_heads);
     if (p->num_heads / p->num_kv_heads > 64)
         return fail(VA_ERR_UNSUPPORTED, "more than 64 query heads per kv head");
-    if (p->head_dim != 64 && p->head_dim != 128)
-        return fail(VA_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", p->head_dim);
+    if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 512)
+        return fail(VA_ERR_UNSUPPORTED, "head_dim %d is not 64, 128 or 512", p->head_dim);
     if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return fail(VA_ERR_UNSUPPORTED, "scale must be finite and > 0");
     if (p->window_left < 0 || p->window_right < 0 || p->topk < 0 ||
         (long long)p->window_left + p->window_right + 1 + p->topk > va::kSpListMax)

@@ -54,6 +54,11 @@ struct Elt<__bf16> {
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
+    // acc += a b with acc held in AGPRs (see mfma_agpr_drain)
+    static __device__ __forceinline__ void mfma_agpr(f32x16 &acc, v8 a, v8 b)
+    {
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    }
 };
 template <>
 struct Elt<_Float16> {
@@ -68,16 +73,39 @@ struct Elt<_Float16> {
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
+    static __device__ __forceinline__ void mfma_agpr(f32x16 &acc, v8 a, v8 b)
+    {
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    }
 };
+
+// Wait states between the last matrix instruction into an AGPR accumulator
+// and any other read of it (16-pass instructions need 18); the leading
+// s_nop of mfma_agpr covers a VALU write of its A / B operand just before.
+// The matrix instructions into AGPRs are written in assembly because the
+// compiler selects one register form for all of a kernel's matrix
+// instructions (this file is built with the VGPR form for the others).
+__device__ __forceinline__ void mfma_agpr_drain(f32x16 &acc)
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc));
+}
+// Places acc in AGPRs here, so that values written by VALU code (the zero
+// start, a rescale) do not carry the accumulators into VGPRs across the loop.
+__device__ __forceinline__ void in_agpr(f32x16 &acc)
+{
+    asm volatile("" : "+a"(acc));
+}
 
 // Physical 16-byte chunk of logical chunk c in LDS row r is c ^ swz(r): the
 // rows of a row-wise operand read and the 4 rows x 4 chunks of a
 // transposing read land on distinct chunks (D = 128; D = 64 per pair of
-// rows sharing a 256-byte bank line).
+// rows sharing a 256-byte bank line).  Rows of D = 512 are 4 bank lines:
+// a chunk's bank depends on its index mod 16 only, which the D = 128
+// pattern permutes the same way.
 template <int D>
 __device__ __forceinline__ int swz(int r)
 {
-    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    return D >= 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 // 16 bytes per lane, global -> LDS (lane i writes LDS bytes [lds + 16 i, +16));
@@ -104,13 +132,19 @@ __device__ __forceinline__ float halves_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// D = 512 (the README's head size): 32-key tiles (64 KB of double-buffered
+// LDS), O accumulators (256 registers) in AGPRs, one wave per SIMD.
 template <typename T, int D>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void k5_sparse16(SparseArgs a)
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(D == 512 ? 1 : 2, D == 512 ? 1 : 2)))
+void k5_sparse16(SparseArgs a)
 {
     using E = Elt<T>;
     typedef typename E::v8 v8;
     typedef typename E::v4 v4;
-    constexpr int BN = 64;             // keys per tile
+    constexpr bool BIG = D == 512;
+    constexpr int BN = BIG ? 32 : 64;  // keys per tile
+    constexpr int NMB = BN / 32;       // 32-key blocks of a tile (MFMA M side)
+    constexpr int NT4 = BN / 16;       // 16-key P V steps
     constexpr int NCH = D / 8;         // 16-byte chunks per row
     constexpr int KS = D / 16;         // QK^T k-steps
     constexpr int MD = D / 32;         // 32-wide blocks of the head dimension
@@ -144,15 +178,19 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 
     // LDS offsets: row-wise K operand read of key row 32 mb + n, chunk
-    // 2 ks + h2; transposing V^T read of rows 16 t4 + 4 h2 + q4 (+8)
+    // 2 ks + h2; transposing V^T read of rows 16 t4 + 4 h2 + q4 (+8), chunk
+    // 4 md + 2 ((lane & 31) >> 4) + ((l16 & 3) >> 1).  The swizzle changes
+    // the low 4 bits of a chunk index only, so chunks 16 and above are a
+    // constant byte offset from a lane's address of the low ones (8 + 8
+    // address registers at d512).
     auto koff = [&](int mb, int ks) -> uint32_t {
         const int r = mb * 32 + n;
-        return r * ROWB + (((ks * 2 + h2) ^ swz<D>(r)) << 4);
+        return r * ROWB + ((((ks & 7) * 2 + h2) ^ swz<D>(r)) << 4) + (ks >> 3) * 256;
     };
     auto toff = [&](int md, int half) -> uint32_t {
         const int r = h2 * 4 + q4 + half * 8;
-        const int col = md * 32 + ((lane & 31) >> 4) * 16 + (l16 & 3) * 4;
-        return r * ROWB + (((col >> 3) ^ swz<D>(r)) << 4) + (col & 7) * 2;
+        const int ch = (md & 3) * 4 + ((lane & 31) >> 4) * 2 + ((l16 & 3) >> 1);
+        return r * ROWB + ((ch ^ swz<D>(r)) << 4) + (l16 & 1) * 8 + (md >> 2) * 256;
     };
     const float sink2 = (a.sinks && head_ok) ? a.sinks[head] * kLog2e : -INFINITY;
 
@@ -239,9 +277,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
         f32x16 o[MD];
 #pragma unroll
-        for (int md = 0; md < MD; ++md)
+        for (int md = 0; md < MD; ++md) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) o[md][v] = 0.f;
+            if constexpr (BIG) in_agpr(o[md]);
+        }
         float m_run = sink2, l_run = (sink2 != -INFINITY && h2 == 0) ? 1.f : 0.f;
 
         if (ntiles > 0) issue(0, 0);
@@ -252,24 +292,28 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (tau + 1 < ntiles) issue(tau + 1, slot ^ 1);
             const char *kt = s_tile + slot * TILEB;
             // S^T = K Q^T: lane value v of block mb is key 32 mb + 8 (v/4) + 4 h2 + v%4
-            f32x16 S[2];
+            f32x16 S[NMB];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
+            for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) S[mb][v] = 0.f;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
+                for (int ks = 0; ks < KS; ++ks) {
                     S[mb] = E::mfma(*(const v8 *)(kt + koff(mb, ks)), qf[ks], S[mb]);
+                    // d512: at most 8 K operand reads ahead (Q^T holds 128 registers)
+                    if constexpr (BIG)
+                        if (ks % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+                }
             }
             float mx = -INFINITY;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) S[mb][v] *= a.scale_log2;
             if (masked) {
                 // keys that select nothing (list entry -1) drop out
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
+                for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
                     for (int e4 = 0; e4 < 4; ++e4) {
                         const int4 row = *(const int4 *)&s_list[tau * BN + mb * 32 + e4 * 8 + h2 * 4];
@@ -280,7 +324,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     }
             }
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[mb][v]);
             // the running max moves only when a tile raises it by more than
@@ -292,15 +336,18 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
                 l_run *= alpha;
 #pragma unroll
-                for (int md = 0; md < MD; ++md)
+                for (int md = 0; md < MD; ++md) {
+                    if constexpr (BIG) mfma_agpr_drain(o[md]);
 #pragma unroll
                     for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
+                    if constexpr (BIG) in_agpr(o[md]);
+                }
                 m_run = m_new;
             }
             const float m_use = m_run == -INFINITY ? 0.f : m_run;
             float rs = 0.f;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const float pr = __builtin_amdgcn_exp2f(S[mb][v] - m_use);
@@ -310,7 +357,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             l_run += rs;
             // O^T += V^T P^T, 16 keys per step
 #pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4) {
+            for (int t4 = 0; t4 < NT4; ++t4) {
                 f32x8 pv;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) pv[e] = S[t4 >> 1][(t4 & 1) * 8 + e];
@@ -319,7 +366,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 for (int md = 0; md < MD; ++md) {
                     const v4 va = E::read_tr(kt + toff(md, 0) + t4 * 16 * ROWB);
                     const v4 vb = E::read_tr(kt + toff(md, 1) + t4 * 16 * ROWB);
-                    o[md] = E::mfma(__builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[md]);
+                    const v8 vf = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+                    if constexpr (BIG) E::mfma_agpr(o[md], vf, pb);
+                    else o[md] = E::mfma(vf, pb, o[md]);
                 }
             }
             wait_vmem();
@@ -327,6 +376,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
 
         // epilogue: lane (head n, half h2) holds O^T[32 md + 8 i + 4 h2 + j]
+        if constexpr (BIG) {
+#pragma unroll
+            for (int md = 0; md < MD; ++md) mfma_agpr_drain(o[md]);
+        }
         const float l = halves_sum(l_run);
         const float inv = l > 0.f ? 1.f / l : 0.f;
         if (head_ok) {
@@ -352,13 +405,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 hipError_t launch_sparse16(const SparseArgs &a, bool f16, int head_dim, hipStream_t s)
 {
     const dim3 g((a.T + a.tok_per_wg - 1) / a.tok_per_wg, a.Hkv), blk(128);
-    if (f16) {
-        if (head_dim == 128) hipLaunchKernelGGL((k5_sparse16<_Float16, 128>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((k5_sparse16<_Float16, 64>), g, blk, 0, s, a);
-    } else {
-        if (head_dim == 128) hipLaunchKernelGGL((k5_sparse16<__bf16, 128>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((k5_sparse16<__bf16, 64>), g, blk, 0, s, a);
-    }
+#define VA_DIMS(TT)                                                                      \
+    do {                                                                                 \
+        if (head_dim == 512) hipLaunchKernelGGL((k5_sparse16<TT, 512>), g, blk, 0, s, a); \
+        else if (head_dim == 128) hipLaunchKernelGGL((k5_sparse16<TT, 128>), g, blk, 0, s, a); \
+        else hipLaunchKernelGGL((k5_sparse16<TT, 64>), g, blk, 0, s, a);                 \
+    } while (0)
+    if (f16) VA_DIMS(_Float16);
+    else VA_DIMS(__bf16);
+#undef VA_DIMS
     return hipGetLastError();
 }
 
