@@ -209,6 +209,15 @@ __device__ __forceinline__ void map_block(int bid, int nheads, int &item, int &h
         head = bid % nheads;
     }
 }
+
+// Bijection of [0, n) that gives each XCD a contiguous range: workgroup id
+// bid runs on XCD bid % 8, and XCD x takes ids x, x + 8, ... in turn, so
+// ranges of about n / 8 consecutive items each share one L2.
+__device__ __forceinline__ int xcd_contiguous(int bid, int n)
+{
+    const int q = n >> 3, r = n & 7, x = bid & 7, j = bid >> 3;
+    return x < r ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
 #endif
 
 }  // namespace va

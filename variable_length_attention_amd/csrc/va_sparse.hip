@@ -155,8 +155,13 @@ void k5_sparse16(SparseArgs a)
     __shared__ __attribute__((aligned(16))) char s_tile[2 * TILEB];
     __shared__ __attribute__((aligned(16))) int s_list[kSpListMax];  // physical row per key, -1: none
 
-    const int c = blockIdx.y;
-    const int t0 = blockIdx.x * a.tok_per_wg;
+    // (kv head, token chunk) of this workgroup: each XCD walks a contiguous
+    // stretch of tokens, whose windows and selected compressed rows (one
+    // sequence's cache) stay in its L2
+    const int nchunks = gridDim.x;
+    const int wg = xcd_contiguous(blockIdx.x + blockIdx.y * nchunks, nchunks * gridDim.y);
+    const int c = wg / nchunks;
+    const int t0 = (wg - c * nchunks) * a.tok_per_wg;
     const int t_end = min(a.T, t0 + a.tok_per_wg);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -260,11 +265,15 @@ void k5_sparse16(SparseArgs a)
 
         // tile tau's rows into slot
         auto issue = [&](int tau, int slot) {
+            // all list entries first: one LDS round trip, not one per copy
+            int rows[LPW];
+#pragma unroll
+            for (int u = 0; u < LPW; ++u) rows[u] = s_list[tau * BN + (wave * LPW + u) * RPI + lane / NCH];
 #pragma unroll
             for (int u = 0; u < LPW; ++u) {
                 const int r = (wave * LPW + u) * RPI + lane / NCH;
                 const int kk = tau * BN + r;
-                const int row = s_list[kk];
+                const int row = rows[u];
                 const char *base = (const char *)(kk < nwin ? a.ori_kv : a.cmp_kv);
                 const int chunk = (lane % NCH) ^ swz<D>(r);
                 // a key that selects nothing re-reads row 0 of the original
