@@ -49,7 +49,9 @@ KERNEL_SOURCES = {
     "prefill_bf16": ["va_prefill_bf16.hip", "va_internal.h"],
     "decode_bf16": ["va_decode.hip", "va_internal.h"],
     "f32": ["va_prefill_f32.hip", "va_internal.h"],
+    "window_bf16": ["va_window.hip", "va_internal.h"],
 }
+PATH_NAMES = ["prefill_bf16", "decode_bf16", "f32", "window_bf16"]  # index = varlen_attn_path
 
 
 def log(msg):
@@ -456,7 +458,7 @@ def main():
         r = {"workload": spec.name, "ms_per_step": ms_step, "ms_prepass": ms_plan,
              "tflops": fl / (ms_step * 1e-3) / 1e12, "gbs": by / (ms_step * 1e-3) / 1e9,
              "tokens_per_s": case["T_q"] / (ms_step * 1e-3), "flop": fl, "bytes": by,
-             "kernel_path": ["prefill_bf16", "decode_bf16", "f32"][path]}
+             "kernel_path": PATH_NAMES[path]}
         traffic = measured_traffic(r["kernel_path"], spec.name)
         if hbm_bound:
             ach = by / (ms_kernel * 1e-3) / 1e9

@@ -156,6 +156,27 @@ def test_workspace_size_and_kernel_path():
     # float32 always takes the float32 kernels
     p = _prob(dtype=0, head_dim=64, num_heads=4, num_kv_heads=2)
     assert lib.varlen_attn_path(ctypes.byref(p), 0) == 2
+    # 64 query heads on one kv head, window (127, 0): the sliding-window kernel
+    c4 = dict(num_heads=64, num_kv_heads=1, total_q=25750, total_k=25750, batch=8, max_seqlen_q=8192,
+              max_seqlen_k=8192, causal=0, window_left=127, window_right=0)
+    p = _prob(**c4)
+    assert lib.varlen_attn_path(ctypes.byref(p), 0) == 3
+    assert lib.varlen_attn_workspace_size(ctypes.byref(p), 0) > 0
+    assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, dtype=2))), 0) == 3       # f16
+    assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, num_heads=32))), 0) == 3  # 32 per kv head
+    assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, causal=1, window_right=-1))), 0) == 3
+    assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, head_dim=64, window_left=280))), 0) == 3
+    # not taken: 16 heads per kv head, unbounded sides, no room for 4 rows, paged
+    assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, num_heads=16))), 0) == 0
+    assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, window_left=-1))), 0) == 0
+    assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, window_right=-1))), 0) == 0
+    assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, window_left=149))), 0) == 0
+    assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, num_blocks=400, block_size=64,
+                                                             block_table_stride=128))), 1) == 0
+    assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, dtype=0, head_dim=64))), 0) == 2
+    p = _prob(**c4)
+    p.alibi_slopes = 0x10000000                                                          # ALiBi: tile kernel
+    assert lib.varlen_attn_path(ctypes.byref(p), 0) == 0
     # invalid -> 0 bytes / -1
     p = _prob(head_dim=80)
     assert lib.varlen_attn_workspace_size(ctypes.byref(p), 0) == 0

@@ -273,9 +273,10 @@ def test_stress_value_ranges_of_the_ascend_example():
 
 
 # ------------------------------------------------------------------ work partition
-def _plan_cpu(case, mode, bm=128, bn=64):
+def _plan_cpu(case, mode, bm=128, bn=64, sort=True):
     """Independent recomputation of the pre-pass list (deterministic order:
-    cost descending, then item index)."""
+    cost descending, then item index; index order for the sliding-window
+    kernel's items)."""
     INF = 1 << 30
     left = case["window_left"] if case["window_left"] >= 0 else INF
     right = 0 if case["causal"] else (case["window_right"] if case["window_right"] >= 0 else INF)
@@ -318,8 +319,24 @@ def _plan_cpu(case, mode, bm=128, bn=64):
                 k_hi = min(hi, k_lo + split)
                 items.append(((k_hi - k_lo + 255) // 256, (b, idx, k_lo, k_hi)))
                 idx += 1
-    order = sorted(range(len(items)), key=lambda i: (-min(items[i][0], 4095), i))
+    order = sorted(range(len(items)), key=lambda i: (-min(items[i][0], 4095), i) if sort else i)
     return np.asarray([items[i][1] for i in order], np.int32).reshape(-1, 4)
+
+
+def _window_rows(case):
+    """Query rows per item of the sliding-window kernel (0: not taken): 16-bit
+    contiguous K/V, 32..64 heads per kv head, both window sides bounded
+    (causal bounds the right), room for 4 rows in the 152 (d128) / 304 (d64)
+    LDS rows; about 2048 items per kv head, at most 32 rows."""
+    g = case["H"] // case["Hkv"]
+    right = 0 if case["causal"] else case["window_right"]
+    if case["dtype"] == "f32" or case.get("paged") or not 32 <= g <= 64 or case["window_left"] < 0 or right < 0:
+        return 0
+    room = (152 if case["D"] == 128 else 304) - case["window_left"] - right
+    if room < 4:
+        return 0
+    want = (max(1, case["T_q"]) * case["Hkv"] + 2047) // 2048
+    return max(4, min(room, want, 32))
 
 
 def _lengths_only_case(B, lo, hi, seed, H=8, Hkv=2, D=128, causal=True, decode_k=None):
@@ -377,7 +394,8 @@ def test_work_partition_bit_exact(which):
                           window=(case["window_left"], case["window_right"]), paged=paged,
                           num_blocks=case.get("num_blocks", 0), block_size=case.get("block_size", 0),
                           block_table_stride=case["block_table"].shape[1] if paged else 0)
-    assert path == (1 if mode == "decode" else (2 if case["dtype"] == "f32" else 0))
-    bm, bn = (64, 32) if case["dtype"] == "f32" else (128, 64)
-    ref = _plan_cpu(case, mode, bm, bn)
+    rows = _window_rows(case)
+    assert path == (1 if mode == "decode" else (2 if case["dtype"] == "f32" else (3 if rows else 0)))
+    bm, bn = (64, 32) if case["dtype"] == "f32" else ((rows, 64) if rows else (128, 64))
+    ref = _plan_cpu(case, mode, bm, bn, sort=not rows)
     np.testing.assert_array_equal(items.cpu().numpy(), ref)

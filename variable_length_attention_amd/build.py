@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libvarlen_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["va_api.cpp", "va_plan.hip", "va_prefill_bf16.hip", "va_prefill_f32.hip", "va_decode.hip",
-           "va_check.hip", "va_backward.hip", "va_merge.hip", "va_sparse.hip"]
+           "va_check.hip", "va_backward.hip", "va_merge.hip", "va_sparse.hip", "va_window.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-command-line-argument"]

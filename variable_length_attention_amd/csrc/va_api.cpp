@@ -50,7 +50,7 @@ bool device_check_enabled()
     return e && e[0] == '1';
 }
 
-enum Path { kPathPrefill = 0, kPathDecode = 1, kPathF32 = 2 };
+enum Path { kPathPrefill = 0, kPathDecode = 1, kPathF32 = 2, kPathWindow = 3 };
 
 struct Layout {
     int path = -1;
@@ -113,15 +113,38 @@ va_status check_problem(const va_problem *p, int paged)
     return VA_OK;
 }
 
+// Query rows per work item of the sliding-window kernel, or 0 when it does
+// not apply: 16-bit contiguous K/V, no ALiBi, 32..64 query heads per kv
+// head, a window bounded on both sides (causal bounds the right side) that
+// leaves room for at least 4 rows in the LDS window.  About 2048 items per
+// kv head fill the chip several times over; more rows per item share more
+// of the window.
+int window_rows(const va_problem *p, int paged)
+{
+    const int g = p->num_heads / p->num_kv_heads;
+    const int right = p->causal ? 0 : p->window_right;
+    if (p->dtype == VA_F32 || paged || alibi_of(p) || g < 32 || g > 64 || p->window_left < 0 || right < 0)
+        return 0;
+    const long long room = (long long)va::win_cap(p->head_dim) - p->window_left - right;
+    if (room < 4) return 0;
+    const long long want = ((long long)p->total_q * p->num_kv_heads + 2047) / 2048;
+    return (int)std::max<long long>(4, std::min<long long>({room, want, 32}));
+}
+
 va_status make_layout(const va_problem *p, int paged, Layout &L)
 {
     const int g = p->num_heads / p->num_kv_heads;
+    const int wrows = window_rows(p, paged);
     if (p->dtype == VA_F32) {
         L.path = kPathF32;
         L.bm = va::kBMf32;
         L.bn = va::kBNf32;
     } else if ((long long)g * p->max_seqlen_q <= va::kDecRows) {
         L.path = kPathDecode;
+    } else if (wrows > 0) {
+        L.path = kPathWindow;
+        L.bm = wrows;
+        L.bn = va::kBN;
     } else {
         L.path = kPathPrefill;
         L.bm = va::kBM;
@@ -130,6 +153,9 @@ va_status make_layout(const va_problem *p, int paged, Layout &L)
     long long n_max;
     if (L.path == kPathDecode) {
         n_max = va::kDecTargetUnits / p->num_kv_heads + (long long)p->batch + 1;
+        L.grid = n_max * p->num_kv_heads;
+    } else if (L.path == kPathWindow) {
+        n_max = ((long long)p->total_q + (long long)p->batch * (L.bm - 1)) / L.bm;
         L.grid = n_max * p->num_kv_heads;
     } else {
         n_max = ((long long)p->total_q + (long long)p->batch * (L.bm - 1)) / L.bm;
@@ -249,6 +275,7 @@ va::AttnArgs make_args(const Call &c)
     else a.right = p->window_right >= 0 ? p->window_right : va::kInfOff;
     a.scale = p->scale;
     a.scale_log2 = p->scale * va::kLog2e;
+    a.item_rows = 0;
     return a;
 }
 
@@ -261,7 +288,7 @@ va::PlanArgs make_plan(const Call &c, const Layout &L, const va::AttnArgs &a)
     pa.lens_k_is_prefix = c.paged ? 0 : 1;
     pa.B = a.B; pa.Hkv = a.Hkv;
     pa.left = a.left; pa.right = a.right;
-    pa.mode = L.path == kPathDecode ? va::kPlanDecode : va::kPlanPrefill;
+    pa.mode = L.path == kPathDecode ? va::kPlanDecode : L.path == kPathWindow ? va::kPlanWindow : va::kPlanPrefill;
     pa.bm = L.bm; pa.bn = L.bn;
     pa.n_max = L.n_max;
     pa.count = (int32_t *)(ws + L.off_count);
@@ -315,12 +342,14 @@ va_status run(const Call &c, hipStream_t s)
     Layout L;
     if ((st = make_layout(c.p, c.paged, L))) return st;
     if ((st = check_pointers(c, L))) return st;
-    const va::AttnArgs a = make_args(c);
+    va::AttnArgs a = make_args(c);
+    a.item_rows = L.path == kPathWindow ? L.bm : 0;
     const va::PlanArgs pa = make_plan(c, L, a);
     if (device_check_enabled() && (st = device_check(c, L, s))) return st;
     if (log_enabled())
         fprintf(stderr, "[varlen_attn] path=%s D=%d paged=%d B=%d H=%d Hkv=%d total_q=%d grid=%lld ws=%zu\n",
-                L.path == kPathPrefill ? "prefill16" : L.path == kPathDecode ? "decode16" : "f32",
+                L.path == kPathPrefill ? "prefill16" : L.path == kPathDecode ? "decode16"
+                                                   : L.path == kPathWindow ? "window16" : "f32",
                 c.p->head_dim, c.paged, a.B, a.H, a.Hkv, c.p->total_q, L.grid, L.total);
     hipError_t e = va::launch_plan(pa, s);
     if (e == hipSuccess) {
@@ -331,6 +360,9 @@ va_status run(const Call &c, hipStream_t s)
             e = va::launch_prefill16(a, c.p->dtype == VA_F16, a.alibi != nullptr, c.p->head_dim, mode, pa.items,
                                      pa.seqinfo, pa.count, (int)L.grid, s);
         }
+        else if (L.path == kPathWindow)
+            e = va::launch_window16(a, c.p->dtype == VA_F16, c.p->head_dim, pa.items, pa.seqinfo, pa.count,
+                                    (int)L.grid, s);
         else if (L.path == kPathF32)
             e = va::launch_prefill_f32(a, c.p->head_dim, c.paged, pa.items, pa.seqinfo, pa.count, (int)L.grid, s);
         else {

@@ -47,13 +47,21 @@ struct AttnArgs {
     int32_t bs_shift;            // log2(block_size) when a power of two, else -1
     int32_t left, right;         // visible keys of query position p: [p-left, p+right]
     float scale, scale_log2;     // scale and scale * log2(e)
+    int32_t item_rows;           // sliding-window kernel: query rows per work item
 };
+
+// Sliding-window kernel for 32..64 query heads per kv head: LDS rows of the
+// window (K and V each, 76 KB in all, two workgroups per CU); a work item of
+// R query rows needs left + right + R <= win_cap(D).
+constexpr int win_cap(int D) { return D == 128 ? 152 : 304; }
 
 // Prefill: items are (sequence, block of bm query rows) with their key range.
 // Decode: (sequence, split of the visible keys).  Backward key blocks:
 // (sequence, block of bm key rows) with the range of query rows that see
 // any of those keys.
-enum PlanMode : int32_t { kPlanPrefill = 0, kPlanDecode = 1, kPlanBwdKeys = 2 };
+// Window: the prefill's items of bm query rows, in index order (the
+// sliding-window kernel's items cost about the same, no sort needed).
+enum PlanMode : int32_t { kPlanPrefill = 0, kPlanDecode = 1, kPlanBwdKeys = 2, kPlanWindow = 3 };
 
 // How the prefill kernel fetches K/V rows: buffer loads over one
 // sequence's rows (contiguous, every sequence span below 2 GiB), plain
@@ -154,6 +162,8 @@ hipError_t launch_backward_bf16(const BwdArgs &a, int head_dim, int total_q, con
                                 int k_grid, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, bool part_bf16, bool out_bf16, hipStream_t s);
 hipError_t launch_sparse16(const SparseArgs &a, bool f16, int head_dim, hipStream_t s);
+hipError_t launch_window16(const AttnArgs &a, bool f16, int head_dim, const int4 *items, const int4 *seqinfo,
+                           const int32_t *count, int grid, hipStream_t s);
 hipError_t launch_plan(const PlanArgs &pa, hipStream_t s);
 hipError_t launch_prefill16(const AttnArgs &a, bool f16, bool alibi, int head_dim, int mode, const int4 *items,
                             const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);

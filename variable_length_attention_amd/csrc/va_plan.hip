@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
         const int b = base + tid;
         int n = 0;
         if (b < a.B) {
-            if (a.mode == kPlanPrefill) {
+            if (a.mode == kPlanPrefill || a.mode == kPlanWindow) {
                 n = (q_len(b) + a.bm - 1) / a.bm;
             } else if (a.mode == kPlanBwdKeys) {
                 n = (k_len(b) + a.bm - 1) / a.bm;  // every key block, even with no query rows
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
         }
         const int b = lo_b;
         const int s = idx - offs[b];
-        if (a.mode == kPlanPrefill) {
+        if (a.mode == kPlanPrefill || a.mode == kPlanWindow) {
             const int Lq = q_len(b), Lk = k_len(b);
             const int i0 = s * a.bm, i1 = min(Lq, i0 + a.bm);
             int lo = 0, hi = 0;
@@ -192,7 +192,15 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
         return make_int4(b, idx, k_lo, k_hi);
     };
 
-    if (N <= kSortMax) {
+    if (a.mode == kPlanWindow) {
+        // 3w. index order
+        for (int idx = tid; idx < N; idx += kPlanThreads) {
+            int cost;
+            const int4 itm = make_item(idx, cost);
+            a.items[idx] = itm;
+            a.seqinfo[idx] = seq_info(itm.x);
+        }
+    } else if (N <= kSortMax) {
         // 3a. sort keys in LDS: ascending key = descending cost, then index
         for (int idx = tid; idx < N; idx += kPlanThreads) {
             int cost;

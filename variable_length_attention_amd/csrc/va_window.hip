@@ -1,0 +1,374 @@
+// Sliding-window attention for wide GQA / MQA groups (32 to 64 query heads
+// per kv head) on gfx950 matrix cores: the first scenario of the
+// SparseAttnSharedkv README (window (127, 0) over the original keys, 64
+// query heads on one kv head, per-head sinks) with separate K and V.
+//
+// Query row i of sequence b (p = i + Lk_b - Lq_b) sees keys
+// [p - left, p + right] within [0, Lk_b); for each query head h
+//   O[i, h] = softmax_j(scale <q[i, h], k_j>, sink_h) . v_j,
+//   LSE[i, h] = natural log of that softmax's denominator.
+//
+// One workgroup = 4 waves = one block of R consecutive query rows of one
+// sequence and one kv head.  The union of the block's windows (at most
+// left + right + R rows of K and of V) is copied global -> LDS once; then
+// every row of the block is computed against its own window slice, heads on
+// the MFMA N side (S^T = K Q^T with keys on M, one lane per head; O^T +=
+// V^T P^T through the transposing LDS read).  A row's 64-key tiles cover
+// exactly its window, so a full window does no masked work, and the waves
+// never wait for each other after the copy: 64 heads take 2 waves per row
+// and 2 rows run at once (32 heads: 1 wave per row, 4 rows at once).
+#include "va_internal.h"
+
+namespace va {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
+
+template <typename T>
+struct Elt;
+template <>
+struct Elt<__bf16> {
+    typedef bf16x8 v8;
+    typedef bf16x4 v4;
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ v4 read_tr(const char *p)
+    {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)((__attribute__((address_space(3))) char *)(p)));
+    }
+    static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Elt<_Float16> {
+    typedef f16x8 v8;
+    typedef f16x4 v4;
+    typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ v4 read_tr(const char *p)
+    {
+        return __builtin_bit_cast(
+            v4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)((__attribute__((address_space(3))) char *)(p))));
+    }
+    static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// Physical 16-byte chunk of logical chunk c in LDS row r is c ^ swz(r): the
+// rows of a row-wise operand read and the 4 rows x 4 chunks of a
+// transposing read land on distinct chunks (D = 128; D = 64 per pair of
+// rows sharing a 256-byte bank line).  It depends on r mod 16 only.
+template <int D>
+__device__ __forceinline__ int swz(int r)
+{
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// 16 bytes per lane, global -> LDS (lane i writes LDS bytes [lds + 16 i, +16));
+// no register results, M0 carries the LDS address.  Ordered by the vector
+// memory wait and the barrier that follow the copies.
+__device__ __forceinline__ void copy16_global(const void *src, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)(p);
+}
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Makes x available at this point of the instruction stream (an empty
+// volatile statement that reads and writes it): operands read in one batch
+// are waited for once, and the next batch's reads are issued while the
+// matrix instructions that use this one run.
+template <typename V>
+__device__ __forceinline__ void pin(V &x)
+{
+    asm volatile("" : "+v"(x));
+}
+
+// The O accumulators hold O[head][d] with lane (n, h2) <-> d = 32 md + n and
+// register v <-> head (v/4) 8 + 4 h2 + v%4.  Per-head scalars live one head
+// per lane (lanes h and h + 32); this returns the one of register v's head.
+__device__ __forceinline__ float head_value(float x, int v, int h2)
+{
+    const int hh = (v >> 2) * 8 + (v & 3);
+    const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), hh));
+    const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), hh + 4));
+    return h2 ? hi : lo;
+}
+
+__device__ __forceinline__ float halves_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k6_window16(
+    AttnArgs a, const int4 *__restrict__ items, const int4 *__restrict__ seqinfo, const int32_t *__restrict__ count)
+{
+    using E = Elt<T>;
+    typedef typename E::v8 v8;
+    typedef typename E::v4 v4;
+    typedef typename E::v2 v2;
+    constexpr int CAP = win_cap(D);    // LDS rows of the window (K and V each)
+    constexpr int NCH = D / 8;         // 16-byte chunks per row
+    constexpr int KS = D / 16;         // QK^T k-steps
+    constexpr int MD = D / 32;         // 32-wide blocks of the head dimension
+    constexpr int RPI = 64 / NCH;      // rows one 64-lane copy fills
+    constexpr int ROWB = 2 * D;        // bytes per LDS row
+    static_assert(CAP % RPI == 0, "whole copies");
+    __shared__ __attribute__((aligned(16))) char s_k[CAP * ROWB];
+    __shared__ __attribute__((aligned(16))) char s_v[CAP * ROWB];
+
+    const int c = blockIdx.x % a.Hkv;
+    const int item = blockIdx.x / a.Hkv;
+    const int n_items = *count;
+    if (item >= n_items) return;
+    const int4 it = items[item];
+    const int4 si = seqinfo[item];
+    const int i0 = it.y, kv_lo = it.z, kv_hi = it.w;
+    const int q0 = si.x, Lq = si.y, k0 = si.z, Lk = si.w;
+    const int delta = Lk - Lq;
+    const int nwin = kv_hi - kv_lo;              // <= left + right + R <= CAP (host)
+    const int rows_here = min(a.item_rows, Lq - i0);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, h2 = lane >> 5, l16 = lane & 15, q4 = l16 >> 2;
+
+    // ---- the block's window: rows kv_lo .. kv_hi-1 to LDS rows 0 .. nwin-1;
+    // rows past nwin (read only as keys outside a row's window) repeat the
+    // last row, so every value the products meet is finite
+    if (nwin > 0) {
+        const int nl = min(CAP, (nwin + 63 + RPI - 1) / RPI * RPI);
+        const char *kb = (const char *)a.k + ((size_t)k0 * a.Hkv + c) * ROWB;
+        const char *vb = (const char *)a.v + ((size_t)k0 * a.Hkv + c) * ROWB;
+        for (int u = wave; u < nl / RPI; u += 4) {
+            const int r = u * RPI + lane / NCH;
+            const int chunk = (lane % NCH) ^ swz<D>(r);
+            const size_t off = (size_t)(kv_lo + min(r, nwin - 1)) * a.Hkv * ROWB + chunk * 16;
+            copy16_global(kb + off, lds_addr(s_k + u * 1024));
+            copy16_global(vb + off, lds_addr(s_v + u * 1024));
+        }
+    }
+
+    // waves per row (1: up to 32 heads, 2: up to 64) and rows in flight
+    const int wpr = a.g > 32 ? 2 : 1;
+    const int rif = 4 / wpr;
+    const int hrow = (wave % wpr) * 32 + n;      // head of the group this lane owns
+    const bool head_ok = hrow < a.g;
+    const int head = c * a.g + (head_ok ? hrow : 0);
+    const float sink2 = (a.sinks && head_ok) ? a.sinks[head] * kLog2e : -INFINITY;
+
+    // Q^T operand fragments of block row r (clamped to the block): lane
+    // (head n, half h2) holds d = 16 ks + 8 h2 .. +8 (lanes past the group
+    // read head 0; their results are never stored).  Each row's are loaded
+    // before the previous row's stores: loads and stores share one counter,
+    // so the wait for them then leaves the stores in flight.
+    auto load_q = [&](int r, v8 (&dst)[KS]) {
+        const size_t tq = (size_t)q0 + i0 + min(r, rows_here - 1);
+        const uint16_t *qp = (const uint16_t *)a.q + (tq * a.H + head) * D + h2 * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) dst[ks] = __builtin_bit_cast(v8, *(const u32x4 *)(qp + ks * 16));
+    };
+    v8 qf[KS];
+    load_q(wave / wpr, qf);
+
+    wait_vmem();
+    __syncthreads();
+
+    for (int r = wave / wpr; r < rows_here; r += rif) {
+        const int i = i0 + r;
+        const int p = i + delta;
+        const int kst = max(0, p - a.left);
+        const int ken = min(Lk - 1, p + a.right);
+        const int nk = max(0, ken - kst + 1);
+        const int ntiles = (nk + 63) / 64;
+        const int base = kst - kv_lo;            // LDS row of the row's first key
+        const size_t t = (size_t)q0 + i;
+        // byte offsets within a row: K operand chunk 2 ks + h2 of a row
+        // congruent to base + n (mod 16); V^T chunk 4 md + 2 ((lane & 31) >> 4)
+        // + ((l16 & 3) >> 1) of a row congruent to base + 4 h2 + q4 + 8 half
+        const int kx = swz<D>(base + n);
+        const int vx0 = swz<D>(base + h2 * 4 + q4), vx1 = swz<D>(base + h2 * 4 + q4 + 8);
+        auto kofs = [&](int ks) -> uint32_t { return ((ks * 2 + h2) ^ kx) << 4; };
+        auto vofs = [&](int md, int half) -> uint32_t {
+            const int ch = md * 4 + ((lane & 31) >> 4) * 2 + ((l16 & 3) >> 1);
+            return ((ch ^ (half ? vx1 : vx0)) << 4) | ((l16 & 1) * 8);
+        };
+        // LDS row of a key, clamped to the allocation (a clamped row only
+        // serves keys past the row's window, whose weight is 0)
+        auto rowb = [&](int rr) -> uint32_t { return (uint32_t)min(rr, CAP - 1) * ROWB; };
+
+        f32x16 o[MD];
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[md][v] = 0.f;
+        float m_run = sink2, l_run = (sink2 != -INFINITY && h2 == 0) ? 1.f : 0.f;
+
+        for (int tau = 0; tau < ntiles; ++tau) {
+            const int tb = base + tau * 64;
+            // S^T = K Q^T: lane value v of block mb is key 64 tau + 32 mb + 8 (v/4) + 4 h2 + v%4
+            f32x16 S[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) S[mb][v] = 0.f;
+                // the block's K operands in one batch of reads, then the products
+                const char *kr = s_k + rowb(tb + mb * 32 + n);
+                v8 kf[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const v8 *)(kr + kofs(ks));
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) pin(kf[ks]);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) S[mb] = E::mfma(kf[ks], qf[ks], S[mb]);
+            }
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) S[mb][v] *= a.scale_log2;
+            if (tau * 64 + 64 > nk) {
+                // the last tile of a window that is not a multiple of 64 keys
+                const int lim = nk - tau * 64 - 4 * h2;
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        S[mb][v] = mb * 32 + 8 * (v >> 2) + (v & 3) >= lim ? -INFINITY : S[mb][v];
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[mb][v]);
+            // the running max moves only when a tile raises it by more than
+            // 2^8 (log2 units) for some head: until then the probabilities
+            // stay below 2^8 and the O / l rescale is skipped
+            mx = halves_max(mx);
+            if (__ballot(mx > m_run + 8.f) != 0ull) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float av = head_value(alpha, v, h2);
+#pragma unroll
+                    for (int md = 0; md < MD; ++md) o[md][v] *= av;
+                }
+                m_run = m_new;
+            }
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;
+            float rs = 0.f;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float pr = __builtin_amdgcn_exp2f(S[mb][v] - m_use);
+                    S[mb][v] = pr;
+                    rs += pr;
+                }
+            l_run += rs;
+            // O += P V, 16 keys per step: rows 16 t4 + 4 h2 + q4 (+8).  The
+            // P fragment (heads on M) comes straight from the S^T
+            // accumulators, the V fragment from the transposing read.
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4) {
+                f32x8 pv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pv[e] = S[t4 >> 1][(t4 & 1) * 8 + e];
+                const v8 pb = __builtin_convertvector(pv, v8);
+                const char *v0 = s_v + rowb(tb + t4 * 16 + h2 * 4 + q4);
+                const char *v1 = s_v + rowb(tb + t4 * 16 + h2 * 4 + q4 + 8);
+                v8 vf[MD];
+#pragma unroll
+                for (int md = 0; md < MD; ++md) {
+                    const v4 va = E::read_tr(v0 + vofs(md, 0));
+                    const v4 vb = E::read_tr(v1 + vofs(md, 1));
+                    vf[md] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+#pragma unroll
+                for (int md = 0; md < MD; ++md) pin(vf[md]);
+#pragma unroll
+                for (int md = 0; md < MD; ++md) o[md] = E::mfma(pb, vf[md], o[md]);
+            }
+        }
+
+        load_q(r + rif, qf);   // the next row's fragments (qf is not read again)
+
+        // epilogue: register v of lane (n, h2) holds O[head (v/4) 8 + 4 h2 +
+        // v%4][32 md + n].  Neighbour lanes trade values (heads h, h + 1 at
+        // d = n, n + 1) so that each lane stores two consecutive d of one
+        // head: every store covers 64 contiguous bytes of 4 heads.  Buffer
+        // stores over this row's heads of the group: the range check drops
+        // heads past the group (and every LSE lane when lse is NULL), so no
+        // branch splits the stores from the loads above.
+        const float l = halves_sum(l_run);
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        float iv[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) iv[v] = head_value(inv, v, h2);
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            (char *)a.out + (t * a.H + (size_t)c * a.g) * D * 2, (short)0, a.g * D * 2, 0x00020000);
+        const bool odd = n & 1;
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+            for (int vp = 0; vp < 8; ++vp) {
+                const float x = o[md][2 * vp] * iv[2 * vp], y = o[md][2 * vp + 1] * iv[2 * vp + 1];
+                // quad_perm [1, 0, 3, 2]: the value of lane n ^ 1
+                const float z = __int_as_float(
+                    __builtin_amdgcn_mov_dpp(__float_as_int(odd ? x : y), 0xB1, 0xF, 0xF, false));
+                const int hd = (wave % wpr) * 32 + (vp >> 1) * 8 + 4 * h2 + 2 * (vp & 1) + (odd ? 1 : 0);
+                const uint32_t pk =
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector(odd ? f32x2{z, y} : f32x2{x, z}, v2));
+                __builtin_amdgcn_raw_buffer_store_b32(pk, ro, hd * D * 2 + (md * 32 + (n & ~1)) * 2, 0, 0);
+            }
+        const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+            a.lse ? (void *)(a.lse + t * a.H + (size_t)c * a.g) : nullptr, (short)0, a.lse ? a.g * 4 : 0, 0x00020000);
+        const float lse = l > 0.f ? (m_run + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, h2 == 0 ? hrow * 4 : a.g * 4, 0, 0);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_window16(const AttnArgs &a, bool f16, int head_dim, const int4 *items, const int4 *seqinfo,
+                           const int32_t *count, int grid, hipStream_t s)
+{
+    const dim3 g(grid), blk(256);
+#define VA_DIMS(TT)                                                                                     \
+    do {                                                                                                \
+        if (head_dim == 128) hipLaunchKernelGGL((k6_window16<TT, 128>), g, blk, 0, s, a, items, seqinfo, count); \
+        else hipLaunchKernelGGL((k6_window16<TT, 64>), g, blk, 0, s, a, items, seqinfo, count);           \
+    } while (0)
+    if (f16) VA_DIMS(_Float16);
+    else VA_DIMS(__bf16);
+#undef VA_DIMS
+    return hipGetLastError();
+}
+
+}  // namespace va
