@@ -283,8 +283,8 @@ va_status varlen_attn_sparse_sharedkv(const va_sparse_problem *p, const void *q,
 
 /* Which kernel family a call with these arguments would use:
  * 0 = prefill tiles, 1 = split-KV decode with combine, 2 = float32 path,
- * 3 = sliding-window kernel (16-bit contiguous K/V, 32..64 query heads per
- * kv head, window bounded on both sides, no ALiBi); -1 if invalid. */
+ * 3 = sliding-window kernel (16-bit K/V, contiguous or paged, 32..64 query
+ * heads per kv head, window bounded on both sides, no ALiBi); -1 if invalid. */
 int varlen_attn_path(const va_problem *p, int paged);
 
 /* Thread-local text for the last non-OK status returned on this thread. */

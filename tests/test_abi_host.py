@@ -166,13 +166,13 @@ def test_workspace_size_and_kernel_path():
     assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, num_heads=32))), 0) == 3  # 32 per kv head
     assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, causal=1, window_right=-1))), 0) == 3
     assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, head_dim=64, window_left=280))), 0) == 3
-    # not taken: 16 heads per kv head, unbounded sides, no room for 4 rows, paged
+    assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, num_blocks=400, block_size=64,
+                                                             block_table_stride=128))), 1) == 3  # paged
+    # not taken: 16 heads per kv head, unbounded sides, no room for 4 rows
     assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, num_heads=16))), 0) == 0
     assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, window_left=-1))), 0) == 0
     assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, window_right=-1))), 0) == 0
     assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, window_left=149))), 0) == 0
-    assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, num_blocks=400, block_size=64,
-                                                             block_table_stride=128))), 1) == 0
     assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, dtype=0, head_dim=64))), 0) == 2
     p = _prob(**c4)
     p.alibi_slopes = 0x10000000                                                          # ALiBi: tile kernel

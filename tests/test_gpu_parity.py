@@ -325,12 +325,12 @@ def _plan_cpu(case, mode, bm=128, bn=64, sort=True):
 
 def _window_rows(case):
     """Query rows per item of the sliding-window kernel (0: not taken): 16-bit
-    contiguous K/V, 32..64 heads per kv head, both window sides bounded
-    (causal bounds the right), room for 4 rows in the 152 (d128) / 304 (d64)
-    LDS rows; about 2048 items per kv head, at most 32 rows."""
+    K/V, 32..64 heads per kv head, both window sides bounded (causal bounds
+    the right), room for 4 rows in the 152 (d128) / 304 (d64) LDS rows;
+    about 2048 items per kv head, at most 32 rows."""
     g = case["H"] // case["Hkv"]
     right = 0 if case["causal"] else case["window_right"]
-    if case["dtype"] == "f32" or case.get("paged") or not 32 <= g <= 64 or case["window_left"] < 0 or right < 0:
+    if case["dtype"] == "f32" or not 32 <= g <= 64 or case["window_left"] < 0 or right < 0:
         return 0
     room = (152 if case["D"] == 128 else 304) - case["window_left"] - right
     if room < 4:

@@ -8,8 +8,8 @@ accumulation, probabilities rounded to the input type for P V).  Cases cover
 the README's first scenario (64 heads on one kv head, window (127, 0),
 sinks), 32 and 48 heads per kv head, d64, two-sided windows, windows that
 leave room for only a few rows per work item, query / key lengths that
-differ (end-aligned rows that see nothing), empty sequences, and rows with
-one visible key.
+differ (end-aligned rows that see nothing), empty sequences, rows with one
+visible key, and paged K/V (block sizes 128 and 48).
 """
 import pytest
 
@@ -35,9 +35,12 @@ def _path(case):
     from variable_length_attention_amd import api
     dt = {"bf16": torch.bfloat16, "f16": torch.float16}[case["dtype"]]
     q = torch.empty((case["T_q"], case["H"], case["D"]), dtype=dt)   # shape and dtype only
+    paged = bool(case.get("paged"))
+    kw = dict(num_blocks=case["num_blocks"], block_size=case["block_size"],
+              block_table_stride=case["block_table"].shape[1]) if paged else {}
     p = api.make_problem(q, case["Hkv"], case["T_k"], case["B"], case["max_q"], case["max_k"], case["scale"],
-                         case["causal"], (case["window_left"], case["window_right"]))
-    return api.kernel_path(p)
+                         case["causal"], (case["window_left"], case["window_right"]), **kw)
+    return api.kernel_path(p, paged)
 
 
 CASES = {
@@ -55,6 +58,12 @@ CASES = {
     "window_leaves_four_rows": (dict(H=64, Hkv=1, D=128, window=(147, 1), sinks=True), [200, 17], None),
     "window_leaves_twelve_rows_f16": (dict(H=64, Hkv=1, D=128, dtype="f16", window=(140, 0), sinks=False),
                                       [333], None),
+    # paged K/V (the README's PA_ND cache): 128-token blocks, and 48-token
+    # blocks (not a power of two) with 32 heads per kv head; permuted tables
+    "readme_scenario1_paged_blocks_128": (dict(H=64, Hkv=1, D=128, window=(127, 0), sinks=True, paged=True,
+                                               block_size=128), [200, 33, 1], [700, 33, 90]),
+    "paged_blocks_48_g32_d64_f16": (dict(H=64, Hkv=2, D=64, dtype="f16", window=(90, 3), sinks=True, paged=True,
+                                         block_size=48), [60, 5, 130], [500, 5, 130]),
 }
 
 

@@ -114,16 +114,16 @@ va_status check_problem(const va_problem *p, int paged)
 }
 
 // Query rows per work item of the sliding-window kernel, or 0 when it does
-// not apply: 16-bit contiguous K/V, no ALiBi, 32..64 query heads per kv
-// head, a window bounded on both sides (causal bounds the right side) that
-// leaves room for at least 4 rows in the LDS window.  About 2048 items per
-// kv head fill the chip several times over; more rows per item share more
-// of the window.
-int window_rows(const va_problem *p, int paged)
+// not apply: 16-bit K/V (contiguous or paged), no ALiBi, 32..64 query heads
+// per kv head, a window bounded on both sides (causal bounds the right
+// side) that leaves room for at least 4 rows in the LDS window.  About 2048
+// items per kv head fill the chip several times over; more rows per item
+// share more of the window.
+int window_rows(const va_problem *p)
 {
     const int g = p->num_heads / p->num_kv_heads;
     const int right = p->causal ? 0 : p->window_right;
-    if (p->dtype == VA_F32 || paged || alibi_of(p) || g < 32 || g > 64 || p->window_left < 0 || right < 0)
+    if (p->dtype == VA_F32 || alibi_of(p) || g < 32 || g > 64 || p->window_left < 0 || right < 0)
         return 0;
     const long long room = (long long)va::win_cap(p->head_dim) - p->window_left - right;
     if (room < 4) return 0;
@@ -134,7 +134,7 @@ int window_rows(const va_problem *p, int paged)
 va_status make_layout(const va_problem *p, int paged, Layout &L)
 {
     const int g = p->num_heads / p->num_kv_heads;
-    const int wrows = window_rows(p, paged);
+    const int wrows = window_rows(p);
     if (p->dtype == VA_F32) {
         L.path = kPathF32;
         L.bm = va::kBMf32;
@@ -361,8 +361,8 @@ va_status run(const Call &c, hipStream_t s)
                                      pa.seqinfo, pa.count, (int)L.grid, s);
         }
         else if (L.path == kPathWindow)
-            e = va::launch_window16(a, c.p->dtype == VA_F16, c.p->head_dim, pa.items, pa.seqinfo, pa.count,
-                                    (int)L.grid, s);
+            e = va::launch_window16(a, c.p->dtype == VA_F16, c.p->head_dim, c.paged, pa.items, pa.seqinfo,
+                                    pa.count, (int)L.grid, s);
         else if (L.path == kPathF32)
             e = va::launch_prefill_f32(a, c.p->head_dim, c.paged, pa.items, pa.seqinfo, pa.count, (int)L.grid, s);
         else {

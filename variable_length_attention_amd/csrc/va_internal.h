@@ -162,8 +162,8 @@ hipError_t launch_backward_bf16(const BwdArgs &a, int head_dim, int total_q, con
                                 int k_grid, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, bool part_bf16, bool out_bf16, hipStream_t s);
 hipError_t launch_sparse16(const SparseArgs &a, bool f16, int head_dim, hipStream_t s);
-hipError_t launch_window16(const AttnArgs &a, bool f16, int head_dim, const int4 *items, const int4 *seqinfo,
-                           const int32_t *count, int grid, hipStream_t s);
+hipError_t launch_window16(const AttnArgs &a, bool f16, int head_dim, bool paged, const int4 *items,
+                           const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);
 hipError_t launch_plan(const PlanArgs &pa, hipStream_t s);
 hipError_t launch_prefill16(const AttnArgs &a, bool f16, bool alibi, int head_dim, int mode, const int4 *items,
                             const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);

@@ -1,7 +1,8 @@
 // Sliding-window attention for wide GQA / MQA groups (32 to 64 query heads
 // per kv head) on gfx950 matrix cores: the first scenario of the
 // SparseAttnSharedkv README (window (127, 0) over the original keys, 64
-// query heads on one kv head, per-head sinks) with separate K and V.
+// query heads on one kv head, per-head sinks) with separate K and V,
+// contiguous or paged through a block table.
 //
 // Query row i of sequence b (p = i + Lk_b - Lq_b) sees keys
 // [p - left, p + right] within [0, Lk_b); for each query head h
@@ -124,7 +125,7 @@ __device__ __forceinline__ float halves_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k6_window16(
     AttnArgs a, const int4 *__restrict__ items, const int4 *__restrict__ seqinfo, const int32_t *__restrict__ count)
 {
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (item >= n_items) return;
     const int4 it = items[item];
     const int4 si = seqinfo[item];
-    const int i0 = it.y, kv_lo = it.z, kv_hi = it.w;
+    const int b = it.x, i0 = it.y, kv_lo = it.z, kv_hi = it.w;
     const int q0 = si.x, Lq = si.y, k0 = si.z, Lk = si.w;
     const int delta = Lk - Lq;
     const int nwin = kv_hi - kv_lo;              // <= left + right + R <= CAP (host)
@@ -158,19 +159,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, h2 = lane >> 5, l16 = lane & 15, q4 = l16 >> 2;
 
-    // ---- the block's window: rows kv_lo .. kv_hi-1 to LDS rows 0 .. nwin-1;
-    // rows past nwin (read only as keys outside a row's window) repeat the
-    // last row, so every value the products meet is finite
+    // ---- the block's window: rows kv_lo .. kv_hi-1 (contiguous, or
+    // through the block table) to LDS rows 0 .. nwin-1; rows past nwin (read
+    // only as keys outside a row's window) repeat the last row, so every
+    // value the products meet is finite
     if (nwin > 0) {
         const int nl = min(CAP, (nwin + 63 + RPI - 1) / RPI * RPI);
-        const char *kb = (const char *)a.k + ((size_t)k0 * a.Hkv + c) * ROWB;
-        const char *vb = (const char *)a.v + ((size_t)k0 * a.Hkv + c) * ROWB;
         for (int u = wave; u < nl / RPI; u += 4) {
             const int r = u * RPI + lane / NCH;
             const int chunk = (lane % NCH) ^ swz<D>(r);
-            const size_t off = (size_t)(kv_lo + min(r, nwin - 1)) * a.Hkv * ROWB + chunk * 16;
-            copy16_global(kb + off, lds_addr(s_k + u * 1024));
-            copy16_global(vb + off, lds_addr(s_v + u * 1024));
+            const size_t off = kv_row_offset<D, PAGED>(a, b, k0, c, kv_lo + min(r, nwin - 1)) * 2 + chunk * 16;
+            copy16_global((const char *)a.k + off, lds_addr(s_k + u * 1024));
+            copy16_global((const char *)a.v + off, lds_addr(s_v + u * 1024));
         }
     }
 
@@ -356,18 +356,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 }  // namespace
 
-hipError_t launch_window16(const AttnArgs &a, bool f16, int head_dim, const int4 *items, const int4 *seqinfo,
-                           const int32_t *count, int grid, hipStream_t s)
+hipError_t launch_window16(const AttnArgs &a, bool f16, int head_dim, bool paged, const int4 *items,
+                           const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s)
 {
     const dim3 g(grid), blk(256);
-#define VA_DIMS(TT)                                                                                     \
-    do {                                                                                                \
-        if (head_dim == 128) hipLaunchKernelGGL((k6_window16<TT, 128>), g, blk, 0, s, a, items, seqinfo, count); \
-        else hipLaunchKernelGGL((k6_window16<TT, 64>), g, blk, 0, s, a, items, seqinfo, count);           \
+#define VA_LAUNCH(TT, DD, PP) hipLaunchKernelGGL((k6_window16<TT, DD, PP>), g, blk, 0, s, a, items, seqinfo, count)
+#define VA_DIMS(TT)                                                           \
+    do {                                                                      \
+        if (head_dim == 128) {                                                \
+            if (paged) VA_LAUNCH(TT, 128, true); else VA_LAUNCH(TT, 128, false); \
+        } else {                                                              \
+            if (paged) VA_LAUNCH(TT, 64, true); else VA_LAUNCH(TT, 64, false);   \
+        }                                                                     \
     } while (0)
     if (f16) VA_DIMS(_Float16);
     else VA_DIMS(__bf16);
 #undef VA_DIMS
+#undef VA_LAUNCH
     return hipGetLastError();
 }
 
