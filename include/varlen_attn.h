@@ -180,7 +180,7 @@ va_status varlen_attn_plan(const va_problem *p, int paged, const int32_t *cu_seq
                            int32_t *count, void *workspace, size_t workspace_bytes,
                            void *stream);
 
-/* Backward (bf16, contiguous K/V), following the boostr CPU backward
+/* Backward (bf16 or fp16, contiguous K/V), following the boostr CPU backward
  * varlen_attention_bwd: given dout [total_q, H, D] and the forward's out and
  * lse (lse carries any sink), writes
  *   dq [total_q, H, D] = scale * sum_j dS_ij k_j
@@ -188,11 +188,11 @@ va_status varlen_attn_plan(const va_problem *p, int paged, const int32_t *cu_seq
  * with P_ij = exp(scale <q_i, k_j> - lse_i) over the allowed keys of the
  * forward (same causal / window arguments), dS_ij = P_ij (<dout_i, v_j> -
  * sum_d dout_i,d out_i,d), and dk / dv of a kv head summed over the query
- * heads that share it.  dq, dk, dv are in the input dtype (bf16; accumulated
+ * heads that share it.  dq, dk, dv are in the input dtype (accumulated
  * in float32) and fully overwritten; keys no query sees get zero gradients.
  * The gradient of sink logits is not computed.  Same ownership, stream and
  * error rules as the forward; dq, dk, dv may not overlap any input, the
- * workspace or each other; p->dtype must be VA_BF16 (else
+ * workspace or each other; p->dtype must be VA_BF16 or VA_F16 (else
  * VA_ERR_UNSUPPORTED).  `workspace` holds at least
  * varlen_attn_bwd_workspace_size(p) bytes. */
 size_t varlen_attn_bwd_workspace_size(const va_problem *p);

@@ -204,7 +204,7 @@ def test_backward_rejects_before_launching():
     assert lib.varlen_attn_bwd_workspace_size(ctypes.byref(_prob(dtype=0))) == 0
     assert _bwd(_prob(dtype=0)) == 4                                   # float32: unsupported
     assert _bwd(_prob(head_dim=96)) == 4
-    assert _bwd(_prob(dtype=2)) == 4                                   # float16: the backward is bf16 only
+    assert _bwd(_prob(dtype=2), ws_bytes=64) == 7                      # float16 accepted (then: workspace)
     assert _bwd(p, dout=None) == 1
     assert _bwd(p, lse=None) == 1
     assert _bwd(p, dq=A[1]) == 5                                       # dq aliases q

@@ -11,7 +11,13 @@ largest gradient element, so each of dq, dk, dv must satisfy
 max|got - ref| <= 2e-2 * max|ref| (the forward's bf16 bound of 2e-2, taken
 relative to the gradient's scale, which grows with the number of summed rows).
 Keys that no query sees must get exactly zero gradients.
+
+fp16 inputs run the same kernels with the fp16 matrix instructions; their
+roundings are 2^-11 instead of 2^-9, so the bound is 5e-3 of max |ref| (the
+forward's fp16 bound on O).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -22,7 +28,7 @@ from helpers import announce, dev, run_case, to_f64
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-REL_TOL = 2e-2
+REL_TOL = {"bf16": 2e-2, "f16": 5e-3}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -35,8 +41,14 @@ def _gpu():
 
 
 def _dout(case, seed=99):
+    """Seeded dout in the case's 16-bit type (bf16 as bits, fp16 as float16)."""
     rng = np.random.default_rng(seed)
-    return W.f32_to_bf16_bits(rng.standard_normal((case["T_q"], case["H"], case["D"]), dtype=np.float32))
+    x = rng.standard_normal((case["T_q"], case["H"], case["D"]), dtype=np.float32)
+    return x.astype(np.float16) if case["dtype"] == "f16" else W.f32_to_bf16_bits(x)
+
+
+def _dout_f64(case, dout):
+    return dout.astype(np.float64) if case["dtype"] == "f16" else W.bf16_bits_to_f32(dout)
 
 
 def _run(case, dout_bits=None):
@@ -79,7 +91,7 @@ def _structural_zeros(case):
 def _check(case, what):
     announce(f"backward {what}")
     out, lse, dout_bits, dq, dk, dv = _run(case)
-    ref = oracle.backward(case, W.bf16_bits_to_f32(dout_bits), to_f64(out), to_f64(lse))
+    ref = oracle.backward(case, _dout_f64(case, dout_bits), to_f64(out), to_f64(lse))
     row_zero, key_zero = _structural_zeros(case)
     errs = {}
     for nm, got, r, zero in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, (row_zero, key_zero, key_zero)):
@@ -88,7 +100,7 @@ def _check(case, what):
         scale = max(np.abs(r).max(), 1e-30)
         err = np.abs(g - r).max() / scale
         errs[nm] = err
-        assert err <= REL_TOL, f"{what}: {nm} max error {err:.3e} of max |ref| {scale:.3e}"
+        assert err <= REL_TOL[case["dtype"]], f"{what}: {nm} max error {err:.3e} of max |ref| {scale:.3e}"
         # rows with nothing to attend / keys nobody sees: exactly zero
         if zero.any():
             assert np.all(r.reshape(r.shape[0], -1)[zero] == 0)
@@ -137,3 +149,19 @@ def test_backward_is_deterministic():
     b = _run(case, dout_bits=a[2])
     for x, y in zip(a[3:], b[3:]):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def _f16(spec):
+    return dataclasses.replace(spec, dtype="f16", name=spec.name + "_f16")
+
+
+def test_backward_f16_causal_gqa_prefill_scaled():
+    case = W.make_case(_f16(W.scaled(W.config(2), B=5, max_len=600, seed=W.config(2).seed + 500)))
+    assert case["q"].dtype == np.float16
+    _check(case, "f16 bf16_causal_gqa_prefill scaled (B=5, lengths <= 600)")
+
+
+def test_backward_f16_window_sinks_d64():
+    spec = _f16(W.Spec("bwd_f16_window_d64", 4343, "bf16", 8, 2, 64, ("fixed", [200, 90, 1]),
+                       window=(40, 9), sinks=True))
+    _check(W.make_case(spec, lens_q=[200, 90, 1], lens_k=[260, 90, 5]), "f16 two-sided window, sinks, d64")

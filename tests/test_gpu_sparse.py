@@ -71,6 +71,9 @@ CASES = {
     # 512 indices per token, 128-token blocks, sinks
     "readme_config_d512": dict(lens_q=[64, 37], seqused_kv=[3000, 2100], H=64, Hkv=1, D=512,
                                window=(127, 0), topk=512, cmp_ratio=4, ori_bs=128, cmp_bs=128),
+    # the README's first scenario at its head size: window (127, 0) only (topk 0), K = V
+    "readme_scenario1_window_only_d512": dict(lens_q=[130, 7], seqused_kv=[900, 7], H=64, Hkv=1, D=512,
+                                              window=(127, 0), topk=0, cmp_ratio=4, ori_bs=128, cmp_bs=128),
     "d512_f16_ragged_invalid_gqa_no_sinks": dict(lens_q=[5, 0, 40, 1], seqused_kv=[300, 7, 90, 1], H=24, Hkv=2,
                                                  D=512, dtype="f16", window=(20, 3), topk=50, cmp_ratio=2,
                                                  invalid_frac=0.2, sinks=False, ori_bs=32, cmp_bs=16),

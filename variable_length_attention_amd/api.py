@@ -245,10 +245,11 @@ def bwd_workspace_size(problem: _lib.VaProblem) -> int:
 def varlen_attn_bwd(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
                     max_seqlen_k: int, *, scale: Optional[float] = None, causal: bool = False,
                     window: Tuple[int, int] = (-1, -1), dq=None, dk=None, dv=None, workspace=None):
-    """Backward of varlen_attn for bf16 contiguous K/V: returns (dq, dk, dv)
-    (allocated when not given) from dout and the forward's out / lse."""
+    """Backward of varlen_attn for bf16 / fp16 contiguous K/V: returns (dq,
+    dk, dv) (allocated when not given) from dout and the forward's out / lse."""
     dev = _check_tensors(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, dq, dk, dv, workspace)
     _need(dout.shape == q.shape and out.shape == q.shape, "dout and out must have q's shape")
+    _need(all(t.dtype == q.dtype for t in (dout, k, v, out)), "dout, q, k, v and out must share a dtype")
     _need(k.dim() == 3 and v.shape == k.shape, "k and v must be [total_k, num_kv_heads, head_dim]")
     _need(lse.dtype == torch.float32 and tuple(lse.shape) == (q.shape[0], q.shape[1]),
           "lse must be float32 [total_q, num_heads]")

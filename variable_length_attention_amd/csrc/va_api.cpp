@@ -409,7 +409,8 @@ va_status bwd_layout(const va_problem *p, BwdLayout &L)
 {
     va_status st = check_problem(p, 0);
     if (st) return st;
-    if (p->dtype != VA_BF16) return fail(VA_ERR_UNSUPPORTED, "the backward takes bf16 inputs");
+    if (p->dtype != VA_BF16 && p->dtype != VA_F16)
+        return fail(VA_ERR_UNSUPPORTED, "the backward takes bf16 or fp16 inputs");
     if (alibi_of(p)) return fail(VA_ERR_UNSUPPORTED, "the backward does not take alibi_slopes");
     const long long nq = ((long long)p->total_q + (long long)p->batch * (va::kBM - 1)) / va::kBM;
     const long long nk = ((long long)p->total_k + (long long)p->batch * (va::kBwdKeys - 1)) / va::kBwdKeys;
@@ -507,8 +508,8 @@ va_status varlen_attn_bwd(const va_problem *p, const void *dout, const void *q, 
     hipError_t e = va::launch_plan(pq, s);
     if (e == hipSuccess) e = va::launch_plan(pk, s);
     if (e == hipSuccess)
-        e = va::launch_backward_bf16(a, p->head_dim, p->total_q, pq.items, pq.seqinfo, pq.count, (int)L.qp.grid,
-                                     pk.items, pk.seqinfo, pk.count, (int)L.kp.grid, s);
+        e = va::launch_backward16(a, p->dtype == VA_F16, p->head_dim, p->total_q, pq.items, pq.seqinfo, pq.count,
+                                  (int)L.qp.grid, pk.items, pk.seqinfo, pk.count, (int)L.kp.grid, s);
     if (e != hipSuccess) return fail(VA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return VA_OK;
 }

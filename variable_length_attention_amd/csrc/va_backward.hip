@@ -1,4 +1,5 @@
-// bf16 backward of the varlen attention forward on gfx950 matrix cores.
+// Backward of the varlen attention forward on gfx950 matrix cores, for bf16
+// or fp16 inputs (one template over the 16-bit type, fp32 accumulation).
 //
 // Method: the steps of the boostr CPU backward varlen_attention_bwd, given
 // the forward's out and lse (a sink enters only through lse):
@@ -38,11 +39,61 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
 
-__device__ __forceinline__ bf16x4 lds_read_tr(const char *p)
-{
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)((__attribute__((address_space(3))) char *)(p)));
-}
+// The 16-bit input type's transposing LDS read, matrix instruction (in the
+// VGPR form, and into AGPR accumulators through assembly: the compiler
+// selects one register form for all of a kernel's matrix instructions; the
+// leading s_nop covers the two wait states after a VALU write of an A / B
+// operand, which the compiler does not see into the block) and widening of
+// the low / high half of a 32-bit word.
+template <typename T>
+struct Elt;
+template <>
+struct Elt<__bf16> {
+    typedef bf16x8 v8;
+    typedef bf16x4 v4;
+    static __device__ __forceinline__ v4 read_tr(const char *p)
+    {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)((__attribute__((address_space(3))) char *)(p)));
+    }
+    static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ void mfma_agpr(f32x16 &acc, v8 a, v8 b)
+    {
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    }
+    static __device__ __forceinline__ float lo(uint32_t x) { return __uint_as_float(x << 16); }
+    static __device__ __forceinline__ float hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+};
+template <>
+struct Elt<_Float16> {
+    typedef f16x8 v8;
+    typedef f16x4 v4;
+    static __device__ __forceinline__ v4 read_tr(const char *p)
+    {
+        return __builtin_bit_cast(
+            v4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)((__attribute__((address_space(3))) char *)(p))));
+    }
+    static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ void mfma_agpr(f32x16 &acc, v8 a, v8 b)
+    {
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    }
+    static __device__ __forceinline__ float lo(uint32_t x) { return (float)__builtin_bit_cast(_Float16, (uint16_t)x); }
+    static __device__ __forceinline__ float hi(uint32_t x)
+    {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
+    }
+};
 
 // Physical 16-byte chunk of logical chunk c in LDS row r is c ^ swz(r).
 // For 256-byte rows (D = 128) the 16 rows of a row-wise operand read get 16
@@ -99,17 +150,8 @@ __device__ __forceinline__ void copy_tile(const char *src, int rows, size_t rows
     }
 }
 
-// acc += A B on the matrix cores with the accumulator held in AGPRs (the
-// dK / dV kernel keeps 256 accumulator registers there and everything else
-// in VGPRs).  Written in assembly because the compiler selects one register
-// form for all of a kernel's matrix instructions.  The leading s_nop covers
-// the two wait states a matrix instruction needs after a VALU write of its
-// A / B operand (the compiler does not see into the block).
-__device__ __forceinline__ void mfma_agpr(f32x16 &acc, bf16x8 a, bf16x8 b)
-{
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// Wait states between the last matrix instruction into acc and any other
+// The dK / dV kernel keeps its 256 accumulator registers in AGPRs
+// (Elt::mfma_agpr) and everything else in VGPRs.  Wait states between the last matrix instruction into acc and any other
 // read of it (VALU, LDS or memory instructions read AGPRs only after the
 // matrix pipeline has written them back; 16 passes need 18).
 __device__ __forceinline__ void mfma_agpr_drain(f32x16 &acc)
@@ -122,15 +164,15 @@ __device__ __forceinline__ void mfma_agpr_drain(f32x16 &acc)
 // side effects is otherwise free to sink towards its uses).
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 
-// bf16 pairs of a 32-bit word widened to fp32
-__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
 // ------------------------------------------------------------------ B0
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void k_bwd_dot(const uint16_t *__restrict__ dout, const uint16_t *__restrict__ out,
                                                  float *__restrict__ dvec, int rows)
 {
+    using E = Elt<T>;
+    typedef typename E::v8 v8;
+    typedef typename E::v4 v4;
     constexpr int LPR = D / 8;        // lanes per (row, head), 16 bytes each
     constexpr int RPB = 256 / LPR;    // (row, head) pairs per workgroup
     const int r = blockIdx.x * RPB + threadIdx.x / LPR;
@@ -140,7 +182,7 @@ __global__ __launch_bounds__(256) void k_bwd_dot(const uint16_t *__restrict__ do
         const u32x4 x = *(const u32x4 *)(dout + (size_t)r * D + l * 8);
         const u32x4 y = *(const u32x4 *)(out + (size_t)r * D + l * 8);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc += bf_lo(x[e]) * bf_lo(y[e]) + bf_hi(x[e]) * bf_hi(y[e]);
+        for (int e = 0; e < 4; ++e) acc += E::lo(x[e]) * E::lo(y[e]) + E::hi(x[e]) * E::hi(y[e]);
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -148,10 +190,13 @@ __global__ __launch_bounds__(256) void k_bwd_dot(const uint16_t *__restrict__ do
 }
 
 // ------------------------------------------------------------------ B1
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dq(
     BwdArgs a, const int4 *__restrict__ items, const int4 *__restrict__ seqinfo, const int32_t *__restrict__ count)
 {
+    using E = Elt<T>;
+    typedef typename E::v8 v8;
+    typedef typename E::v4 v4;
     constexpr int BN = 64;
     constexpr int NCH = D / 8;
     constexpr int KS = D / 16;
@@ -208,7 +253,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
 
     // Q^T and dO^T operand fragments: lane (row n, half h2) holds d = 16 ks + 8 h2 .. +8
-    bf16x8 qf[KS], df[KS];
+    v8 qf[KS], df[KS];
     {
         const size_t off = ((size_t)(q0 + (row_ok ? row : 0)) * a.H + head) * D + h2 * 8;
         const uint16_t *qp = (const uint16_t *)a.q + off;
@@ -218,8 +263,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             u32x4 x = *(const u32x4 *)(qp + ks * 16);
             u32x4 y = *(const u32x4 *)(dp + ks * 16);
             if (!row_ok) { x = u32x4{0, 0, 0, 0}; y = u32x4{0, 0, 0, 0}; }
-            qf[ks] = __builtin_bit_cast(bf16x8, x);
-            df[ks] = __builtin_bit_cast(bf16x8, y);
+            qf[ks] = __builtin_bit_cast(v8, x);
+            df[ks] = __builtin_bit_cast(v8, y);
         }
     }
     // lse in log2 units; rows without any allowed key (lse = -inf) and rows
@@ -266,14 +311,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int v = 0; v < 16; ++v) { S[0][v] = 0.f; S[1][v] = 0.f; P[0][v] = 0.f; P[1][v] = 0.f; }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 k0f = *(const bf16x8 *)(kt + koff(ks));
-                const bf16x8 k1f = *(const bf16x8 *)(kt + koff(ks) + 32 * ROWB);
-                const bf16x8 v0f = *(const bf16x8 *)(vt + koff(ks));
-                const bf16x8 v1f = *(const bf16x8 *)(vt + koff(ks) + 32 * ROWB);
-                S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[ks], S[0], 0, 0, 0);
-                S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[ks], S[1], 0, 0, 0);
-                P[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0f, df[ks], P[0], 0, 0, 0);
-                P[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1f, df[ks], P[1], 0, 0, 0);
+                const v8 k0f = *(const v8 *)(kt + koff(ks));
+                const v8 k1f = *(const v8 *)(kt + koff(ks) + 32 * ROWB);
+                const v8 v0f = *(const v8 *)(vt + koff(ks));
+                const v8 v1f = *(const v8 *)(vt + koff(ks) + 32 * ROWB);
+                S[0] = E::mfma(k0f, qf[ks], S[0]);
+                S[1] = E::mfma(k1f, qf[ks], S[1]);
+                P[0] = E::mfma(v0f, df[ks], P[0]);
+                P[1] = E::mfma(v1f, df[ks], P[1]);
             }
             if (!(j0 >= flo && j0 + BN - 1 <= fhi)) {
                 // key j is allowed iff (unsigned)(j - lo) <= (unsigned)(hi - lo)
@@ -298,14 +343,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     const float p = __builtin_amdgcn_exp2f(fmaf(S[t4 >> 1][ix], a.scale_log2, -lse2));
                     x[e] = p * (P[t4 >> 1][ix] - dvr);
                 }
-                const bf16x8 dsb = __builtin_convertvector(x, bf16x8);
+                const v8 dsb = __builtin_convertvector(x, v8);
                 // dQ^T += K^T dS^T
 #pragma unroll
                 for (int md = 0; md < MD; ++md) {
-                    const bf16x4 ka = lds_read_tr(kt + toff(md, 0) + t4 * 16 * ROWB);
-                    const bf16x4 kb = lds_read_tr(kt + toff(md, 1) + t4 * 16 * ROWB);
-                    const bf16x8 kf = __builtin_shufflevector(ka, kb, 0, 1, 2, 3, 4, 5, 6, 7);
-                    dqa[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, dsb, dqa[md], 0, 0, 0);
+                    const v4 ka = E::read_tr(kt + toff(md, 0) + t4 * 16 * ROWB);
+                    const v4 kb = E::read_tr(kt + toff(md, 1) + t4 * 16 * ROWB);
+                    const v8 kf = __builtin_shufflevector(ka, kb, 0, 1, 2, 3, 4, 5, 6, 7);
+                    dqa[md] = E::mfma(kf, dsb, dqa[md]);
                 }
             }
         }
@@ -329,7 +374,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             f32x4 x;
 #pragma unroll
             for (int j = 0; j < 4; ++j) x[j] = dqa[md][i * 4 + j] * a.scale;
-            const bf16x4 y = __builtin_convertvector(x, bf16x4);
+            const v4 y = __builtin_convertvector(x, v4);
             const int phys = (md * 4 + i) ^ (n % NCH);
             *(u32x2 *)(ow + n * ROWB + phys * 16 + h2 * 8) = __builtin_bit_cast(u32x2, y);
         }
@@ -349,10 +394,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ------------------------------------------------------------------ B2
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd_dkdv(
     BwdArgs a, const int4 *__restrict__ items, const int4 *__restrict__ seqinfo, const int32_t *__restrict__ count)
 {
+    using E = Elt<T>;
+    typedef typename E::v8 v8;
+    typedef typename E::v4 v4;
     constexpr int QT = 64;             // query rows per tile
     constexpr int KS = D / 16;
     constexpr int MD = D / 32;
@@ -396,7 +444,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // K^T operand fragments (B side) in registers: lane (key n, half h2)
     // holds d = 16 ks + 8 h2 .. +8; the V rows of the block go to LDS (the
     // dP products read them from there: registers are short)
-    bf16x8 kf[2][KS];
+    v8 kf[2][KS];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         const size_t off = ((size_t)(k0 + (key_ok[kb] ? keyv[kb] : 0)) * a.Hkv + c) * D + h2 * 8;
@@ -405,7 +453,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 x = *(const u32x4 *)(kp + ks * 16);
             if (!key_ok[kb]) x = u32x4{0, 0, 0, 0};
-            kf[kb][ks] = __builtin_bit_cast(bf16x8, x);
+            kf[kb][ks] = __builtin_bit_cast(v8, x);
         }
     }
     {
@@ -527,14 +575,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int v = 0; v < 16; ++v) S[kb][v] = 0.f;
         // all Q operands first: one LDS latency for the 2 KS products
-        bf16x8 qa[KS];
+        v8 qa[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qa[ks] = *(const bf16x8 *)(qt + roff(ks));
+        for (int ks = 0; ks < KS; ++ks) qa[ks] = *(const v8 *)(qt + roff(ks));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[0][ks], S[0], 0, 0, 0);
-            S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[1][ks], S[1], 0, 0, 0);
+            S[0] = E::mfma(qa[ks], kf[0][ks], S[0]);
+            S[1] = E::mfma(qa[ks], kf[1][ks], S[1]);
         }
         if (!full) {
 #pragma unroll
@@ -566,32 +614,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             pin(p);
             S[kb][v] = p;
         };
-        bf16x8 oa = *(const bf16x8 *)(ot + roff(0));
-        bf16x8 v0 = *(const bf16x8 *)(vt + voff(0, 0));
-        bf16x8 v1 = *(const bf16x8 *)(vt + voff(1, 0));
+        v8 oa = *(const v8 *)(ot + roff(0));
+        v8 v0 = *(const v8 *)(vt + voff(0, 0));
+        v8 v1 = *(const v8 *)(vt + voff(1, 0));
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 oc = oa, vc0 = v0, vc1 = v1;
+            const v8 oc = oa, vc0 = v0, vc1 = v1;
             if (ks + 1 < KS) {
-                oa = *(const bf16x8 *)(ot + roff(ks + 1));
-                v0 = *(const bf16x8 *)(vt + voff(0, ks + 1));
-                v1 = *(const bf16x8 *)(vt + voff(1, ks + 1));
+                oa = *(const v8 *)(ot + roff(ks + 1));
+                v0 = *(const v8 *)(vt + voff(0, ks + 1));
+                v1 = *(const v8 *)(vt + voff(1, ks + 1));
             }
             // 32 values over 2 KS matrix instructions
             constexpr int EPS = 16 / KS;
             static_assert(2 * KS * EPS == 32, "every probability gets a slot");
             copy_part(ks);
-            P[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oc, vc0, P[0], 0, 0, 0);
+            P[0] = E::mfma(oc, vc0, P[0]);
 #pragma unroll
             for (int e = 0; e < EPS; ++e) prob((ks * 2) * EPS + e);
             __builtin_amdgcn_sched_barrier(0);
-            P[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oc, vc1, P[1], 0, 0, 0);
+            P[1] = E::mfma(oc, vc1, P[1]);
 #pragma unroll
             for (int e = 0; e < EPS; ++e) prob((ks * 2 + 1) * EPS + e);
             __builtin_amdgcn_sched_barrier(0);
         }
         // bf16 probabilities: the dV operand
-        bf16x8 pb[2][2];
+        v8 pb[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -599,7 +647,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 f32x8 x;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = S[kb][half * 8 + e];
-                pb[kb][half] = __builtin_convertvector(x, bf16x8);
+                pb[kb][half] = __builtin_convertvector(x, v8);
             }
         // dV^T += dO^T P over this wave's 32 rows, interleaved with
         // dS = P (dP - Dv) (in place in P)
@@ -614,24 +662,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const int t4 = rh * 2 + half;  // 16-row step of the tile
 #pragma unroll
             for (int md = 0; md < MD; ++md) {
-                const bf16x4 ta = lds_read_tr(ot + toff(md, 0) + t4 * 16 * ROWB);
-                const bf16x4 tb = lds_read_tr(ot + toff(md, 1) + t4 * 16 * ROWB);
-                const bf16x8 of = __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7);
+                const v4 ta = E::read_tr(ot + toff(md, 0) + t4 * 16 * ROWB);
+                const v4 tb = E::read_tr(ot + toff(md, 1) + t4 * 16 * ROWB);
+                const v8 of = __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7);
                 // 32 values over 4 MD matrix instructions
                 constexpr int EPD = 8 / MD;
                 static_assert(4 * MD * EPD == 32, "every dS value gets a slot");
                 const int sl = (half * MD + md) * 2;
-                mfma_agpr(dva[md][0], of, pb[0][half]);
+                E::mfma_agpr(dva[md][0], of, pb[0][half]);
 #pragma unroll
                 for (int e = 0; e < EPD; ++e) dsm(sl * EPD + e);
                 __builtin_amdgcn_sched_barrier(0);
-                mfma_agpr(dva[md][1], of, pb[1][half]);
+                E::mfma_agpr(dva[md][1], of, pb[1][half]);
 #pragma unroll
                 for (int e = 0; e < EPD; ++e) dsm((sl + 1) * EPD + e);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        bf16x8 db[2][2];
+        v8 db[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -639,23 +687,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 f32x8 x;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = P[kb][half * 8 + e];
-                db[kb][half] = __builtin_convertvector(x, bf16x8);
+                db[kb][half] = __builtin_convertvector(x, v8);
             }
         // dK^T += Q^T dS
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int t4 = rh * 2 + half;
-            bf16x8 qf[MD];
+            v8 qf[MD];
 #pragma unroll
             for (int md = 0; md < MD; ++md) {
-                const bf16x4 ta = lds_read_tr(qt + toff(md, 0) + t4 * 16 * ROWB);
-                const bf16x4 tb = lds_read_tr(qt + toff(md, 1) + t4 * 16 * ROWB);
+                const v4 ta = E::read_tr(qt + toff(md, 0) + t4 * 16 * ROWB);
+                const v4 tb = E::read_tr(qt + toff(md, 1) + t4 * 16 * ROWB);
                 qf[md] = __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7);
             }
 #pragma unroll
             for (int md = 0; md < MD; ++md)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) mfma_agpr(dka[md][kb], qf[md], db[kb][half]);
+                for (int kb = 0; kb < 2; ++kb) E::mfma_agpr(dka[md][kb], qf[md], db[kb][half]);
         }
     };
 
@@ -716,7 +764,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                     for (int j = 0; j < 4; ++j) x[j] = (acc[md][kb][i * 4 + j] + o[j]) * mul;
                     const int d = md * 32 + i * 8 + h2 * 4;
-                    *(u32x2 *)((uint16_t *)dst + base + d) = __builtin_bit_cast(u32x2, __builtin_convertvector(x, bf16x4));
+                    *(u32x2 *)((uint16_t *)dst + base + d) = __builtin_bit_cast(u32x2, __builtin_convertvector(x, v4));
                 }
         }
     };
@@ -731,23 +779,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 }  // namespace
 
-hipError_t launch_backward_bf16(const BwdArgs &a, int head_dim, int total_q, const int4 *q_items,
-                                const int4 *q_seqinfo, const int32_t *q_count, int q_grid,
-                                const int4 *k_items, const int4 *k_seqinfo, const int32_t *k_count,
-                                int k_grid, hipStream_t s)
+hipError_t launch_backward16(const BwdArgs &a, bool f16, int head_dim, int total_q, const int4 *q_items,
+                             const int4 *q_seqinfo, const int32_t *q_count, int q_grid, const int4 *k_items,
+                             const int4 *k_seqinfo, const int32_t *k_count, int k_grid, hipStream_t s)
 {
     const int rows = total_q * a.H;
-    if (head_dim == 128) {
-        hipLaunchKernelGGL(k_bwd_dot<128>, dim3((rows + 15) / 16), dim3(256), 0, s,
-                           (const uint16_t *)a.dout, (const uint16_t *)a.out, a.dvec, rows);
-        hipLaunchKernelGGL(k_bwd_dq<128>, dim3(q_grid), dim3(256), 0, s, a, q_items, q_seqinfo, q_count);
-        hipLaunchKernelGGL(k_bwd_dkdv<128>, dim3(k_grid), dim3(256), 0, s, a, k_items, k_seqinfo, k_count);
+#define VA_BWD(TT, DD)                                                                                   \
+    do {                                                                                                 \
+        hipLaunchKernelGGL((k_bwd_dot<TT, DD>), dim3((rows + 256 / (DD / 8) - 1) / (256 / (DD / 8))), dim3(256), 0, s, \
+                           (const uint16_t *)a.dout, (const uint16_t *)a.out, a.dvec, rows);          \
+        hipLaunchKernelGGL((k_bwd_dq<TT, DD>), dim3(q_grid), dim3(256), 0, s, a, q_items, q_seqinfo, q_count); \
+        hipLaunchKernelGGL((k_bwd_dkdv<TT, DD>), dim3(k_grid), dim3(256), 0, s, a, k_items, k_seqinfo, k_count); \
+    } while (0)
+    if (f16) {
+        if (head_dim == 128) VA_BWD(_Float16, 128);
+        else VA_BWD(_Float16, 64);
     } else {
-        hipLaunchKernelGGL(k_bwd_dot<64>, dim3((rows + 31) / 32), dim3(256), 0, s,
-                           (const uint16_t *)a.dout, (const uint16_t *)a.out, a.dvec, rows);
-        hipLaunchKernelGGL(k_bwd_dq<64>, dim3(q_grid), dim3(256), 0, s, a, q_items, q_seqinfo, q_count);
-        hipLaunchKernelGGL(k_bwd_dkdv<64>, dim3(k_grid), dim3(256), 0, s, a, k_items, k_seqinfo, k_count);
+        if (head_dim == 128) VA_BWD(__bf16, 128);
+        else VA_BWD(__bf16, 64);
     }
+#undef VA_BWD
     return hipGetLastError();
 }
 
