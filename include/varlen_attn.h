@@ -188,7 +188,9 @@ va_status varlen_attn_plan(const va_problem *p, int paged, const int32_t *cu_seq
  * with P_ij = exp(scale <q_i, k_j> - lse_i) over the allowed keys of the
  * forward (same causal / window arguments), dS_ij = P_ij (<dout_i, v_j> -
  * sum_d dout_i,d out_i,d), and dk / dv of a kv head summed over the query
- * heads that share it.  dq, dk, dv are in the input dtype (accumulated
+ * heads that share it; with p->alibi_slopes the scores carry the forward's
+ * bias (-slope_h |i + Lk - Lq - j|, the slopes being an input like q).  dq,
+ * dk, dv are in the input dtype (accumulated
  * in float32) and fully overwritten; keys no query sees get zero gradients.
  * The gradient of sink logits is not computed.  Same ownership, stream and
  * error rules as the forward; dq, dk, dv may not overlap any input, the

@@ -51,12 +51,14 @@ def test_version_one_problem_struct_is_accepted():
     # a caller built against version 1 (struct ends after block_table_stride)
     # (host checks only: the size queries launch nothing)
     lib = _lib.load()
-    p = _prob()
+    # 64 heads on one kv head, window (127, 0): slopes send it to the tile kernel
+    p = _prob(num_heads=64, num_kv_heads=1, causal=0, window_left=127, window_right=0)
     p.alibi_slopes = 0x1234
-    assert lib.varlen_attn_bwd_workspace_size(ctypes.byref(p)) == 0     # slopes: backward refuses
+    assert lib.varlen_attn_path(ctypes.byref(p), 0) == 0
     p.struct_size = _lib.VaProblem.block_table_stride.offset + 4
-    assert lib.varlen_attn_bwd_workspace_size(ctypes.byref(p)) > 0      # beyond the struct: not read
+    assert lib.varlen_attn_path(ctypes.byref(p), 0) == 3                 # beyond the struct: not read
     assert lib.varlen_attn_workspace_size(ctypes.byref(p), 0) > 0
+    assert lib.varlen_attn_bwd_workspace_size(ctypes.byref(p)) > 0
     p.struct_size -= 4
     assert lib.varlen_attn_workspace_size(ctypes.byref(p), 0) == 0      # shorter than version 1
 

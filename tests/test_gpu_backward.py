@@ -14,7 +14,8 @@ Keys that no query sees must get exactly zero gradients.
 
 fp16 inputs run the same kernels with the fp16 matrix instructions; their
 roundings are 2^-11 instead of 2^-9, so the bound is 5e-3 of max |ref| (the
-forward's fp16 bound on O).
+forward's fp16 bound on O).  With ALiBi slopes (geometric, 2^(-8 (h+1) / H))
+both sides add the forward's bias to the recomputed scores.
 """
 import dataclasses
 
@@ -60,7 +61,8 @@ def _run(case, dout_bits=None):
     cu_q, cu_k = dev(case["cu_q"], torch), dev(case["cu_k"], torch)
     dq, dk, dv = va.varlen_attn_bwd(dout, q, k, v, out, lse, cu_q, cu_k, case["max_q"], case["max_k"],
                                     scale=case["scale"], causal=case["causal"],
-                                    window=(case["window_left"], case["window_right"]))
+                                    window=(case["window_left"], case["window_right"]),
+                                    alibi_slopes=dev(case.get("alibi"), torch))
     torch.cuda.synchronize()
     return out, lse, dout_bits, dq, dk, dv
 
@@ -165,3 +167,21 @@ def test_backward_f16_window_sinks_d64():
     spec = _f16(W.Spec("bwd_f16_window_d64", 4343, "bf16", 8, 2, 64, ("fixed", [200, 90, 1]),
                        window=(40, 9), sinks=True))
     _check(W.make_case(spec, lens_q=[200, 90, 1], lens_k=[260, 90, 5]), "f16 two-sided window, sinks, d64")
+
+
+def _slopes(H):
+    return (2.0 ** (-8.0 * np.arange(1, H + 1) / H)).astype(np.float32)
+
+
+def test_backward_alibi_causal_gqa_prefill_scaled():
+    case = W.make_case(W.scaled(W.config(2), B=5, max_len=600, seed=W.config(2).seed + 600))
+    case["alibi"] = _slopes(case["H"])
+    _check(case, "alibi bf16_causal_gqa_prefill scaled (B=5, lengths <= 600)")
+
+
+def test_backward_alibi_f16_window_end_aligned_d64():
+    spec = _f16(W.Spec("bwd_alibi_f16_d64", 4444, "bf16", 8, 2, 64, ("fixed", [120, 33, 200]),
+                       window=(50, 5), sinks=True))
+    case = W.make_case(spec, lens_q=[120, 33, 200], lens_k=[300, 33, 210])
+    case["alibi"] = _slopes(case["H"])
+    _check(case, "alibi f16 two-sided window, sinks, end-aligned, d64")

@@ -244,9 +244,11 @@ def bwd_workspace_size(problem: _lib.VaProblem) -> int:
 
 def varlen_attn_bwd(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
                     max_seqlen_k: int, *, scale: Optional[float] = None, causal: bool = False,
-                    window: Tuple[int, int] = (-1, -1), dq=None, dk=None, dv=None, workspace=None):
+                    window: Tuple[int, int] = (-1, -1), dq=None, dk=None, dv=None, workspace=None,
+                    alibi_slopes=None):
     """Backward of varlen_attn for bf16 / fp16 contiguous K/V: returns (dq,
-    dk, dv) (allocated when not given) from dout and the forward's out / lse."""
+    dk, dv) (allocated when not given) from dout and the forward's out / lse
+    (``alibi_slopes``: the forward's slopes, when it had them)."""
     dev = _check_tensors(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, dq, dk, dv, workspace)
     _need(dout.shape == q.shape and out.shape == q.shape, "dout and out must have q's shape")
     _need(all(t.dtype == q.dtype for t in (dout, k, v, out)), "dout, q, k, v and out must share a dtype")
@@ -259,7 +261,7 @@ def varlen_attn_bwd(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seq
     dv = torch.empty_like(v) if dv is None else dv
     _need(dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape, "gradient shapes")
     p = make_problem(q, k.shape[1], k.shape[0], cu_seqlens_q.numel() - 1, max_seqlen_q, max_seqlen_k,
-                     scale, causal, window)
+                     scale, causal, window, alibi_slopes=alibi_slopes)
     need = bwd_workspace_size(p)
     if need == 0:
         _lib.check(_lib.load().varlen_attn_bwd(ctypes.byref(p), *([None] * 12), ctypes.c_size_t(0), None))

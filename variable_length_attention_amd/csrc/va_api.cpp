@@ -411,7 +411,6 @@ va_status bwd_layout(const va_problem *p, BwdLayout &L)
     if (st) return st;
     if (p->dtype != VA_BF16 && p->dtype != VA_F16)
         return fail(VA_ERR_UNSUPPORTED, "the backward takes bf16 or fp16 inputs");
-    if (alibi_of(p)) return fail(VA_ERR_UNSUPPORTED, "the backward does not take alibi_slopes");
     const long long nq = ((long long)p->total_q + (long long)p->batch * (va::kBM - 1)) / va::kBM;
     const long long nk = ((long long)p->total_k + (long long)p->batch * (va::kBwdKeys - 1)) / va::kBwdKeys;
     const long long gq = nq * p->num_heads, gk = nk * p->num_kv_heads;
@@ -475,8 +474,8 @@ va_status varlen_attn_bwd(const va_problem *p, const void *dout, const void *q, 
     const void *al16[] = {dout, q, k, v, out, dq, dk, dv, workspace};
     for (const void *ptr : al16)
         if (!aligned(ptr, 16)) return fail(VA_ERR_ALIGN, "data pointers and the workspace must be 16-byte aligned");
-    if (!aligned(lse, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
-        return fail(VA_ERR_ALIGN, "lse and cu_seqlens must be 4-byte aligned");
+    if (!aligned(lse, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(alibi_of(p), 4))
+        return fail(VA_ERR_ALIGN, "lse, cu_seqlens and alibi_slopes must be 4-byte aligned");
     const size_t D = (size_t)p->head_dim;
     const size_t qb = (size_t)p->total_q * p->num_heads * D * 2;
     const size_t kb = (size_t)p->total_k * p->num_kv_heads * D * 2;
@@ -484,7 +483,7 @@ va_status varlen_attn_bwd(const va_problem *p, const void *dout, const void *q, 
     const Range ins[] = {{dout, qb}, {q, qb}, {k, kb}, {v, kb}, {out, qb},
                          {lse, (size_t)p->total_q * p->num_heads * 4},
                          {cu_seqlens_q, 4 * ((size_t)p->batch + 1)}, {cu_seqlens_k, 4 * ((size_t)p->batch + 1)},
-                         {workspace, workspace_bytes}};
+                         {alibi_of(p), alibi_of(p) ? 4 * (size_t)p->num_heads : 0}, {workspace, workspace_bytes}};
     for (int i = 0; i < 3; ++i) {
         for (const Range &r : ins)
             if (overlaps(outs[i], r)) return fail(VA_ERR_ALIAS, "dq, dk and dv must not overlap an input or the workspace");
@@ -502,13 +501,15 @@ va_status varlen_attn_bwd(const va_problem *p, const void *dout, const void *q, 
     else a.right = p->window_right >= 0 ? p->window_right : va::kInfOff;
     a.scale = p->scale;
     a.scale_log2 = p->scale * va::kLog2e;
+    a.alibi = alibi_of(p);
     hipStream_t s = (hipStream_t)stream;
     const va::PlanArgs pq = bwd_plan(p, cu_seqlens_q, cu_seqlens_k, a, ws, L.qp, va::kPlanPrefill);
     const va::PlanArgs pk = bwd_plan(p, cu_seqlens_q, cu_seqlens_k, a, ws, L.kp, va::kPlanBwdKeys);
     hipError_t e = va::launch_plan(pq, s);
     if (e == hipSuccess) e = va::launch_plan(pk, s);
     if (e == hipSuccess)
-        e = va::launch_backward16(a, p->dtype == VA_F16, p->head_dim, p->total_q, pq.items, pq.seqinfo, pq.count,
+        e = va::launch_backward16(a, p->dtype == VA_F16, a.alibi != nullptr, p->head_dim, p->total_q, pq.items,
+                                  pq.seqinfo, pq.count,
                                   (int)L.qp.grid, pk.items, pk.seqinfo, pk.count, (int)L.kp.grid, s);
     if (e != hipSuccess) return fail(VA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return VA_OK;

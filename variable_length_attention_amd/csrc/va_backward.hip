@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void k_bwd_dot(const uint16_t *__restrict__ do
 }
 
 // ------------------------------------------------------------------ B1
-template <typename T, int D>
+template <typename T, int D, bool ALIBI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dq(
     BwdArgs a, const int4 *__restrict__ items, const int4 *__restrict__ seqinfo, const int32_t *__restrict__ count)
 {
@@ -270,6 +270,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // lse in log2 units; rows without any allowed key (lse = -inf) and rows
     // past the end get +inf, which makes every probability 0
     float lse2 = INFINITY, dvr = 0.f;
+    // ALiBi in log2 units: - slope log2(e) |row + delta - j|
+    const float sl2 = ALIBI ? a.alibi[head] * kLog2e : 0.f;
     if (row_ok) {
         const size_t ri = (size_t)(q0 + row) * a.H + head;
         const float l = a.lse[ri];
@@ -333,14 +335,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         S[mb][v] = d > span ? -INFINITY : S[mb][v];
                     }
             }
-            // dS^T in bf16, laid out as the B operand of step t4 (keys 16 t4 ..)
+            // dS^T in the input type, laid out as the B operand of step t4 (keys 16 t4 ..)
+            const float abase = (float)(row + delta - j0 - 4 * h2);
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4) {
                 f32x8 x;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int ix = (t4 & 1) * 8 + e;
-                    const float p = __builtin_amdgcn_exp2f(fmaf(S[t4 >> 1][ix], a.scale_log2, -lse2));
+                    float y = fmaf(S[t4 >> 1][ix], a.scale_log2, -lse2);
+                    if constexpr (ALIBI)
+                        y = fmaf(-sl2, fabsf(abase - (float)(32 * (t4 >> 1) + 8 * (ix >> 2) + (ix & 3))), y);
+                    const float p = __builtin_amdgcn_exp2f(y);
                     x[e] = p * (P[t4 >> 1][ix] - dvr);
                 }
                 const v8 dsb = __builtin_convertvector(x, v8);
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ------------------------------------------------------------------ B2
-template <typename T, int D>
+template <typename T, int D, bool ALIBI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd_dkdv(
     BwdArgs a, const int4 *__restrict__ items, const int4 *__restrict__ seqinfo, const int32_t *__restrict__ count)
 {
@@ -493,6 +499,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // read into registers here and written to LDS by row_store() at the end
     // of the current step, so that waiting for them never waits for copies
     float st_l2 = INFINITY, st_dv = 0.f;
+    // ALiBi slope (log2 units) of the next step's head and of this step's
+    float sl_next = 0.f, sl_cur = 0.f;
     auto tile_row = [&](int s) { return qlo + (s % qtiles) * QT; };
     auto tile_head = [&](int s) { return c * a.g + s / qtiles; };
     // copies of step s's tiles: KS parts of one 16-byte-per-lane copy each
@@ -522,6 +530,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int r0 = tile_row(s);
         st_l2 = INFINITY;
         st_dv = 0.f;
+        if constexpr (ALIBI) sl_next = a.alibi[h] * kLog2e;
         const int r = r0 + tid;
         if (tid < QT && r < qhi) {
             const size_t ri = (size_t)(q0 + r) * a.H + h;
@@ -608,9 +617,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) P[kb][v] = 0.f;
+        // ALiBi: row 32 rh + 8 (v/4) + 4 h2 + v%4 of the tile against key keyv[kb]
+        float abase[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) abase[kb] = (float)(r0 + rh * 32 + 4 * h2 + delta - keyv[kb]);
         auto prob = [&](int idx) {
             const int kb = idx >> 4, v = idx & 15;
-            float p = __builtin_amdgcn_exp2f(fmaf(S[kb][v], a.scale_log2, -l2r[v >> 2][v & 3]));
+            float y = fmaf(S[kb][v], a.scale_log2, -l2r[v >> 2][v & 3]);
+            if constexpr (ALIBI) y = fmaf(-sl_cur, fabsf(abase[kb] + (float)(8 * (v >> 2) + (v & 3))), y);
+            float p = __builtin_amdgcn_exp2f(y);
             pin(p);
             S[kb][v] = p;
         };
@@ -713,6 +728,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int part = 0; part < KS; ++part) copy_part(part);
         issue(0, 0);
         row_store(0);
+        sl_cur = sl_next;
     }
     wait_vmem();
     __syncthreads();
@@ -724,6 +740,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int r0 = tile_row(s);
         step(slot, r0, tile_full(r0));
         if (more) row_store(slot ^ 1);  // the next step's slot is not read in this step
+        sl_cur = sl_next;
         wait_vmem();
         __syncthreads();
     }
@@ -779,17 +796,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 }  // namespace
 
-hipError_t launch_backward16(const BwdArgs &a, bool f16, int head_dim, int total_q, const int4 *q_items,
+hipError_t launch_backward16(const BwdArgs &a, bool f16, bool alibi, int head_dim, int total_q, const int4 *q_items,
                              const int4 *q_seqinfo, const int32_t *q_count, int q_grid, const int4 *k_items,
                              const int4 *k_seqinfo, const int32_t *k_count, int k_grid, hipStream_t s)
 {
     const int rows = total_q * a.H;
+#define VA_BWD2(TT, DD, AA)                                                                              \
+    do {                                                                                                 \
+        hipLaunchKernelGGL((k_bwd_dq<TT, DD, AA>), dim3(q_grid), dim3(256), 0, s, a, q_items, q_seqinfo, q_count); \
+        hipLaunchKernelGGL((k_bwd_dkdv<TT, DD, AA>), dim3(k_grid), dim3(256), 0, s, a, k_items, k_seqinfo, k_count); \
+    } while (0)
 #define VA_BWD(TT, DD)                                                                                   \
     do {                                                                                                 \
         hipLaunchKernelGGL((k_bwd_dot<TT, DD>), dim3((rows + 256 / (DD / 8) - 1) / (256 / (DD / 8))), dim3(256), 0, s, \
                            (const uint16_t *)a.dout, (const uint16_t *)a.out, a.dvec, rows);          \
-        hipLaunchKernelGGL((k_bwd_dq<TT, DD>), dim3(q_grid), dim3(256), 0, s, a, q_items, q_seqinfo, q_count); \
-        hipLaunchKernelGGL((k_bwd_dkdv<TT, DD>), dim3(k_grid), dim3(256), 0, s, a, k_items, k_seqinfo, k_count); \
+        if (alibi) VA_BWD2(TT, DD, true);                                                                \
+        else VA_BWD2(TT, DD, false);                                                                     \
     } while (0)
     if (f16) {
         if (head_dim == 128) VA_BWD(_Float16, 128);
@@ -799,6 +821,7 @@ hipError_t launch_backward16(const BwdArgs &a, bool f16, int head_dim, int total
         else VA_BWD(__bf16, 64);
     }
 #undef VA_BWD
+#undef VA_BWD2
     return hipGetLastError();
 }
 

@@ -96,6 +96,7 @@ struct BwdArgs {
     int32_t H, Hkv, g;
     int32_t left, right;         // as in AttnArgs
     float scale, scale_log2;
+    const float *alibi;          // [H] slopes or null, as in AttnArgs
 };
 
 // Sliding-window + sparse compressed attention over shared K/V (the
@@ -156,7 +157,7 @@ struct CheckArgs {
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_check(const CheckArgs &c, hipStream_t s);
-hipError_t launch_backward16(const BwdArgs &a, bool f16, int head_dim, int total_q, const int4 *q_items,
+hipError_t launch_backward16(const BwdArgs &a, bool f16, bool alibi, int head_dim, int total_q, const int4 *q_items,
                              const int4 *q_seqinfo, const int32_t *q_count, int q_grid, const int4 *k_items,
                              const int4 *k_seqinfo, const int32_t *k_count, int k_grid, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, bool part_bf16, bool out_bf16, hipStream_t s);
