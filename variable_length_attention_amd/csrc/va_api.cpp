@@ -54,6 +54,7 @@ enum Path { kPathPrefill = 0, kPathDecode = 1, kPathF32 = 2, kPathWindow = 3 };
 
 struct Layout {
     int path = -1;
+    int hpw = 1;                 // prefill: query heads per workgroup
     int n_max = 0;
     int bm = 0, bn = 0;
     long long grid = 0;
@@ -147,6 +148,9 @@ va_status make_layout(const va_problem *p, int paged, Layout &L)
         L.bn = va::kBN;
     } else {
         L.path = kPathPrefill;
+        // GQA groups of a multiple of 4 heads: a workgroup takes 32 rows of
+        // an item for 4 heads (the items stay 128 rows: the same pre-pass)
+        L.hpw = g % 4 == 0 ? 4 : 1;
         L.bm = va::kBM;
         L.bn = va::kBN;
     }
@@ -276,6 +280,7 @@ va::AttnArgs make_args(const Call &c)
     a.scale = p->scale;
     a.scale_log2 = p->scale * va::kLog2e;
     a.item_rows = 0;
+    a.hpw = 1;
     return a;
 }
 
@@ -344,6 +349,7 @@ va_status run(const Call &c, hipStream_t s)
     if ((st = check_pointers(c, L))) return st;
     va::AttnArgs a = make_args(c);
     a.item_rows = L.path == kPathWindow ? L.bm : 0;
+    a.hpw = L.hpw;
     const va::PlanArgs pa = make_plan(c, L, a);
     if (device_check_enabled() && (st = device_check(c, L, s))) return st;
     if (log_enabled())

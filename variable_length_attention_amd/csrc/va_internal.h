@@ -48,6 +48,7 @@ struct AttnArgs {
     int32_t left, right;         // visible keys of query position p: [p-left, p+right]
     float scale, scale_log2;     // scale and scale * log2(e)
     int32_t item_rows;           // sliding-window kernel: query rows per work item
+    int32_t hpw;                 // prefill: query heads per workgroup (1, or 4 of one kv head)
 };
 
 // Sliding-window kernel for 32..64 query heads per kv head: LDS rows of the
