@@ -103,6 +103,17 @@ def test_bf16_prefill_paged_long_queries():
     _check_full(case, "paged prefill")
 
 
+def test_gqa_quarter_items_g16_alibi_sinks_end_aligned():
+    """16 query heads per kv head: each workgroup takes 32 rows of an item for
+    4 heads; with ALiBi, sinks, a window, queries shorter than keys and
+    lengths that leave quarters of an item empty."""
+    spec = W.Spec("quarters_g16", 904, "bf16", 32, 2, 64, ("fixed", [97, 5, 260, 33]), window=(70, 2),
+                  sinks=True)
+    case = W.make_case(spec, lens_q=[97, 5, 260, 33], lens_k=[300, 5, 400, 33])
+    case["alibi"] = (2.0 ** (-8.0 * np.arange(1, 33) / 32)).astype(np.float32)
+    _check_full(case, "GQA quarter items, g = 16, ALiBi, sinks")
+
+
 def test_out_variant_bitwise_equals_allocating_variant():
     import variable_length_attention_amd as va
     for spec in (W.scaled(W.config(2), B=5, max_len=400), W.config(1),
