@@ -73,8 +73,9 @@ extern "C" {
 
 /* 1: forward, plan, backward.  2: adds VA_F16, va_problem.alibi_slopes,
  * varlen_attn_merge and varlen_attn_sparse_sharedkv (version 1 structs are
- * still accepted). */
-#define VARLEN_ATTN_ABI_VERSION 2
+ * still accepted).  3: adds varlen_attn_bwd_sinks (+ its workspace size);
+ * varlen_attn_bwd takes fp16 and alibi_slopes. */
+#define VARLEN_ATTN_ABI_VERSION 3
 
 typedef enum {
     VA_OK = 0,
@@ -203,6 +204,27 @@ va_status varlen_attn_bwd(const va_problem *p, const void *dout, const void *q, 
                           const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, void *dq,
                           void *dk, void *dv, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/* Gradient of the sink logits (bf16 or fp16 forward, D in {64, 128}).  The
+ * sink of head h is one more logit s_h of every query row's softmax with a
+ * zero value row (SparseAttnSharedkv README, sinks parameter), so
+ *   dsinks[h] = - sum_i exp(sinks[h] - lse[i][h]) * sum_d dout[i][h][d] out[i][h][d]
+ * over all query rows i (the chain rule through the softmax; dq, dk, dv are
+ * the ones varlen_attn_bwd writes, which the sinks enter only through lse).
+ *   dout, out   [total_q, H, D] in p->dtype (out and lse from the forward
+ *               call that had these sinks)
+ *   lse         float32 [total_q, H];  sinks  float32 [H]
+ *   dsinks      float32 [H], overwritten; summed in a fixed order, so the
+ *               result is the same on every run
+ * p is validated as for the forward; only its dtype, total_q, num_heads
+ * and head_dim shape the work (the masks enter through out and lse).  `workspace` holds at least
+ * varlen_attn_bwd_sinks_workspace_size(p) bytes (0 for an invalid p).  Same
+ * ownership, stream and error rules as the forward; dsinks may not overlap
+ * an input or the workspace. */
+size_t varlen_attn_bwd_sinks_workspace_size(const va_problem *p);
+va_status varlen_attn_bwd_sinks(const va_problem *p, const void *dout, const void *out, const float *lse,
+                                const float *sinks, float *dsinks, void *workspace, size_t workspace_bytes,
+                                void *stream);
 
 /* Merge of partial attention results computed over disjoint key sets of
  * the same queries: the local step of ring / context-parallel attention,

@@ -15,6 +15,8 @@ which holds no attention arithmetic.
   (sequence, head, 64-row) units.
 * ``brute.dense_forward`` -- an independent dense numpy checker for small
   inputs (full score matrix, boolean mask, ``scipy.special.logsumexp``).
+* ``sink_grad`` -- the gradient of the sink logits (the softmax chain rule
+  for one more logit with a zero value row), written out in float64.
 * ``merge`` -- the log-sum-exp merge of partial results over disjoint key
   sets (the combine step of ring / context-parallel attention that the
   vllm-omni Ulysses wrapper's ring path needs), written out in float64.
@@ -182,6 +184,21 @@ def backward(case: dict, dout, out, lse, nthreads: int | None = None):
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
     return dq, dk, dv
+
+
+def sink_grad(case: dict, dout, out, lse):
+    """Gradient of sum(dout * O) with respect to the sink logits.  The sink of
+    head h is one more logit of every query row's softmax whose value row is
+    zero (SparseAttnSharedkv README, sinks parameter), so by the softmax's
+    chain rule its dS term is exp(s_h - lse_i) (0 - sum_d dout_i,d O_i,d), and
+    dsinks_h is the sum of those terms over every query row.  out and lse are
+    the forward's (with the sinks); returns float64 [H]."""
+    H = case["H"]
+    d_vec = np.einsum("thd,thd->th", np.asarray(dout, np.float64), np.asarray(out, np.float64))
+    lse64 = np.asarray(lse, np.float64)
+    s = np.asarray(case["sinks"], np.float64)[None, :]
+    p_sink = np.where(np.isneginf(lse64), 0.0, np.exp(s - lse64))
+    return -(p_sink * d_vec).sum(axis=0).reshape(H)
 
 
 def merge(o_parts, lse_parts, sinks=None):

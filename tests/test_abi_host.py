@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.varlen_attn_abi_version() == 2
+    assert lib.varlen_attn_abi_version() == 3
 
 
 def test_problem_struct_matches_header(tmp_path):
@@ -276,3 +276,23 @@ def test_sparse_rejects_before_launching():
     assert _sparse(out=A[1]) == 5                     # out aliases the original cache
     assert _sparse(lse=ctypes.c_void_p(A[8].value + 64)) == 5  # lse inside out
     assert _sparse(scale=0.0) == 4
+
+
+def test_sink_gradient_rejects_before_launching():
+    # fake, never dereferenced addresses: each call fails one host check
+    lib = _lib.load()
+    p = _prob()
+    need = lib.varlen_attn_bwd_sinks_workspace_size(ctypes.byref(p))
+    assert need >= 100 * 8 * 4                                          # one float per (row, head)
+    assert lib.varlen_attn_bwd_sinks_workspace_size(ctypes.byref(_prob(dtype=0))) == 0
+
+    def call(p, dout=A[0], out=A[1], lse=A[2], sinks=A[3], dsinks=A[4], ws=A[5], ws_bytes=1 << 20):
+        return lib.varlen_attn_bwd_sinks(ctypes.byref(p), dout, out, lse, sinks, dsinks, ws,
+                                         ctypes.c_size_t(ws_bytes), None)
+    assert call(_prob(dtype=0)) == 4                                    # float32: unsupported
+    assert call(_prob(head_dim=96)) == 4
+    assert call(p, sinks=None) == 1
+    assert call(p, dsinks=None) == 1
+    assert call(p, ws_bytes=64) == 7
+    assert call(p, out=ctypes.c_void_p(A[1].value + 8)) == 6            # not 16-byte aligned
+    assert call(p, dsinks=ctypes.c_void_p(A[2].value + 16)) == 5        # dsinks inside lse

@@ -185,3 +185,27 @@ def test_backward_alibi_f16_window_end_aligned_d64():
     case = W.make_case(spec, lens_q=[120, 33, 200], lens_k=[300, 33, 210])
     case["alibi"] = _slopes(case["H"])
     _check(case, "alibi f16 two-sided window, sinks, end-aligned, d64")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_sink_gradient(dtype):
+    """dsinks from the forward's out / lse against the oracle's sink gradient
+    (same bound as the other gradients, relative to max |ref|), and the same
+    bits on a second run (fixed-order sums)."""
+    import variable_length_attention_amd as va
+    spec = W.scaled(W.config(4), B=3, max_len=500, seed=W.config(4).seed + 700)
+    spec = dataclasses.replace(spec, dtype=dtype, name=spec.name + "_" + dtype)
+    case = W.make_case(spec)
+    announce(f"sink gradient {dtype}")
+    out, lse = run_case(case, torch)
+    dout_bits = _dout(case, seed=101)
+    dout, sinks = dev(dout_bits, torch), dev(case["sinks"], torch)
+    g1 = va.varlen_attn_bwd_sinks(dout, out, lse, sinks)
+    g2 = va.varlen_attn_bwd_sinks(dout, out, lse, sinks)
+    torch.cuda.synchronize()
+    assert torch.equal(g1, g2)
+    ref = oracle.sink_grad(case, _dout_f64(case, dout_bits), to_f64(out), to_f64(lse))
+    got = g1.double().cpu().numpy()
+    err = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
+    announce(f"sink gradient {dtype}: relative error {err:.2e}")
+    assert err <= REL_TOL[dtype]

@@ -26,6 +26,7 @@ EXPORTED = [
     "varlen_attn_fwd_paged", "varlen_attn_free", "varlen_attn_plan", "varlen_attn_path",
     "varlen_attn_last_error", "varlen_attn_abi_version", "varlen_attn_bwd_workspace_size",
     "varlen_attn_bwd", "varlen_attn_merge", "varlen_attn_sparse_sharedkv",
+    "varlen_attn_bwd_sinks_workspace_size", "varlen_attn_bwd_sinks",
 ]
 
 
@@ -92,6 +93,10 @@ def load():
         lib.varlen_attn_bwd_workspace_size.restype = ctypes.c_size_t
         lib.varlen_attn_bwd.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, vp]
         lib.varlen_attn_bwd.restype = ctypes.c_int
+        lib.varlen_attn_bwd_sinks_workspace_size.argtypes = [P]
+        lib.varlen_attn_bwd_sinks_workspace_size.restype = ctypes.c_size_t
+        lib.varlen_attn_bwd_sinks.argtypes = [P] + [vp] * 6 + [ctypes.c_size_t, vp]
+        lib.varlen_attn_bwd_sinks.restype = ctypes.c_int
         i32 = ctypes.c_int32
         lib.varlen_attn_merge.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp]
         lib.varlen_attn_merge.restype = ctypes.c_int

@@ -13,7 +13,9 @@ request "[varlen_attn for inference] add out variant"):
                      README, PageAttention constraints)
   varlen_attn_fwd    the library-allocating C entry point, results copied
                      into torch tensors (for ABI tests)
-  varlen_attn_bwd    backward (dq, dk, dv) for bf16 contiguous K/V
+  varlen_attn_bwd    backward (dq, dk, dv) for bf16 / fp16 contiguous K/V
+  varlen_attn_bwd_sinks
+                     gradient of the per-head sink logits
   varlen_attn_merge  merge of partial results over disjoint key sets
                      through their log-sum-exp (ring / context parallel)
   varlen_attn_sparse_sharedkv
@@ -31,7 +33,7 @@ import torch
 from . import _lib
 
 __all__ = ["varlen_attn", "varlen_attn_out", "varlen_attn_paged", "varlen_attn_fwd", "varlen_attn_bwd",
-           "bwd_workspace_size", "varlen_attn_merge", "varlen_attn_sparse_sharedkv",
+           "bwd_workspace_size", "varlen_attn_bwd_sinks", "varlen_attn_merge", "varlen_attn_sparse_sharedkv",
            "workspace_size", "plan", "kernel_path", "output_shapes", "make_problem"]
 
 _DTYPES = {torch.float32: _lib.VA_F32, torch.bfloat16: _lib.VA_BF16, torch.float16: _lib.VA_F16}
@@ -273,6 +275,30 @@ def varlen_attn_bwd(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seq
         _stream(dev))
     _lib.check(st)
     return dq, dk, dv
+
+
+def varlen_attn_bwd_sinks(dout, out, lse, sinks, *, dsinks=None, workspace=None):
+    """Gradient of the per-head sink logits of a forward call (bf16 / fp16):
+    dsinks[h] = -sum_i exp(sinks[h] - lse[i, h]) * sum_d dout[i, h, d] out[i, h, d].
+    Returns dsinks (float32 [num_heads]; allocated when not given)."""
+    dev = _check_tensors(dout, out, lse, sinks, dsinks, workspace)
+    _need(dout.dim() == 3 and out.shape == dout.shape and out.dtype == dout.dtype,
+          "dout and out must be [total_q, num_heads, head_dim] of one dtype")
+    _need(lse.dtype == torch.float32 and tuple(lse.shape) == (out.shape[0], out.shape[1]),
+          "lse must be float32 [total_q, num_heads]")
+    _need(sinks.dtype == torch.float32 and sinks.numel() == out.shape[1], "sinks must be float32 [num_heads]")
+    dsinks = torch.empty_like(sinks) if dsinks is None else dsinks
+    _need(dsinks.dtype == torch.float32 and dsinks.numel() == out.shape[1], "dsinks must be float32 [num_heads]")
+    p = make_problem(out, 1, 1, 1, 1, 0, None, False, (-1, -1))
+    p.num_kv_heads = p.num_heads
+    need = int(_lib.load().varlen_attn_bwd_sinks_workspace_size(ctypes.byref(p)))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = _lib.load().varlen_attn_bwd_sinks(ctypes.byref(p), _ptr(dout), _ptr(out), _ptr(lse), _ptr(sinks),
+                                           _ptr(dsinks), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                           _stream(dev))
+    _lib.check(st)
+    return dsinks
 
 
 def varlen_attn_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, sinks: Optional[torch.Tensor] = None,

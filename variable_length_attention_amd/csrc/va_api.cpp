@@ -464,6 +464,44 @@ size_t varlen_attn_bwd_workspace_size(const va_problem *p)
     return L.total;
 }
 
+size_t varlen_attn_bwd_sinks_workspace_size(const va_problem *p)
+{
+    if (check_problem(p, 0)) return 0;
+    if (p->dtype != VA_BF16 && p->dtype != VA_F16) return 0;
+    return align_up((size_t)p->total_q * p->num_heads * 4, 256);
+}
+
+va_status varlen_attn_bwd_sinks(const va_problem *p, const void *dout, const void *out, const float *lse,
+                                const float *sinks, float *dsinks, void *workspace, size_t workspace_bytes,
+                                void *stream)
+{
+    va_status st = check_problem(p, 0);
+    if (st) return st;
+    if (p->dtype != VA_BF16 && p->dtype != VA_F16)
+        return fail(VA_ERR_UNSUPPORTED, "the sink gradient takes bf16 or fp16 inputs");
+    if (!dout || !out || !lse || !sinks || !dsinks)
+        return fail(VA_ERR_NULL, "dout, out, lse, sinks and dsinks must be non-NULL");
+    const size_t need = varlen_attn_bwd_sinks_workspace_size(p);
+    if (!workspace || workspace_bytes < need)
+        return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes,
+                    need);
+    if (!aligned(dout, 16) || !aligned(out, 16) || !aligned(workspace, 16))
+        return fail(VA_ERR_ALIGN, "dout, out and the workspace must be 16-byte aligned");
+    if (!aligned(lse, 4) || !aligned(sinks, 4) || !aligned(dsinks, 4))
+        return fail(VA_ERR_ALIGN, "lse, sinks and dsinks must be 4-byte aligned");
+    const size_t rows = (size_t)p->total_q * p->num_heads;
+    const Range o{dsinks, 4 * (size_t)p->num_heads};
+    const Range ins[] = {{dout, rows * p->head_dim * 2}, {out, rows * p->head_dim * 2}, {lse, rows * 4},
+                         {sinks, 4 * (size_t)p->num_heads}, {workspace, workspace_bytes}};
+    for (const Range &r : ins)
+        if (overlaps(o, r)) return fail(VA_ERR_ALIAS, "dsinks must not overlap an input or the workspace");
+    const hipError_t e = va::launch_sink_grad16(dout, out, lse, sinks, dsinks, (float *)workspace,
+                                                p->dtype == VA_F16, p->head_dim, p->total_q, p->num_heads,
+                                                (hipStream_t)stream);
+    if (e != hipSuccess) return fail(VA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return VA_OK;
+}
+
 va_status varlen_attn_bwd(const va_problem *p, const void *dout, const void *q, const void *k,
                           const void *v, const void *out, const float *lse,
                           const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, void *dq,

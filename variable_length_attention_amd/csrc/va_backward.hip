@@ -189,6 +189,56 @@ __global__ __launch_bounds__(256) void k_bwd_dot(const uint16_t *__restrict__ do
     if (l == 0 && r < rows) dvec[r] = acc;
 }
 
+// ------------------------------------------------------------------ B3
+// Gradient of the sink logits.  The sink of head h enters row i's softmax as
+// one more logit s_h with a zero value row, so its dS term is
+// P_sink (0 - Dv_i) with P_sink = exp(s_h - lse_i), and
+//   dsinks_h = - sum_i exp(s_h - lse_i) sum_d dO_i,d O_i,d.
+// Step 1: the term of every (row, head), into the workspace.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_bwd_sink_terms(const uint16_t *__restrict__ dout,
+                                                        const uint16_t *__restrict__ out, const float *__restrict__ lse,
+                                                        const float *__restrict__ sinks, float *__restrict__ terms,
+                                                        int rows, int H)
+{
+    using E = Elt<T>;
+    constexpr int LPR = D / 8;        // lanes per (row, head), 16 bytes each
+    constexpr int RPB = 256 / LPR;    // (row, head) pairs per workgroup
+    const int r = blockIdx.x * RPB + threadIdx.x / LPR;
+    const int l = threadIdx.x % LPR;
+    float acc = 0.f;
+    if (r < rows) {
+        const u32x4 x = *(const u32x4 *)(dout + (size_t)r * D + l * 8);
+        const u32x4 y = *(const u32x4 *)(out + (size_t)r * D + l * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc += E::lo(x[e]) * E::lo(y[e]) + E::hi(x[e]) * E::hi(y[e]);
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (l == 0 && r < rows) {
+        const float ls = lse[r];
+        terms[r] = ls == -INFINITY ? 0.f : __expf(sinks[r % H] - ls) * acc;
+    }
+}
+
+// Step 2: one workgroup per head sums its terms in a fixed order
+// (deterministic): strided partial sums, then a tree in LDS.
+__global__ __launch_bounds__(256) void k_bwd_sink_sum(const float *__restrict__ terms, float *__restrict__ dsinks,
+                                                      int T, int H)
+{
+    __shared__ float part[256];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    float acc = 0.f;
+    for (int i = tid; i < T; i += 256) acc += terms[(size_t)i * H + h];
+    part[tid] = acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) part[tid] += part[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) dsinks[h] = -part[0];
+}
+
 // ------------------------------------------------------------------ B1
 template <typename T, int D, bool ALIBI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dq(
@@ -795,6 +845,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 }  // namespace
+
+hipError_t launch_sink_grad16(const void *dout, const void *out, const float *lse, const float *sinks, float *dsinks,
+                              float *terms, bool f16, int head_dim, int total_q, int H, hipStream_t s)
+{
+    const int rows = total_q * H;
+#define VA_SG(TT, DD)                                                                                       \
+    hipLaunchKernelGGL((k_bwd_sink_terms<TT, DD>), dim3((rows + 256 / (DD / 8) - 1) / (256 / (DD / 8))), dim3(256), 0, \
+                       s, (const uint16_t *)dout, (const uint16_t *)out, lse, sinks, terms, rows, H)
+    if (f16) {
+        if (head_dim == 128) VA_SG(_Float16, 128);
+        else VA_SG(_Float16, 64);
+    } else {
+        if (head_dim == 128) VA_SG(__bf16, 128);
+        else VA_SG(__bf16, 64);
+    }
+#undef VA_SG
+    hipLaunchKernelGGL(k_bwd_sink_sum, dim3(H), dim3(256), 0, s, terms, dsinks, total_q, H);
+    return hipGetLastError();
+}
 
 hipError_t launch_backward16(const BwdArgs &a, bool f16, bool alibi, int head_dim, int total_q, const int4 *q_items,
                              const int4 *q_seqinfo, const int32_t *q_count, int q_grid, const int4 *k_items,

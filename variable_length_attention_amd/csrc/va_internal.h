@@ -161,6 +161,8 @@ hipError_t launch_check(const CheckArgs &c, hipStream_t s);
 hipError_t launch_backward16(const BwdArgs &a, bool f16, bool alibi, int head_dim, int total_q, const int4 *q_items,
                              const int4 *q_seqinfo, const int32_t *q_count, int q_grid, const int4 *k_items,
                              const int4 *k_seqinfo, const int32_t *k_count, int k_grid, hipStream_t s);
+hipError_t launch_sink_grad16(const void *dout, const void *out, const float *lse, const float *sinks, float *dsinks,
+                              float *terms, bool f16, int head_dim, int total_q, int H, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, bool part_bf16, bool out_bf16, hipStream_t s);
 hipError_t launch_sparse16(const SparseArgs &a, bool f16, int head_dim, hipStream_t s);
 hipError_t launch_window16(const AttnArgs &a, bool f16, int head_dim, bool paged, const int4 *items,
