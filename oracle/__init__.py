@@ -15,6 +15,8 @@ which holds no attention arithmetic.
   (sequence, head, 64-row) units.
 * ``brute.dense_forward`` -- an independent dense numpy checker for small
   inputs (full score matrix, boolean mask, ``scipy.special.logsumexp``).
+* ``backward_sampled`` -- the backward's definitions at chosen dq rows and
+  dk / dv keys (numpy, float64), for workloads too large for ``backward``.
 * ``sink_grad`` -- the gradient of the sink logits (the softmax chain rule
   for one more logit with a zero value row), written out in float64.
 * ``merge`` -- the log-sum-exp merge of partial results over disjoint key
@@ -183,6 +185,87 @@ def backward(case: dict, dout, out, lse, nthreads: int | None = None):
                                nthreads or default_threads())
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
+    return dq, dk, dv
+
+
+def _wide(a, dtype):
+    return _widen16(a, dtype) if dtype in ("bf16", "f16") else np.asarray(a, np.float64)
+
+
+def _key_range(i, delta, Lk, case):
+    """Visible keys [lo, hi] of query row i (p = i + delta): [p - left,
+    p + right] within [0, Lk), with causal capping the right side at p and
+    -1 meaning unbounded."""
+    p = i + delta
+    lo = 0 if case["window_left"] < 0 else max(0, p - case["window_left"])
+    right = 0 if case["causal"] else case["window_right"]
+    hi = Lk - 1 if right < 0 else min(Lk - 1, p + right)
+    return lo, hi
+
+
+def backward_sampled(case: dict, dout, out, lse, rows, keys):
+    """The backward's definitions evaluated at chosen outputs only (for
+    workloads too large for ``backward``): dq at query (token, head) pairs
+    ``rows`` and dk, dv at key (token, kv head) pairs ``keys``.  With
+    P_ij = exp(s_ij - lse_i), s_ij = scale <q_i, k_j> (+ ALiBi bias),
+    Dv_i = <dout_i, out_i>, dS_ij = P_ij (<dout_i, v_j> - Dv_i):
+    dq_i = scale sum_j dS_ij k_j over the keys row i sees; dk_j = scale
+    sum_{i, h} dS_ij q_i and dv_j = sum_{i, h} P_ij dout_i over the rows and
+    query heads of the kv head that see key j (the gradients the boostr CPU
+    backward ``varlen_attention_bwd`` accumulates, here per output element).
+    Contiguous K/V; float64."""
+    if case.get("paged"):
+        raise ValueError("the backward oracle takes contiguous K/V")
+    dt, H, Hkv = case["dtype"], case["H"], case["Hkv"]
+    g = H // Hkv
+    cu_q, cu_k = np.asarray(case["cu_q"], np.int64), np.asarray(case["cu_k"], np.int64)
+    q, k, v = (np.asarray(case[x]) for x in ("q", "k", "v"))
+    dout, out, lse = (np.asarray(x) for x in (dout, out, lse))   # widened where read
+    alibi = case.get("alibi")
+    sc = float(case["scale"])
+
+    def scores(qv, kv, h, p, js):
+        s = sc * (kv @ qv)
+        if alibi is not None:
+            s = s - float(alibi[h]) * np.abs(p - js)
+        return s
+
+    dq = np.zeros((len(rows[0]), case["D"]))
+    for n, (t, h) in enumerate(zip(*rows)):
+        b = int(np.searchsorted(cu_q, t, side="right") - 1)
+        i, Lq, Lk = t - cu_q[b], cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        lo, hi = _key_range(i, Lk - Lq, Lk, case)
+        if hi < lo:
+            continue
+        js = np.arange(lo, hi + 1)
+        c = h // g
+        kb = _wide(k[cu_k[b] + js, c], dt)
+        vb = _wide(v[cu_k[b] + js, c], dt)
+        do_t, o_t = dout[t, h].astype(np.float64), out[t, h].astype(np.float64)
+        pr = np.exp(scores(_wide(q[t, h], dt), kb, h, i + Lk - Lq, js) - float(lse[t, h]))
+        ds = pr * (vb @ do_t - do_t @ o_t)
+        dq[n] = sc * (ds @ kb)
+    dk = np.zeros((len(keys[0]), case["D"]))
+    dv = np.zeros_like(dk)
+    for n, (u, c) in enumerate(zip(*keys)):
+        b = int(np.searchsorted(cu_k, u, side="right") - 1)
+        j, Lq, Lk = u - cu_k[b], cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        bounds = [_key_range(i, Lk - Lq, Lk, case) for i in range(Lq)]
+        ii = np.array([i for i, (lo, hi) in enumerate(bounds) if lo <= j <= hi], np.int64)
+        if ii.size == 0:
+            continue
+        kj, vj = _wide(k[u, c], dt), _wide(v[u, c], dt)
+        for h in range(c * g, (c + 1) * g):
+            t = cu_q[b] + ii
+            qh = _wide(q[t, h], dt)
+            s = sc * (qh @ kj)
+            if alibi is not None:
+                s = s - float(alibi[h]) * np.abs(ii + Lk - Lq - j)
+            do_t, o_t = dout[t, h].astype(np.float64), out[t, h].astype(np.float64)
+            pr = np.exp(s - lse[t, h].astype(np.float64))
+            ds = pr * (do_t @ vj - np.sum(do_t * o_t, axis=1))
+            dk[n] += sc * (ds @ qh)
+            dv[n] += pr @ do_t
     return dq, dk, dv
 
 

@@ -24,7 +24,7 @@ import pytest
 
 import oracle
 import workloads as W
-from helpers import announce, dev, run_case, to_f64
+from helpers import announce, dev, run_case, sample_pairs, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -209,3 +209,48 @@ def test_sink_gradient(dtype):
     err = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
     announce(f"sink gradient {dtype}: relative error {err:.2e}")
     assert err <= REL_TOL[dtype]
+
+
+def test_backward_full_size_causal_gqa_prefill_sampled():
+    """The benchmark's backward workload at full size (16 sequences of 128 to
+    4096 tokens, 32 query heads on 8 kv heads, d128, causal) in the
+    benchmark's launch configuration (preallocated dq / dk / dv and
+    workspace): dq on sampled (token, head) pairs and dk, dv on sampled
+    (key, kv head) pairs against the oracle's per-output evaluation, with
+    the scaled tests' bound taken relative to the sample's largest gradient
+    element; every element finite."""
+    import variable_length_attention_amd as va
+    case = W.make_case(W.config(2))
+    announce("backward full size: forward")
+    out, lse = run_case(case, torch)
+    dout_bits = _dout(case, seed=123)
+    q, k, v = dev(case["q"], torch), dev(case["k"], torch), dev(case["v"], torch)
+    cu_q, cu_k = dev(case["cu_q"], torch), dev(case["cu_k"], torch)
+    win = (case["window_left"], case["window_right"])
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    prob = va.make_problem(q, k.shape[1], k.shape[0], case["B"], case["max_q"], case["max_k"], case["scale"],
+                           case["causal"], win)
+    ws = torch.empty(va.bwd_workspace_size(prob), dtype=torch.uint8, device="cuda")
+    announce("backward full size: running")
+    va.varlen_attn_bwd(dev(dout_bits, torch), q, k, v, out, lse, cu_q, cu_k, case["max_q"], case["max_k"],
+                       scale=case["scale"], causal=case["causal"], window=win, dq=dq, dk=dk, dv=dv, workspace=ws)
+    torch.cuda.synchronize()
+    for nm, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(x).all()), f"{nm} has non-finite values"
+    toks, heads = sample_pairs(case, 64, seed=5)
+    rng = np.random.default_rng(6)
+    T_k = int(case["cu_k"][-1])
+    ktoks = np.concatenate([rng.integers(0, T_k, 64), case["cu_k"][:-1], case["cu_k"][1:] - 1]).astype(np.int64)
+    kheads = rng.integers(0, case["Hkv"], len(ktoks))
+    announce(f"backward full size: oracle on {len(toks)} rows and {len(ktoks)} keys")
+    ref = oracle.backward_sampled(case, W.bf16_bits_to_f32(dout_bits), out.float().cpu().numpy(),
+                                  lse.cpu().numpy(),
+                                  (toks, heads), (ktoks, kheads))
+    got = (dq[torch.from_numpy(toks).cuda(), torch.from_numpy(heads).cuda()],
+           dk[torch.from_numpy(ktoks).cuda(), torch.from_numpy(kheads).cuda()],
+           dv[torch.from_numpy(ktoks).cuda(), torch.from_numpy(kheads).cuda()])
+    for nm, g, r in zip(("dq", "dk", "dv"), got, ref):
+        scale = max(np.abs(r).max(), 1e-30)
+        err = np.abs(to_f64(g) - r).max() / scale
+        announce(f"backward full size {nm}: max error {err:.2e} of max |ref| {scale:.3e}")
+        assert err <= REL_TOL["bf16"], f"{nm} max error {err:.3e} of max |ref| {scale:.3e}"
