@@ -542,8 +542,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     const size_t qstride = (size_t)a.H * D * 2;
     const int qtiles = (qhi - qlo + QT - 1) / QT;
-    const int total = qtiles * a.g;  // (head of the group, query tile) steps
-    // step s: head c g + s / qtiles, query rows qlo + QT (s % qtiles) ..
+    const int total = qtiles * a.g;  // (query tile, head of the group) steps
+    // step s: query rows qlo + QT (qtiles - 1 - s / g) .., head c g + s % g:
+    // the g heads of one tile in a row (their rows are adjacent in memory),
+    // tiles from the last one down (measured 2-3% faster than head-major
+    // ascending order on a causal GQA workload)
     // step s: copies of its Q / dO tiles into slot `slot`; its per-row lse
     // (log2 units; +inf for rows past the range or without keys) and Dv are
     // read into registers here and written to LDS by row_store() at the end
@@ -551,8 +554,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float st_l2 = INFINITY, st_dv = 0.f;
     // ALiBi slope (log2 units) of the next step's head and of this step's
     float sl_next = 0.f, sl_cur = 0.f;
-    auto tile_row = [&](int s) { return qlo + (s % qtiles) * QT; };
-    auto tile_head = [&](int s) { return c * a.g + s / qtiles; };
+    auto tile_row = [&](int s) { return qlo + (qtiles - 1 - s / a.g) * QT; };
+    auto tile_head = [&](int s) { return c * a.g + s % a.g; };
     // copies of step s's tiles: KS parts of one 16-byte-per-lane copy each
     // (Q rows, then dO rows), issued one at a time between the matrix
     // instructions of the previous step; with no step s the buffers are
