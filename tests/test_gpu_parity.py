@@ -238,6 +238,40 @@ def test_single_key_rows_are_value_rows_bitwise():
             np.testing.assert_array_equal(o[t, h], case["v"][t, h // g])
 
 
+def test_key_range_beyond_4gib_per_kv_array():
+    """One sequence whose K and V arrays each hold more than 4 GiB (300000
+    keys x 64 kv heads x d128 in bf16), non-causal, 32 query rows on the
+    prefill kernel.  Buffer descriptors hold 32-bit byte counts, so for K/V
+    spans of 2 GiB and more the host selects the kernel's 64-bit-address
+    load mode; this is the only test at that size.  Closed form: K = 0 makes
+    every score 0, so O is the mean of V over all keys and LSE = ln(Lk); V is
+    1 on a set of rows (every 997th row plus the rows around key
+    Lk - 2^32 / row_bytes) and 0 elsewhere, so O = |set| / Lk."""
+    import variable_length_attention_amd as va
+    from variable_length_attention_amd import api
+    Lk, Tq, H, D = 300000, 32, 64, 128
+    row_bytes = H * D * 2
+    edge = Lk - (1 << 32) // row_bytes
+    ones = np.zeros(Lk, bool)
+    ones[::997] = True
+    ones[edge - 100:edge + 100] = True
+    announce(f"long key range: {Lk} keys x {H} kv heads (K, V {Lk * row_bytes / 2**30:.2f} GiB each)")
+    q = torch.randn((Tq, H, D), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).cuda()
+    k = torch.zeros((Lk, H, D), dtype=torch.bfloat16, device="cuda")
+    v = torch.from_numpy(ones.astype(np.float32)).to(torch.bfloat16).cuda()[:, None, None].expand(Lk, H, D).contiguous()
+    cu_q = torch.tensor([0, Tq], dtype=torch.int32, device="cuda")
+    cu_k = torch.tensor([0, Lk], dtype=torch.int32, device="cuda")
+    p = api.make_problem(q, H, Lk, 1, Tq, Lk, 0.088, False, (-1, -1))
+    assert api.kernel_path(p, False) == 0, "this shape takes the prefill kernel"
+    out, lse = va.varlen_attn(q, k, v, cu_q, cu_k, Tq, Lk, scale=0.088, return_lse=True)
+    torch.cuda.synchronize()
+    want = ones.sum() / Lk
+    o = out.float().cpu().numpy()
+    assert np.all(np.abs(o - want) <= 2.0 ** -8 * want), f"O range [{o.min()}, {o.max()}], want {want}"
+    np.testing.assert_allclose(lse.cpu().numpy(), np.log(Lk), rtol=0, atol=1e-4)
+    del k, v
+
+
 def test_empty_rows_and_sink_only_rows():
     """More queries than keys with causal end alignment: leading rows see no
     key (O = 0, LSE = -inf); with sinks they see only the sink (O = 0,

@@ -241,12 +241,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // tile past the end (t >= ntiles) is harmless: buffer mode reads an
     // empty range (zeros), the other modes re-read the last row; the
     // destination slot is a free one either way.
-    // buffer mode: raw buffer over rows j0 .. kv_hi-1 of tile t (reads past
-    // the end return 0)
+    // buffer mode: raw buffer over rows j0 .. min(kv_hi, j0 + BN) - 1 of tile
+    // t (reads past the end return 0; at most BN rows, so the 32-bit byte
+    // count cannot wrap for long key ranges)
     auto tile_rsrc = [&](int t, bool is_v) -> u32x4 {
         const int j0 = kv_lo + t * BN;
         const char *seq = is_v ? vseq : kseq;
-        const uint32_t nrec = j0 < kv_hi ? (uint32_t)((kv_hi - j0) * rowstride) : 0u;
+        const uint32_t nrec = j0 < kv_hi ? (uint32_t)(min(kv_hi - j0, BN) * rowstride) : 0u;
         const uint64_t addr = (uint64_t)(uintptr_t)(seq + j0 * rowstride);
         return u32x4{(uint32_t)addr, (uint32_t)(addr >> 32) & 0xffffu, nrec, 0x00020000u};
     };
