@@ -540,6 +540,7 @@ va_status varlen_attn_bwd(const va_problem *p, const void *dout, const void *q, 
     a.dvec = (float *)(ws + L.dvec);
     a.dq = dq; a.dk = dk; a.dv = dv;
     a.H = p->num_heads; a.Hkv = p->num_kv_heads; a.g = p->num_heads / p->num_kv_heads;
+    a.hpw = a.g % 4 == 0 ? 4 : 1;
     a.left = p->window_left >= 0 ? p->window_left : va::kInfOff;
     if (p->causal) a.right = 0;
     else a.right = p->window_right >= 0 ? p->window_right : va::kInfOff;

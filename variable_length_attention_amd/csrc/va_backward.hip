@@ -258,28 +258,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     char *const kring = (char *)smem;
     char *const vring = kring + 2 * TILEB;
 
-    int item, head;
-    map_block(blockIdx.x, a.H, item, head);
+    // a.hpw == 1: the item's 128 query rows of one head (32 per wave).
+    // a.hpw == 4: a quarter of the item (32 rows) for 4 heads that share a kv
+    // head (one head per wave): the waves see the same keys, so none of them
+    // waits through tiles only another wave's rows need.
+    int item, slot;
+    map_block(blockIdx.x, a.H, item, slot);
     const int n_items = *count;
     const int4 it = items[item];
     const int4 si = seqinfo[item];
     asm volatile("" ::"s"(it.x), "s"(si.x), "s"(n_items));
     if (item >= n_items) return;
-    const int i0 = it.y, kv_lo = it.z, kv_hi = it.w;
+    int i0 = it.y, kv_lo = it.z, kv_hi = it.w;
     const int q0 = si.x, Lq = si.y, k0 = si.z, Lk = si.w;
     const int delta = Lk - Lq;
-    const int c = head / a.g;
+    if (a.hpw != 1) {
+        // this quarter's rows and the union of their visible keys
+        i0 += (slot & 3) * 32;
+        if (i0 >= Lq) return;
+        int l0, h0, l1, h1;
+        row_bounds(i0, delta, Lk, a.left, a.right, l0, h0);
+        row_bounds(min(i0 + 31, Lq - 1), delta, Lk, a.left, a.right, l1, h1);
+        kv_lo = Lk > 0 ? l0 : 0;
+        kv_hi = Lk > 0 ? max(h1 + 1, kv_lo) : 0;
+    }
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, h2 = lane >> 5, l16 = lane & 15, q4 = l16 >> 2;
-    const int row = i0 + wave * 32 + n;
+    const int wrow = a.hpw == 1 ? wave * 32 : 0;  // the wave's first row
+    const int head = a.hpw == 1 ? slot : (slot >> 2) * 4 + wave;
+    const int c = head / a.g;                     // the same for every wave
+    const int row = i0 + wrow + n;
     const bool row_ok = row < Lq;
     int lo = 1, hi = 0;
     if (row_ok) row_bounds(row, delta, Lk, a.left, a.right, lo, hi);
     int wlo = 1, whi = 0, flo = 0x7fffffff, fhi = -1;
     {
-        const int w0 = i0 + wave * 32, w1 = min(w0 + 31, Lq - 1);
+        const int w0 = i0 + wrow, w1 = min(w0 + 31, Lq - 1);
         if (w0 < Lq) {
             int l0, h0, l1, h1;
             row_bounds(w0, delta, Lk, a.left, a.right, l0, h0);
@@ -441,7 +457,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int u = 0; u < 32 / RPW; ++u) {
             const int r = u * RPW + lane / NCH;
-            const int orow = i0 + wave * 32 + r;
+            const int orow = i0 + wrow + r;
             const u32x4 v = *(const u32x4 *)(ow + r * ROWB + ((cidx ^ (r % NCH)) << 4));
             if (orow < Lq)
                 *(u32x4 *)((uint16_t *)a.dq + ((size_t)(q0 + orow) * a.H + head) * D + cidx * 8) = v;

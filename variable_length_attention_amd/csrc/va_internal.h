@@ -98,6 +98,7 @@ struct BwdArgs {
     int32_t left, right;         // as in AttnArgs
     float scale, scale_log2;
     const float *alibi;          // [H] slopes or null, as in AttnArgs
+    int32_t hpw;                 // dQ kernel: query heads per workgroup (1, or 4 of one kv head)
 };
 
 // Sliding-window + sparse compressed attention over shared K/V (the
