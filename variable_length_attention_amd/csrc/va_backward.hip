@@ -570,8 +570,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float st_l2 = INFINITY, st_dv = 0.f;
     // ALiBi slope (log2 units) of the next step's head and of this step's
     float sl_next = 0.f, sl_cur = 0.f;
-    auto tile_row = [&](int s) { return qlo + (qtiles - 1 - s / a.g) * QT; };
-    auto tile_head = [&](int s) { return c * a.g + s % a.g; };
+    // step s = t g + h (t: query tile counted from the last, h: head offset),
+    // tracked as the pair (t, h) so that no step divides by g
+    auto tile_row = [&](int t) { return qlo + (qtiles - 1 - t) * QT; };
     // copies of step s's tiles: KS parts of one 16-byte-per-lane copy each
     // (Q rows, then dO rows), issued one at a time between the matrix
     // instructions of the previous step; with no step s the buffers are
@@ -580,9 +581,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     static_assert(2 * LPW == KS, "one copy part per K step");
     u32x4 rs_q = {0, 0, 0, 0}, rs_o = {0, 0, 0, 0};
     int cp_slot = 0;
-    auto copy_setup = [&](int s, int slot) {
-        const int rows = s < total ? min(qhi - tile_row(s), QT) : 0;
-        const size_t off = s < total ? ((size_t)(q0 + tile_row(s)) * a.H + tile_head(s)) * D * 2 : 0;
+    auto copy_setup = [&](bool valid, int t, int hoff, int slot) {
+        const int rows = valid ? min(qhi - tile_row(t), QT) : 0;
+        const size_t off = valid ? ((size_t)(q0 + tile_row(t)) * a.H + c * a.g + hoff) * D * 2 : 0;
         rs_q = rows_rsrc((const char *)a.q + off, rows, qstride);
         rs_o = rows_rsrc((const char *)a.dout + off, rows, qstride);
         cp_slot = slot;
@@ -594,9 +595,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         char *dst = (part < LPW ? qring : oring) + cp_slot * TILEB + (wave * LPW + u) * 1024;
         copy16_buffer(part < LPW ? rs_q : rs_o, (uint32_t)(r * qstride) + chunk * 16, lds_addr(dst));
     };
-    auto issue = [&](int s, int slot) {
-        const int h = tile_head(s);
-        const int r0 = tile_row(s);
+    auto issue = [&](int t, int hoff) {
+        const int h = c * a.g + hoff;
+        const int r0 = tile_row(t);
         st_l2 = INFINITY;
         st_dv = 0.f;
         if constexpr (ALIBI) sl_next = a.alibi[h] * kLog2e;
@@ -792,7 +793,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
 
     if (total > 0) {
-        copy_setup(0, 0);
+        copy_setup(true, 0, 0, 0);
 #pragma unroll
         for (int part = 0; part < KS; ++part) copy_part(part);
         issue(0, 0);
@@ -801,15 +802,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     wait_vmem();
     __syncthreads();
+    int ct = 0;          // query tile of step s
+    int nt = 0, nh = 1;  // query tile and head offset of step s + 1
+    if (nh == a.g) { nh = 0; nt = 1; }
     for (int s = 0; s < total; ++s) {
         const int slot = s & 1;
         const bool more = s + 1 < total;
-        copy_setup(s + 1, slot ^ 1);
-        if (more) issue(s + 1, slot ^ 1);
-        const int r0 = tile_row(s);
+        copy_setup(more, nt, nh, slot ^ 1);
+        if (more) issue(nt, nh);
+        const int r0 = tile_row(ct);
         step(slot, r0, tile_full(r0));
         if (more) row_store(slot ^ 1);  // the next step's slot is not read in this step
         sl_cur = sl_next;
+        ct = nt;
+        if (++nh == a.g) { nh = 0; ++nt; }
         wait_vmem();
         __syncthreads();
     }
