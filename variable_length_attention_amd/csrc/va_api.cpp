@@ -668,6 +668,11 @@ va_status varlen_attn_sparse_sharedkv(const va_sparse_problem *p, const void *q,
     a.g = p->num_heads / p->num_kv_heads; a.topk = p->topk;
     a.ori_bs = p->ori_block_size; a.ori_stride = p->ori_block_table_stride;
     a.cmp_bs = p->cmp_block_size; a.cmp_stride = p->cmp_block_table_stride; a.cmp_ratio = p->cmp_ratio;
+    a.ori_shift = a.cmp_shift = -1;
+    for (int sh = 0; sh < 31; ++sh) {
+        if ((1 << sh) == a.ori_bs) a.ori_shift = sh;
+        if ((1 << sh) == a.cmp_bs) a.cmp_shift = sh;
+    }
     a.left = p->window_left; a.right = p->window_right;
     a.scale_log2 = p->scale * va::kLog2e;
     // tokens per workgroup: the fewest that keep the grid within whole rounds

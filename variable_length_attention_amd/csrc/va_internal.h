@@ -120,6 +120,7 @@ struct SparseArgs {
     int32_t B, T, H, Hkv, g, topk;
     int32_t tok_per_wg;              // consecutive tokens per workgroup
     int32_t ori_bs, ori_stride, cmp_bs, cmp_stride, cmp_ratio;
+    int32_t ori_shift, cmp_shift;    // log2 of ori_bs / cmp_bs when a power of two, else -1
     int32_t left, right;             // window on the original keys (kInfOff = unbounded)
     float scale_log2;
 };

@@ -228,14 +228,24 @@ void k5_sparse16(SparseArgs a)
                 pos[k] = (idx >= 0 && idx < S3) ? idx : -1;
             }
         }
+        // block and slot of a position: shifts for power-of-two block sizes
+        // (an integer division is a long instruction sequence per key)
+        auto blk_of = [&](int x, bool ori) {
+            const int sh = ori ? a.ori_shift : a.cmp_shift;
+            return sh >= 0 ? x >> sh : x / (ori ? a.ori_bs : a.cmp_bs);
+        };
+        auto slot_of = [&](int x, bool ori) {
+            const int bs = ori ? a.ori_bs : a.cmp_bs;
+            return (ori ? a.ori_shift : a.cmp_shift) >= 0 ? x & (bs - 1) : x % bs;
+        };
         int blk[KPT];
 #pragma unroll
         for (int k = 0; k < KPT; ++k) {
             const int kk = tid + 128 * k;
             blk[k] = 0;
             if (pos[k] >= 0)
-                blk[k] = kk < nwin ? a.ori_table[(size_t)b * a.ori_stride + pos[k] / a.ori_bs]
-                                   : a.cmp_table[(size_t)b * a.cmp_stride + pos[k] / a.cmp_bs];
+                blk[k] = kk < nwin ? a.ori_table[(size_t)b * a.ori_stride + blk_of(pos[k], true)]
+                                   : a.cmp_table[(size_t)b * a.cmp_stride + blk_of(pos[k], false)];
         }
         // entries up to the end of the last tile (-1 past L); whether any
         // key of the token selects nothing decides if its tiles are masked
@@ -245,7 +255,7 @@ void k5_sparse16(SparseArgs a)
             const int kk = tid + 128 * k;
             if (kk < ntiles * BN) {
                 const int bs = kk < nwin ? a.ori_bs : a.cmp_bs;
-                const int row = pos[k] >= 0 ? blk[k] * bs + pos[k] % bs : -1;
+                const int row = pos[k] >= 0 ? blk[k] * bs + slot_of(pos[k], kk < nwin) : -1;
                 s_list[kk] = row;
                 none_here |= row < 0;
             }
