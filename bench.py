@@ -385,6 +385,34 @@ def calibrate_attainable(steps):
     print(json.dumps(res), flush=True)
 
 
+def calibrate_mfma(iters):
+    """Attainable matrix rate: a full-chip stream of 32x32x16 bf16 products
+    (libva_probe.so), with random and with all-zero operands, and with 2..8
+    vector instructions (v_exp_f32 / v_fma_f32) issued after every product,
+    at one and two waves per SIMD.  Reports TFLOP/s, the fraction of the
+    datasheet peak and the shader clock the waves ran at."""
+    import ctypes
+    import torch
+    torch.cuda.init()
+    lib = ctypes.CDLL(os.path.join(ROOT, "variable_length_attention_amd", "libva_probe.so"))
+    d = ctypes.c_double
+    lib.va_probe_mfma_stream.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(d)] * 3
+    lib.va_probe_mfma_stream.restype = ctypes.c_int
+    rows = []
+    cases = [(wps, zero, 0, 0) for wps in (1, 2) for zero in (0, 1)]
+    cases += [(wps, 0, k, op) for wps in (1, 2) for op in (0, 1) for k in (2, 4, 6, 8)]
+    for wps, zero, k, op in cases:
+        ms, tf, mhz = d(), d(), d()
+        rc = lib.va_probe_mfma_stream(wps, iters, zero, k, op, ctypes.byref(ms), ctypes.byref(tf), ctypes.byref(mhz))
+        if rc != 0:
+            raise RuntimeError(f"va_probe_mfma_stream failed: hip error {rc}")
+        rows.append({"waves_per_simd": wps, "data": "zero" if zero else "random",
+                     "valu_per_mfma": k, "valu_op": ("v_exp_f32", "v_fma_f32")[op] if k else None,
+                     "ms": round(ms.value, 4), "tflops": round(tf.value, 1),
+                     "frac_of_peak": round(tf.value / PEAK_BF16_TFLOPS, 4), "shader_mhz": round(mhz.value)})
+        print(json.dumps(rows[-1]), flush=True)
+
+
 # ---------------------------------------------------------------- CPU baseline
 def cpu_baseline(case, budget_s=15.0):
     import oracle
@@ -425,7 +453,12 @@ def main():
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     ap.add_argument("--calibrate-attainable", action="store_true",
                     help="only measure a large bf16 GEMM and a large read-only reduction")
+    ap.add_argument("--calibrate-mfma", type=int, default=0, metavar="ITERS",
+                    help="only run the matrix-core stream probe (ITERS groups of 4 products per wave)")
     args = ap.parse_args()
+    if args.calibrate_mfma:
+        calibrate_mfma(args.calibrate_mfma)
+        return
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, max(1, args.steps))
         return

@@ -1,0 +1,162 @@
+// Attainable-rate probes for the roofline denominators (not part of the
+// attention library; built as libva_probe.so and called by the benchmark).
+//
+// va_probe_mfma_stream: every wave of a full-chip grid runs a stream of
+// v_mfma_f32_32x32x16_bf16 on four independent accumulators (consecutive
+// products use different operands), optionally with K vector instructions
+// (v_exp_f32 or v_fma_f32) issued between products, as an attention
+// softmax interleaves them.  It reports the matrix rate the chip sustains
+// with that data under its power limit, and the shader clock it ran at
+// (s_memtime cycles against the 100 MHz s_memrealtime counter).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t hash32(uint32_t x)
+{
+    x ^= x >> 16; x *= 0x7feb352dU; x ^= x >> 15; x *= 0x846ca68bU; x ^= x >> 16;
+    return x;
+}
+
+// a bf16 pair with random mantissa and sign, exponent near 1 (finite sums)
+__device__ __forceinline__ uint32_t rand_bf16x2(uint32_t s)
+{
+    const uint32_t h = hash32(s);
+    const uint32_t lo = 0x3f00u | (h & 0x807fu), hi = 0x3f00u | ((h >> 16) & 0x807fu);
+    return lo | (hi << 16);
+}
+
+template <int K, int OP>
+__global__ __launch_bounds__(256) void mfma_stream(int iters, int zero, float *sink, unsigned long long *clk)
+{
+    const uint32_t gid = blockIdx.x * 256 + threadIdx.x;
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        u32x4 x, y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            x[r] = zero ? 0u : rand_bf16x2(gid * 64 + j * 8 + r);
+            y[r] = zero ? 0u : rand_bf16x2(gid * 64 + j * 8 + 4 + r + 0x9e3779b9u);
+        }
+        a[j] = __builtin_bit_cast(bf16x8, x);
+        b[j] = __builtin_bit_cast(bf16x8, y);
+    }
+    f32x16 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = 0.001f * (float)(i + (gid & 7));
+    const float f1 = 0.999f, f2 = 0.0001f;
+
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[j]) : "v"(a[j]), "v"(b[j]));
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float &x = e[(j * K + k) & 7];
+                if constexpr (OP == 0) asm volatile("v_exp_f32 %0, %0" : "+v"(x));
+                else asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x) : "v"(f1), "v"(f2));
+            }
+        }
+    }
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s += acc[j][v];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += e[i];
+    sink[gid] = s;
+    if ((threadIdx.x & 63) == 0) {
+        const int w = gid >> 6;
+        clk[2 * w] = t1 - t0;
+        clk[2 * w + 1] = r1 - r0;
+    }
+}
+
+template <int K, int OP>
+void launch(int grid, int iters, int zero, float *sink, unsigned long long *clk, hipStream_t s)
+{
+    hipLaunchKernelGGL((mfma_stream<K, OP>), dim3(grid), dim3(256), 0, s, iters, zero, sink, clk);
+}
+
+}  // namespace
+
+// Runs the stream on the current device: waves_per_simd waves on each SIMD
+// of every compute unit, iters groups of 4 products per wave, K = valu
+// vector instructions (op 0: v_exp_f32, 1: v_fma_f32) after every product.
+// Outputs: kernel time (ms, HIP events), matrix rate (TFLOP/s) and the mean
+// shader clock of the waves (MHz).  Returns 0, or a hipError_t.
+extern "C" int va_probe_mfma_stream(int waves_per_simd, int iters, int zero_data, int valu, int op, double *ms,
+                                    double *tflops, double *mhz)
+{
+    int dev = 0;
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return (int)e;
+    if (waves_per_simd < 1 || waves_per_simd > 8 || iters < 1 || valu < 0 || valu > 8 || (op != 0 && op != 1))
+        return (int)hipErrorInvalidValue;
+    const int grid = prop.multiProcessorCount * waves_per_simd;  // 4 waves per workgroup = one per SIMD
+    const int waves = grid * 4;
+    float *sink = nullptr;
+    unsigned long long *clk = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    void (*fn)(int, int, int, float *, unsigned long long *, hipStream_t) = nullptr;
+    switch (valu * 2 + op) {
+    case 0: case 1: fn = launch<0, 0>; break;
+    case 4: fn = launch<2, 0>; break;
+    case 5: fn = launch<2, 1>; break;
+    case 8: fn = launch<4, 0>; break;
+    case 9: fn = launch<4, 1>; break;
+    case 12: fn = launch<6, 0>; break;
+    case 13: fn = launch<6, 1>; break;
+    case 16: fn = launch<8, 0>; break;
+    case 17: fn = launch<8, 1>; break;
+    default: return (int)hipErrorInvalidValue;
+    }
+    e = hipMalloc(&sink, (size_t)grid * 256 * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc(&clk, (size_t)waves * 2 * sizeof(unsigned long long));
+    if (e == hipSuccess) e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    if (e == hipSuccess) {
+        fn(grid, iters / 4 + 1, zero_data, sink, clk, 0);  // warm-up (clock ramp)
+        hipEventRecord(e0, 0);
+        fn(grid, iters, zero_data, sink, clk, 0);
+        hipEventRecord(e1, 0);
+        e = hipEventSynchronize(e1);
+    }
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e == hipSuccess) {
+        float t = 0.f;
+        hipEventElapsedTime(&t, e0, e1);
+        unsigned long long *h = new unsigned long long[(size_t)waves * 2];
+        e = hipMemcpy(h, clk, (size_t)waves * 2 * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+        double cyc = 0, real = 0;
+        for (int w = 0; w < waves; ++w) { cyc += (double)h[2 * w]; real += (double)h[2 * w + 1]; }
+        delete[] h;
+        *ms = t;
+        *tflops = (double)waves * iters * 4.0 * 32768.0 / (t * 1e-3) / 1e12;
+        *mhz = real > 0 ? cyc / real * 100.0 : 0.0;
+    }
+    if (e0) hipEventDestroy(e0);
+    if (e1) hipEventDestroy(e1);
+    if (sink) hipFree(sink);
+    if (clk) hipFree(clk);
+    return (int)e;
+}
