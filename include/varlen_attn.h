@@ -155,6 +155,23 @@ va_status varlen_attn_fwd(const va_problem *p, const void *q, const void *k,
                           const int32_t *cu_seqlens_k, const float *sinks,
                           void **out, float **lse, void *stream);
 
+/* Out variant for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and arguments as varlen_attn_fwd_out (bitwise the same results)
+ * without a workspace argument.  The work list and the decode partials live
+ * in a 64 MiB device array inside the library, one per device, held until the
+ * process ends; its address is resolved on the first call on a device.  A
+ * call whose workspace would exceed 64 MiB (varlen_attn_workspace_size(p, 0))
+ * returns VA_ERR_WORKSPACE and enqueues nothing.  The call allocates nothing
+ * and needs no cleared memory (the pre-pass rewrites everything it reads).
+ * All calls on one device share that array: calls that overlap in time on
+ * one device (on different streams, or from different threads without
+ * stream ordering) race and give undefined results. */
+va_status varlen_attn_fwd_out_noalloc(const va_problem *p, const void *q, const void *k,
+                                      const void *v, const int32_t *cu_seqlens_q,
+                                      const int32_t *cu_seqlens_k, const float *sinks,
+                                      void *out, float *lse, void *stream);
+
 /* Paged K/V (SparseAttnSharedkv README, PageAttention constraints; pull
  * request "[varlen_attn for inference] add out variant", page_table and
  * seqused_k arguments): key length of sequence b is seqused_k[b]; keys are

@@ -10,7 +10,7 @@ kernels behind the C ABI of include/varlen_attn.h; this package only binds it.
 """
 from .api import (bwd_workspace_size, kernel_path, make_problem, output_shapes, plan, varlen_attn,
                   varlen_attn_bwd, varlen_attn_bwd_sinks, varlen_attn_fwd, varlen_attn_merge, varlen_attn_out,
-                  varlen_attn_paged, varlen_attn_sparse_sharedkv, workspace_size)
+                  varlen_attn_out_noalloc, varlen_attn_paged, varlen_attn_sparse_sharedkv, workspace_size)
 
-__all__ = ["varlen_attn", "varlen_attn_out", "varlen_attn_paged", "varlen_attn_fwd", "varlen_attn_bwd",
+__all__ = ["varlen_attn", "varlen_attn_out", "varlen_attn_out_noalloc", "varlen_attn_paged", "varlen_attn_fwd", "varlen_attn_bwd",
            "varlen_attn_bwd_sinks", "varlen_attn_merge", "varlen_attn_sparse_sharedkv", "workspace_size", "bwd_workspace_size", "plan", "kernel_path", "output_shapes", "make_problem"]

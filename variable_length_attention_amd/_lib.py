@@ -26,7 +26,7 @@ EXPORTED = [
     "varlen_attn_fwd_paged", "varlen_attn_free", "varlen_attn_plan", "varlen_attn_path",
     "varlen_attn_last_error", "varlen_attn_abi_version", "varlen_attn_bwd_workspace_size",
     "varlen_attn_bwd", "varlen_attn_merge", "varlen_attn_sparse_sharedkv",
-    "varlen_attn_bwd_sinks_workspace_size", "varlen_attn_bwd_sinks",
+    "varlen_attn_bwd_sinks_workspace_size", "varlen_attn_bwd_sinks", "varlen_attn_fwd_out_noalloc",
 ]
 
 
@@ -74,6 +74,8 @@ def load():
         lib.varlen_attn_workspace_size.restype = ctypes.c_size_t
         lib.varlen_attn_fwd_out.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.varlen_attn_fwd_out.restype = ctypes.c_int
+        lib.varlen_attn_fwd_out_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.varlen_attn_fwd_out_noalloc.restype = ctypes.c_int
         lib.varlen_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), vp]
         lib.varlen_attn_fwd.restype = ctypes.c_int

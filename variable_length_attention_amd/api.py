@@ -138,6 +138,28 @@ def varlen_attn_out(out: torch.Tensor, q, k, v, cu_seqlens_q, cu_seqlens_k, max_
     return lse
 
 
+def varlen_attn_out_noalloc(out: torch.Tensor, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                            max_seqlen_k: int, *, scale: Optional[float] = None, causal: bool = False,
+                            window: Tuple[int, int] = (-1, -1), sinks=None, lse=None, alibi_slopes=None):
+    """varlen_attn_out without a workspace (the library's per-device scratch
+    array instead): for callers that cannot allocate.  ``lse`` (float32
+    [total_q, num_heads]) is filled when given; calls that overlap in time on
+    one device race."""
+    dev = _check_tensors(out, q, k, v, cu_seqlens_q, cu_seqlens_k, sinks, lse)
+    _need(k.dim() == 3 and v.shape == k.shape, "k and v must be [total_k, num_kv_heads, head_dim]")
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32, "cu_seqlens must be int32")
+    _need(out.dtype == q.dtype and k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v, out must share a dtype")
+    _need(out.shape == q.shape, "out must have q's shape")
+    if sinks is not None:
+        _need(sinks.dtype == torch.float32 and sinks.numel() == q.shape[1], "sinks must be float32 [num_heads]")
+    p = make_problem(q, k.shape[1], k.shape[0], cu_seqlens_q.numel() - 1, max_seqlen_q, max_seqlen_k,
+                     scale, causal, window, alibi_slopes=alibi_slopes)
+    st = _lib.load().varlen_attn_fwd_out_noalloc(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(sinks),
+        _ptr(out), _ptr(lse), _stream(dev))
+    _lib.check(st)
+
+
 def varlen_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, *,
                 scale: Optional[float] = None, causal: bool = False,
                 window: Tuple[int, int] = (-1, -1), sinks=None, return_lse: bool = False, alibi_slopes=None):

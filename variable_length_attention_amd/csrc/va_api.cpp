@@ -16,6 +16,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 namespace {
@@ -453,6 +454,38 @@ va::PlanArgs bwd_plan(const va_problem *p, const int32_t *cu_q, const int32_t *c
     return pa;
 }
 
+// ---------------------------------------------------------------- scratch of the allocation-free entry point
+// varlen_attn_fwd_out_noalloc keeps its workspace (work list, decode
+// partials) in this array instead of a caller buffer.  Every device the
+// library runs on holds its own copy until the process ends.  Host code
+// never uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, resolved once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices] = {};
+
+va_status scratch_of_current_device(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(VA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(VA_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch table covers", dev,
+                    kScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(VA_ERR_HIP, "hipGetSymbolAddress of the scratch array failed: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return VA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -711,6 +744,25 @@ va_status varlen_attn_fwd_out(const va_problem *p, const void *q, const void *k,
 {
     Call c{p, 0, q, k, v, cu_seqlens_q, cu_seqlens_k, nullptr, nullptr, sinks, out, lse, workspace,
            workspace_bytes};
+    return run(c, (hipStream_t)stream);
+}
+
+va_status varlen_attn_fwd_out_noalloc(const va_problem *p, const void *q, const void *k, const void *v,
+                                      const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                      const float *sinks, void *out, float *lse, void *stream)
+{
+    va_status st = check_problem(p, 0);
+    if (st) return st;
+    Layout L;
+    if ((st = make_layout(p, 0, L))) return st;
+    if (L.total > kScratchBytes)
+        return fail(VA_ERR_WORKSPACE,
+                    "the call needs %zu bytes of workspace, above the %zu-byte scratch of "
+                    "varlen_attn_fwd_out_noalloc (varlen_attn_fwd_out takes a caller workspace)",
+                    L.total, kScratchBytes);
+    void *ws = nullptr;
+    if ((st = scratch_of_current_device(&ws))) return st;
+    Call c{p, 0, q, k, v, cu_seqlens_q, cu_seqlens_k, nullptr, nullptr, sinks, out, lse, ws, kScratchBytes};
     return run(c, (hipStream_t)stream);
 }
 
