@@ -52,10 +52,12 @@
  * block_table_stride * block_size, every block id used lies in
  * [0, num_blocks).  Violating them is undefined behaviour.  With the
  * environment variable VARLEN_ATTN_DEVICE_CHECK=1 (read on every call) each
- * call first runs a device-side check of exactly these conditions on its
- * stream, synchronises the stream, and returns VA_ERR_DEVICE_CHECK (nothing
- * else enqueued, out / lse untouched; the workspace may have been written)
- * when one fails.
+ * forward call (varlen_attn_fwd, _fwd_out, _fwd_out_noalloc, _fwd_paged)
+ * first runs a device-side check of exactly these conditions on its stream,
+ * synchronises the stream, and returns VA_ERR_DEVICE_CHECK (nothing else
+ * enqueued, out / lse untouched; the workspace may have been written) when
+ * one fails.  The backward, the sink gradient, the merge and the sparse
+ * shared-KV operator do not run this check.
  *
  * ABI rule: a shipped declaration never changes; a changed signature gets a
  * new _v2 name (the rule PyTorch applies to its stable C shim, per the pull
@@ -74,14 +76,15 @@ extern "C" {
 /* 1: forward, plan, backward.  2: adds VA_F16, va_problem.alibi_slopes,
  * varlen_attn_merge and varlen_attn_sparse_sharedkv (version 1 structs are
  * still accepted).  3: adds varlen_attn_bwd_sinks (+ its workspace size);
- * varlen_attn_bwd takes fp16 and alibi_slopes. */
-#define VARLEN_ATTN_ABI_VERSION 3
+ * varlen_attn_bwd takes fp16 and alibi_slopes.  4: adds
+ * varlen_attn_fwd_out_noalloc. */
+#define VARLEN_ATTN_ABI_VERSION 4
 
 typedef enum {
     VA_OK = 0,
     VA_ERR_NULL = 1,         /* a required pointer is NULL                        */
     VA_ERR_SHAPE = 2,        /* inconsistent sizes (H % H_kv, batch < 1, totals 0) */
-    VA_ERR_DTYPE = 3,        /* dtype not VA_F32 / VA_BF16                        */
+    VA_ERR_DTYPE = 3,        /* dtype not VA_F32 / VA_BF16 / VA_F16               */
     VA_ERR_UNSUPPORTED = 4,  /* head_dim not 64 / 128, window < -1, ...           */
     VA_ERR_ALIAS = 5,        /* out or lse overlaps an input or each other        */
     VA_ERR_ALIGN = 6,        /* a data pointer is not 16-byte aligned             */
@@ -124,12 +127,15 @@ typedef struct {
                                  * pages list alibi_slopes in the op schema of the
                                  * pull request "[varlen_attn for inference] add
                                  * out variant" without its formula; this is the
-                                 * reading taken.  Forward only.                  */
+                                 * reading taken.  Used by every forward kernel
+                                 * and by varlen_attn_bwd (the slopes get no
+                                 * gradient).                                     */
 } va_problem;
 
-/* Bytes of device workspace `varlen_attn_fwd_out` (paged = 0) or
- * `varlen_attn_fwd_paged` (paged = 1) needs for this problem; 0 if the
- * problem is invalid (the entry point then reports why). */
+/* Library helper (no passage of the pages defines it).  Bytes of device
+ * workspace `varlen_attn_fwd_out` (paged = 0) or `varlen_attn_fwd_paged`
+ * (paged = 1) needs for this problem; 0 if the problem is invalid (the entry
+ * point then reports why). */
 size_t varlen_attn_workspace_size(const va_problem *p, int paged);
 
 /* Out variant, contiguous K/V: writes out [total_q, H, D] (and lse when not
@@ -182,7 +188,8 @@ va_status varlen_attn_fwd_paged(const va_problem *p, const void *q, const void *
                                 const float *sinks, void *out, float *lse,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
-/* Releases memory returned by varlen_attn_fwd, stream-ordered. */
+/* Library helper (no passage of the pages defines it): releases memory
+ * returned by varlen_attn_fwd, stream-ordered. */
 va_status varlen_attn_free(void *ptr, void *stream);
 
 /* Work partition of a call (the GPU pre-pass that maps ragged sequences to
@@ -210,11 +217,13 @@ va_status varlen_attn_plan(const va_problem *p, int paged, const int32_t *cu_seq
  * bias (-slope_h |i + Lk - Lq - j|, the slopes being an input like q).  dq,
  * dk, dv are in the input dtype (accumulated
  * in float32) and fully overwritten; keys no query sees get zero gradients.
- * The gradient of sink logits is not computed.  Same ownership, stream and
- * error rules as the forward; dq, dk, dv may not overlap any input, the
+ * The gradient of the sink logits is varlen_attn_bwd_sinks' output.  Same
+ * ownership, stream and error rules as the forward (without the opt-in
+ * device check); dq, dk, dv may not overlap any input, the
  * workspace or each other; p->dtype must be VA_BF16 or VA_F16 (else
  * VA_ERR_UNSUPPORTED).  `workspace` holds at least
- * varlen_attn_bwd_workspace_size(p) bytes. */
+ * varlen_attn_bwd_workspace_size(p) bytes (a library helper; 0 for an
+ * invalid p). */
 size_t varlen_attn_bwd_workspace_size(const va_problem *p);
 va_status varlen_attn_bwd(const va_problem *p, const void *dout, const void *q, const void *k,
                           const void *v, const void *out, const float *lse,
@@ -322,7 +331,8 @@ va_status varlen_attn_sparse_sharedkv(const va_sparse_problem *p, const void *q,
                                       const int32_t *cmp_sparse_indices, const int32_t *cu_seqlens_q,
                                       const float *sinks, void *out, float *lse, void *stream);
 
-/* Which kernel family a call with these arguments would use:
+/* Library helpers (no passage of the pages defines them).
+ * Which kernel family a call with these arguments would use:
  * 0 = prefill tiles, 1 = split-KV decode with combine, 2 = float32 path,
  * 3 = sliding-window kernel (16-bit K/V, contiguous or paged, 32..64 query
  * heads per kv head, window bounded on both sides, no ALiBi); -1 if invalid. */
@@ -331,6 +341,7 @@ int varlen_attn_path(const va_problem *p, int paged);
 /* Thread-local text for the last non-OK status returned on this thread. */
 const char *varlen_attn_last_error(void);
 
+/* VARLEN_ATTN_ABI_VERSION of the built library. */
 int varlen_attn_abi_version(void);
 
 #ifdef __cplusplus

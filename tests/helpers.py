@@ -10,6 +10,9 @@ import workloads as W
 # 2e-2 / 1e-3 with fp32 accumulation
 TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 1e-3), "f16": (5e-3, 1e-3)}
 
+# host threads for oracle runs inside GPU tests: a GPU machine's CPU share
+ORACLE_THREADS = 16
+
 
 def announce(msg: str) -> None:
     sys.stderr.write(f"[gpu-case] {msg}\n")
@@ -70,6 +73,20 @@ def assert_close(case, out, lse, ref_out, ref_lse, what=""):
     assert err_o <= tol_o, f"{what}: max |O - O_ref| = {err_o:.3e} > {tol_o}"
     assert err_l <= tol_l, f"{what}: max |LSE - LSE_ref| = {err_l:.3e} > {tol_l}"
     return err_o, err_l
+
+
+def assert_close_blocks(case, out_t, lse_t, ref_out, ref_lse, what="", rows=2048):
+    """assert_close over all rows, taken in blocks of rows (the GPU tensors
+    are copied block by block); returns the largest (O, LSE) errors."""
+    import torch
+    worst_o, worst_l = 0.0, 0.0
+    for r0 in range(0, int(out_t.shape[0]), rows):
+        r1 = min(r0 + rows, int(out_t.shape[0]))
+        o = out_t[r0:r1].to(torch.float64).cpu().numpy()
+        l = lse_t[r0:r1].to(torch.float64).cpu().numpy()
+        eo, el = assert_close(case, o, l, ref_out[r0:r1], ref_lse[r0:r1], f"{what} rows {r0}..{r1}")
+        worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+    return worst_o, worst_l
 
 
 def sample_pairs(case, n, seed):

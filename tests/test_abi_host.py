@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.varlen_attn_abi_version() == 3
+    assert lib.varlen_attn_abi_version() == 4
 
 
 def test_problem_struct_matches_header(tmp_path):

@@ -132,6 +132,13 @@ SWEEP = [
     ("queries_without_keys", 4, 2, 128, [50, 70, 30], [0, 90, 30], False, (-1, -1), False),
     ("keys_without_queries", 4, 2, 128, [0, 70, 129], [65, 70, 129], True, (-1, -1), False),
     ("single_rows", 4, 1, 128, [1, 1, 1, 2], [1, 5, 130, 2], True, (-1, -1), False),
+    # GQA ratios 4 and 16 (quarter work units of the dQ kernel) with more
+    # queries than keys, causal and end-aligned: leading rows and whole
+    # leading quarters see no key
+    ("q_longer_causal_g4", 8, 2, 128, [70, 40, 130], [30, 0, 100], True, (-1, -1), False),
+    ("q_longer_causal_g4_sinks", 8, 2, 128, [70, 40, 130], [30, 0, 100], True, (-1, -1), True),
+    ("q_longer_causal_g16", 32, 2, 128, [70, 40], [30, 10], True, (-1, -1), False),
+    ("q_longer_causal_g16_sinks", 32, 2, 128, [70, 40], [30, 10], True, (-1, -1), True),
 ]
 
 

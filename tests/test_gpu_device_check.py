@@ -7,7 +7,12 @@ out and lse untouched.  Every call with contents that would be unsafe to
 compute on is preceded, under the same environment, by a harmless violation
 (a max_seqlen_k below the true maximum, which only affects launch sizing)
 that must be reported, so an unsafe input never reaches the kernels if the
-switch were not honoured.
+switch were not honoured.  The paged violations are also safe to compute on
+by themselves: the caches are views into allocations with one spare block
+before and after (block ids -1 and num_blocks land in mapped memory) and
+the block table has a spare row of valid ids (a key count beyond a row reads
+the next row's first entry), so a regression in one condition of the check
+gives a wrong result, not an access outside the allocations.
 """
 import numpy as np
 import pytest
@@ -48,8 +53,8 @@ def _expect_check_error(case, what):
     cu_q = dev(case["cu_q"], torch)
     with pytest.raises(RuntimeError, match="VA_ERR_DEVICE_CHECK"):
         if case.get("paged"):
-            va.varlen_attn_paged(q, dev(case["k_cache"], torch), dev(case["v_cache"], torch),
-                                 dev(case["block_table"], torch), cu_q, dev(case["seqused_k"], torch),
+            va.varlen_attn_paged(q, _padded_cache(case["k_cache"]), _padded_cache(case["v_cache"]),
+                                 _padded_table(case["block_table"]), cu_q, dev(case["seqused_k"], torch),
                                  case["max_q"], case["max_k"], scale=case["scale"], causal=case["causal"],
                                  window=win, sinks=dev(case.get("sinks"), torch), out=out)
         else:
@@ -58,6 +63,22 @@ def _expect_check_error(case, what):
                                causal=case["causal"], window=win, sinks=dev(case.get("sinks"), torch))
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), before.view(torch.int16)), "out was written"
+
+
+def _padded_cache(a):
+    """The cache as a contiguous view with one spare (zero) block before and after it."""
+    t = dev(a, torch)
+    big = torch.zeros((t.shape[0] + 2,) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)
+    big[1:-1] = t
+    return big[1:-1]
+
+
+def _padded_table(a):
+    """The block table as a contiguous view with a spare row of block id 0 after it."""
+    t = dev(a, torch)
+    big = torch.zeros((t.shape[0] + 1, t.shape[1]), dtype=t.dtype, device=t.device)
+    big[:-1] = t
+    return big[:-1]
 
 
 def _canary(case):

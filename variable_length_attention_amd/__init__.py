@@ -3,10 +3,12 @@
 softmax(Q K^T * scale) V over ragged sequences packed in TND layout and
 delimited by cu_seqlens, with GQA, causal / sliding-window masks, per-head
 sink logits and an optional paged KV cache; writes O into a caller buffer and
-returns the float32 log-sum-exp; its backward (dq, dk, dv) for bf16
+returns the float32 log-sum-exp; an out variant that allocates nothing; its
+backward (dq, dk, dv, and the sink-logit gradient) for bf16 / fp16
 contiguous K/V; the log-sum-exp merge of partial results over disjoint key
-sets; and sliding-window + sparse compressed attention over shared K/V.  The computation runs in hand-written HIP
-kernels behind the C ABI of include/varlen_attn.h; this package only binds it.
+sets; and sliding-window + sparse compressed attention over shared K/V.  The
+computation runs in hand-written HIP kernels behind the C ABI of
+include/varlen_attn.h; this package only binds it.
 """
 from .api import (bwd_workspace_size, kernel_path, make_problem, output_shapes, plan, varlen_attn,
                   varlen_attn_bwd, varlen_attn_bwd_sinks, varlen_attn_fwd, varlen_attn_merge, varlen_attn_out,

@@ -93,6 +93,40 @@ def _check_tensors(*ts):
     return dev
 
 
+def _check_rows_f32(t, rows, heads, what):
+    if t is not None:
+        _need(t.dtype == torch.float32 and tuple(t.shape) == (rows, heads),
+              f"{what} must be float32 [total_q, num_heads] = [{rows}, {heads}]")
+
+
+def _check_heads_f32(t, heads, what):
+    if t is not None:
+        _need(t.dtype == torch.float32 and t.dim() == 1 and t.numel() == heads,
+              f"{what} must be float32 [num_heads] = [{heads}]")
+
+
+def _check_forward(q, out, lse, sinks, alibi_slopes, cu_seqlens_q):
+    """Checks shared by the forward bindings: the C library sizes every
+    buffer from q and the problem description, so each tensor handed over
+    must match them (nothing is launched otherwise)."""
+    _need(q.dim() == 3, "q must be [total_q, num_heads, head_dim]")
+    if out is not None:
+        _need(out.dtype == q.dtype and out.shape == q.shape, "out must have q's shape and dtype")
+    _check_rows_f32(lse, q.shape[0], q.shape[1], "lse")
+    _check_heads_f32(sinks, q.shape[1], "sinks")
+    _check_heads_f32(alibi_slopes, q.shape[1], "alibi_slopes")
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.dim() == 1 and cu_seqlens_q.numel() >= 2,
+          "cu_seqlens_q must be int32 [batch + 1]")
+
+
+def _check_contiguous_kv(q, k, v, cu_seqlens_q, cu_seqlens_k):
+    _need(k.dim() == 3 and v.shape == k.shape, "k and v must be [total_k, num_kv_heads, head_dim]")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k and v must share a dtype")
+    _need(k.shape[2] == q.shape[2], "k and v must have q's head_dim")
+    _need(cu_seqlens_k.dtype == torch.int32 and cu_seqlens_k.dim() == 1
+          and cu_seqlens_k.numel() == cu_seqlens_q.numel(), "cu_seqlens_k must be int32 [batch + 1], like cu_seqlens_q")
+
+
 def workspace_size(problem: _lib.VaProblem, paged: bool = False) -> int:
     return int(_lib.load().varlen_attn_workspace_size(ctypes.byref(problem), 1 if paged else 0))
 
@@ -119,17 +153,14 @@ def varlen_attn_out(out: torch.Tensor, q, k, v, cu_seqlens_q, cu_seqlens_k, max_
     """Writes attention over contiguous packed K/V into ``out``; returns the
     float32 LSE when ``return_lse`` (or an ``lse`` buffer is given), else None.
     ``alibi_slopes`` (float32 [num_heads]) adds -slope * |i + Lk - Lq - j|."""
-    dev = _check_tensors(out, q, k, v, cu_seqlens_q, cu_seqlens_k, sinks, lse, workspace)
-    _need(k.dim() == 3 and v.shape == k.shape, "k and v must be [total_k, num_kv_heads, head_dim]")
-    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32, "cu_seqlens must be int32")
-    _need(out.dtype == q.dtype and k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v, out must share a dtype")
-    _need(out.shape == q.shape, "out must have q's shape")
+    dev = _check_tensors(out, q, k, v, cu_seqlens_q, cu_seqlens_k, sinks, lse, workspace, alibi_slopes)
+    _need(out is not None, "out must be given")
+    _check_forward(q, out, lse, sinks, alibi_slopes, cu_seqlens_q)
+    _check_contiguous_kv(q, k, v, cu_seqlens_q, cu_seqlens_k)
     p = make_problem(q, k.shape[1], k.shape[0], cu_seqlens_q.numel() - 1, max_seqlen_q, max_seqlen_k,
                      scale, causal, window, alibi_slopes=alibi_slopes)
     if return_lse and lse is None:
         lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=dev)
-    if sinks is not None:
-        _need(sinks.dtype == torch.float32 and sinks.numel() == q.shape[1], "sinks must be float32 [num_heads]")
     ws = _workspace(p, False, dev, workspace)
     st = _lib.load().varlen_attn_fwd_out(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(sinks),
@@ -145,13 +176,10 @@ def varlen_attn_out_noalloc(out: torch.Tensor, q, k, v, cu_seqlens_q, cu_seqlens
     array instead): for callers that cannot allocate.  ``lse`` (float32
     [total_q, num_heads]) is filled when given; calls that overlap in time on
     one device race."""
-    dev = _check_tensors(out, q, k, v, cu_seqlens_q, cu_seqlens_k, sinks, lse)
-    _need(k.dim() == 3 and v.shape == k.shape, "k and v must be [total_k, num_kv_heads, head_dim]")
-    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32, "cu_seqlens must be int32")
-    _need(out.dtype == q.dtype and k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v, out must share a dtype")
-    _need(out.shape == q.shape, "out must have q's shape")
-    if sinks is not None:
-        _need(sinks.dtype == torch.float32 and sinks.numel() == q.shape[1], "sinks must be float32 [num_heads]")
+    dev = _check_tensors(out, q, k, v, cu_seqlens_q, cu_seqlens_k, sinks, lse, alibi_slopes)
+    _need(out is not None, "out must be given")
+    _check_forward(q, out, lse, sinks, alibi_slopes, cu_seqlens_q)
+    _check_contiguous_kv(q, k, v, cu_seqlens_q, cu_seqlens_k)
     p = make_problem(q, k.shape[1], k.shape[0], cu_seqlens_q.numel() - 1, max_seqlen_q, max_seqlen_k,
                      scale, causal, window, alibi_slopes=alibi_slopes)
     st = _lib.load().varlen_attn_fwd_out_noalloc(
@@ -178,11 +206,17 @@ def varlen_attn_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k,
     """Paged K/V: caches [num_blocks, block_size, num_kv_heads, head_dim],
     block_table int32 [batch, stride], seqused_k int32 [batch]."""
     dev = _check_tensors(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, sinks, out, lse,
-                         workspace)
+                         workspace, alibi_slopes)
+    _check_forward(q, out, lse, sinks, alibi_slopes, cu_seqlens_q)
     _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape,
           "caches must be [num_blocks, block_size, num_kv_heads, head_dim]")
-    _need(block_table.dtype == torch.int32 and block_table.dim() == 2, "block_table must be int32 [batch, stride]")
-    _need(seqused_k.dtype == torch.int32 and cu_seqlens_q.dtype == torch.int32, "seqused_k / cu_seqlens_q must be int32")
+    _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "q and the caches must share a dtype")
+    _need(k_cache.shape[3] == q.shape[2], "the caches must have q's head_dim")
+    batch = cu_seqlens_q.numel() - 1
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == batch,
+          "block_table must be int32 [batch, stride]")
+    _need(seqused_k.dtype == torch.int32 and seqused_k.dim() == 1 and seqused_k.numel() == batch,
+          "seqused_k must be int32 [batch]")
     p = make_problem(q, k_cache.shape[2], 0, cu_seqlens_q.numel() - 1, max_seqlen_q, max_seqlen_k, scale,
                      causal, window, k_cache.shape[0], k_cache.shape[1], block_table.shape[1],
                      alibi_slopes=alibi_slopes)
@@ -217,6 +251,8 @@ def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
     """Calls the library-allocating C entry point ``varlen_attn_fwd`` and
     copies its buffers into torch tensors before releasing them."""
     dev = _check_tensors(q, k, v, cu_seqlens_q, cu_seqlens_k, sinks)
+    _check_forward(q, None, None, sinks, None, cu_seqlens_q)
+    _check_contiguous_kv(q, k, v, cu_seqlens_q, cu_seqlens_k)
     p = make_problem(q, k.shape[1], k.shape[0], cu_seqlens_q.numel() - 1, max_seqlen_q, max_seqlen_k,
                      scale, causal, window)
     lib = _lib.load()
@@ -273,17 +309,16 @@ def varlen_attn_bwd(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seq
     """Backward of varlen_attn for bf16 / fp16 contiguous K/V: returns (dq,
     dk, dv) (allocated when not given) from dout and the forward's out / lse
     (``alibi_slopes``: the forward's slopes, when it had them)."""
-    dev = _check_tensors(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, dq, dk, dv, workspace)
-    _need(dout.shape == q.shape and out.shape == q.shape, "dout and out must have q's shape")
-    _need(all(t.dtype == q.dtype for t in (dout, k, v, out)), "dout, q, k, v and out must share a dtype")
-    _need(k.dim() == 3 and v.shape == k.shape, "k and v must be [total_k, num_kv_heads, head_dim]")
-    _need(lse.dtype == torch.float32 and tuple(lse.shape) == (q.shape[0], q.shape[1]),
-          "lse must be float32 [total_q, num_heads]")
-    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32, "cu_seqlens must be int32")
+    dev = _check_tensors(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, dq, dk, dv, workspace, alibi_slopes)
+    _check_forward(q, out, lse, None, alibi_slopes, cu_seqlens_q)
+    _need(lse is not None, "lse of the forward call must be given")
+    _need(dout.shape == q.shape and dout.dtype == q.dtype, "dout must have q's shape and dtype")
+    _check_contiguous_kv(q, k, v, cu_seqlens_q, cu_seqlens_k)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    _need(dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape, "gradient shapes")
+    _need(dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+          and all(t.dtype == q.dtype for t in (dq, dk, dv)), "dq must be like q, dk and dv like k")
     p = make_problem(q, k.shape[1], k.shape[0], cu_seqlens_q.numel() - 1, max_seqlen_q, max_seqlen_k,
                      scale, causal, window, alibi_slopes=alibi_slopes)
     need = bwd_workspace_size(p)
