@@ -19,10 +19,14 @@ shard (a ring of 8), bound by HBM; and (keys "sparse", "sparse_d512")
 sliding-window + sparse compressed attention over shared K/V at head sizes
 128 and 512.
 
-The roofline figure is for the dominant kernel: its average duration is the
-step time minus the pre-pass time, both measured here with HIP events on
-the stream the kernels run on.  cpu_baseline times the fp64 oracle on a
-bounded sample of rows of the same workload on this host's cores.
+Timing: the K timed steps of a workload run as one captured HIP graph of K
+back-to-back calls (so host gaps between calls do not count), bracketed by
+HIP events on the stream the kernels run on; the same K steps called
+eagerly from Python are reported beside it.  The roofline figure is for the
+dominant kernel: its average duration is the graph-timed call minus the
+graph-timed pre-pass (the call-level fraction is reported too).
+cpu_baseline times the fp64 oracle on this host: per workload, all rows
+(configs 1, 4, 5) or a bounded sample of rows (configs 2, 3).
 """
 from __future__ import annotations
 
@@ -46,10 +50,10 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 # (profiles/traffic.json): a measurement counts only for the exact sources
 # it was taken with.
 KERNEL_SOURCES = {
-    "prefill_bf16": ["va_prefill_bf16.hip", "va_internal.h"],
-    "decode_bf16": ["va_decode.hip", "va_internal.h"],
-    "f32": ["va_prefill_f32.hip", "va_internal.h"],
-    "window_bf16": ["va_window.hip", "va_internal.h"],
+    "prefill_bf16": ["va_prefill_bf16.hip", "va_device.h"],
+    "decode_bf16": ["va_decode.hip"],
+    "f32": ["va_prefill_f32.hip"],
+    "window_bf16": ["va_window.hip"],
 }
 PATH_NAMES = ["prefill_bf16", "decode_bf16", "f32", "window_bf16"]  # index = varlen_attn_path
 
@@ -82,7 +86,7 @@ def flops(case) -> float:
 
 
 def alg_bytes(case) -> float:
-    es = 2 if case["dtype"] == "bf16" else 4
+    es = 4 if case["dtype"] == "f32" else 2
     H, Hkv, D = case["H"], case["Hkv"], case["D"]
     qo = 2.0 * case["T_q"] * H * D * es
     lse = 4.0 * case["T_q"] * H
@@ -103,6 +107,50 @@ def _dev(a, torch):
     if a.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def timed_eager(fn, n, w, torch):
+    """ms per call of fn called n times from Python after w warm-up calls."""
+    for _ in range(w):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def timed_graph(fn, n, w, torch):
+    """ms per call of n back-to-back calls of fn captured in one HIP graph
+    (after w eager warm-up calls and one warm-up replay), timed by HIP
+    events around one replay on the current stream.  Falls back to eager
+    timing if capture is not available."""
+    for _ in range(w):
+        fn()
+    torch.cuda.synchronize()
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+    except Exception as exc:  # pragma: no cover - depends on the runtime
+        log(f"graph capture unavailable ({exc}); timing eagerly")
+        return timed_eager(fn, n, 0, torch)
+    e0, e1 = _events(torch)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
 
 
 def time_case(case, steps, warmup, torch):
@@ -149,36 +197,11 @@ def time_case(case, steps, warmup, torch):
                                         None, 0, None,
                                         ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()), stream))
 
-    def timed(fn, n, w):
-        for _ in range(w):
-            fn()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
-
-    ms_step = timed(step, steps, warmup)
-    # The pre-pass alone is a few microseconds, shorter than a Python call:
-    # time it as a captured graph of back-to-back launches so host gaps do
-    # not count (eager timing if capture is unavailable).
-    try:
-        plan_step()
-        torch.cuda.synchronize()
-        reps = 20
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(reps):
-                plan_step()
-        ms_plan = timed(g.replay, max(1, steps // 2), 1) / reps
-    except Exception as exc:  # pragma: no cover - depends on the runtime
-        log(f"graph capture of the pre-pass unavailable ({exc}); timing it eagerly")
-        ms_plan = timed(plan_step, steps, max(1, warmup))
-    return ms_step, ms_plan, path
+    ms_eager = timed_eager(step, steps, warmup, torch)
+    ms_step = timed_graph(step, steps, 1, torch)
+    # the pre-pass alone (a few microseconds), the same way
+    ms_plan = timed_graph(plan_step, max(steps, 20), 1, torch)
+    return ms_step, ms_plan, path, ms_eager
 
 
 def time_backward(case, steps, warmup, torch):
@@ -205,16 +228,7 @@ def time_backward(case, steps, warmup, torch):
         va.varlen_attn_bwd(dout, q, k, v, out, lse, cu_q, cu_k, case["max_q"], case["max_k"],
                            scale=case["scale"], causal=case["causal"], window=win, dq=dq, dk=dk, dv=dv,
                            workspace=ws)
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    return timed_graph(step, steps, warmup, torch)
 
 
 MERGE_SHAPE = dict(n=8, rows=32768, H=24, D=128)  # ring of 8 over the full-attention shard
@@ -235,17 +249,9 @@ def time_merge(steps, warmup, torch):
 
     def step():
         va.varlen_attn_merge(o_parts, lse_parts, out=out, lse=lse)
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
+    ms = timed_graph(step, steps, warmup, torch)
     nbytes = float(n * rows * H * (D * 4 + 4) + rows * H * (D * 2 + 4))
-    return e0.elapsed_time(e1) / steps, nbytes
+    return ms, nbytes
 
 
 SPARSE_SHAPE = dict(lens_q=[1024] * 4, seqused_kv=[8192] * 4, H=64, Hkv=1, D=128, window=(127, 0), topk=512,
@@ -301,17 +307,9 @@ def time_sparse(steps, warmup, torch, shape=SPARSE_SHAPE):
     def step():
         va.varlen_attn_sparse_sharedkv(*args, sc["max_seqlen_kv"], scale=sc["scale"], window=sc["window"],
                                        cmp_ratio=sc["cmp_ratio"], sinks=sinks, out=out, lse=lse)
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
+    ms = timed_graph(step, steps, warmup, torch)
     fl, by = sparse_work(sc)
-    return e0.elapsed_time(e1) / steps, fl, by
+    return ms, fl, by
 
 
 # ---------------------------------------------------------------- HBM traffic
@@ -414,27 +412,67 @@ def calibrate_mfma(iters):
 
 
 # ---------------------------------------------------------------- CPU baseline
-def cpu_baseline(case, budget_s=15.0):
+CPU_THREADS = 16  # the host-thread share of one GPU on the measurement boxes
+
+
+def host_info():
+    """Threads the oracle uses, the cores visible to this process, nproc and
+    the CPU model."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return {"cores": min(CPU_THREADS, affinity), "affinity_cores": affinity, "nproc": os.cpu_count(),
+            "cpu_model": model}
+
+
+def cpu_baseline(case, budget_s=6.0, full=False):
+    """The fp64 oracle on this host (as it stands, not tuned): every row of
+    the workload when full, else random (token, head) rows for about
+    budget_s seconds.  Rate in mask-adjusted TFLOP/s and query tokens/s."""
     import oracle
-    threads = min(16, oracle.default_threads())
+    info = host_info()
+    threads = info["cores"]
     vis = visible_pairs(case)
-    rng = np.random.default_rng(12345)
-    done_flops, done_rows, spent = 0.0, 0, 0.0
-    n = 64
-    while spent < budget_s:
-        toks = rng.integers(0, case["T_q"], n)
-        heads = rng.integers(0, case["H"], n)
+    if full:
         t0 = time.perf_counter()
-        oracle.forward_rows(case, toks, heads, nthreads=threads)
-        dt = time.perf_counter() - t0
-        spent += dt
-        done_rows += n
-        done_flops += float(4 * case["D"] * vis[toks].sum())
-        if dt < budget_s / 4:
-            n *= 2
-    return {"value": done_flops / spent / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done_rows} random (token, head) rows of the same workload, "
-                      f"{done_flops / 1e9:.1f} mask-adjusted GFLOP in {spent:.1f} s (fp64)"}
+        oracle.forward(case, nthreads=threads)
+        spent = time.perf_counter() - t0
+        done_flops = flops(case)
+        sample = f"all {case['T_q']} x {case['H']} (token, head) rows"
+        tokens = case["T_q"]
+    else:
+        rng = np.random.default_rng(12345)
+        done_flops, done_rows, spent = 0.0, 0, 0.0
+        n = 64
+        while spent < budget_s:
+            toks = rng.integers(0, case["T_q"], n)
+            heads = rng.integers(0, case["H"], n)
+            t0 = time.perf_counter()
+            oracle.forward_rows(case, toks, heads, nthreads=threads)
+            dt = time.perf_counter() - t0
+            spent += dt
+            done_rows += n
+            done_flops += float(4 * case["D"] * vis[toks].sum())
+            if dt < budget_s / 4:
+                n *= 2
+        sample = f"{done_rows} random (token, head) rows"
+        tokens = done_rows / case["H"]
+    r = {"value": done_flops / spent / 1e12, "unit": "TFLOP/s", "kind": "oracle",
+         "tokens_per_s": tokens / spent, "seconds": spent,
+         "sample": f"{sample} of {case['spec'].name}, {done_flops / 1e9:.1f} mask-adjusted GFLOP in "
+                   f"{spent:.1f} s (fp64, {threads} threads)"}
+    r.update(info)
+    return r
 
 
 # ---------------------------------------------------------------- main
@@ -484,11 +522,12 @@ def main():
         log(f"config {n} ({spec.name}): generating input")
         case = W.make_case(spec)
         log(f"config {n}: timing {args.steps} steps after {args.warmup} warm-up")
-        ms_step, ms_plan, path = time_case(case, args.steps, args.warmup, torch)
+        ms_step, ms_plan, path, ms_eager = time_case(case, args.steps, args.warmup, torch)
         fl, by = flops(case), alg_bytes(case)
         ms_kernel = max(ms_step - ms_plan, 1e-6)
         hbm_bound = path == 1 or (fl / by) < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-        r = {"workload": spec.name, "ms_per_step": ms_step, "ms_prepass": ms_plan,
+        r = {"workload": spec.name, "ms_per_step": ms_step, "ms_per_step_eager": ms_eager,
+             "ms_prepass": ms_plan, "ms_kernel": ms_kernel,
              "tflops": fl / (ms_step * 1e-3) / 1e12, "gbs": by / (ms_step * 1e-3) / 1e9,
              "tokens_per_s": case["T_q"] / (ms_step * 1e-3), "flop": fl, "bytes": by,
              "kernel_path": PATH_NAMES[path]}
@@ -496,13 +535,22 @@ def main():
         if hbm_bound:
             ach = by / (ms_kernel * 1e-3) / 1e9
             r["roofline"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                             "frac": ach / PEAK_HBM_GBS, "traffic": traffic}
+                             "frac": ach / PEAK_HBM_GBS, "frac_call": r["gbs"] / PEAK_HBM_GBS,
+                             "traffic": traffic}
         else:
             ach = fl / (ms_kernel * 1e-3) / 1e12
             r["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                             "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic}
-        log(f"config {n}: {ms_step:.4f} ms/step (pre-pass {ms_plan:.4f} ms), {r['tflops']:.1f} TFLOP/s, "
-            f"{r['gbs']:.0f} GB/s, roofline {r['roofline']['frac'] * 100:.1f}% of {r['roofline']['bound']}")
+                             "frac": ach / PEAK_BF16_TFLOPS, "frac_call": r["tflops"] / PEAK_BF16_TFLOPS,
+                             "traffic": traffic}
+        log(f"config {n}: {ms_step:.4f} ms/step in a graph ({ms_eager:.4f} eager; pre-pass {ms_plan:.4f} ms), "
+            f"{r['tflops']:.1f} TFLOP/s, {r['gbs']:.0f} GB/s, roofline {r['roofline']['frac'] * 100:.1f}% "
+            f"of {r['roofline']['bound']}")
+        if not args.no_cpu_baseline:
+            # every row for the small and HBM-bound workloads, a sample of
+            # rows for the two large MFMA-bound ones
+            cb = cpu_baseline(case, full=n in (4, 5))
+            r["cpu_baseline"] = cb
+            log(f"config {n}: oracle {cb['value'] * 1e3:.1f} GFLOP/s on {cb['cores']} threads ({cb['sample']})")
         results[n] = r
         if main_case is None:
             main_case = case
@@ -514,7 +562,7 @@ def main():
         spec16 = dataclasses.replace(W.config(cfgs[0]), dtype="f16", name=W.config(cfgs[0]).name + "_f16")
         log(f"{spec16.name}: generating input")
         case16 = W.make_case(spec16)
-        ms16, mp16, _ = time_case(case16, args.steps, args.warmup, torch)
+        ms16, mp16, _, _ = time_case(case16, args.steps, args.warmup, torch)
         fl16 = flops(case16)
         ach16 = fl16 / (max(ms16 - mp16, 1e-6) * 1e-3) / 1e12
         results["f16"] = {"workload": spec16.name, "ms_per_step": ms16, "ms_prepass": mp16,
@@ -539,6 +587,10 @@ def main():
                    "paged": spec0.paged, "seed": spec0.seed},
         "roofline": main["roofline"],
         "tokens_per_s": main["tokens_per_s"],
+        "ms_per_step_eager": main["ms_per_step_eager"],
+        "ms_kernel": main["ms_kernel"],
+        "timing": "K steps as one captured HIP graph of back-to-back calls, HIP events around the replay; "
+                  "ms_per_step_eager: the same K calls issued from Python",
     }
     if not args.no_backward and spec0.dtype == "bf16" and not spec0.paged:
         log(f"backward on {spec0.name}: timing {args.steps} calls after {args.warmup} warm-up")
@@ -580,8 +632,15 @@ def main():
                               "frac": tf_s / PEAK_BF16_TFLOPS, "traffic": None})}
             log(f"{key}: {ms_s:.4f} ms/call, {tf_s:.1f} TFLOP/s, {gb_s:.0f} GB/s (algorithmic)")
     if not args.no_cpu_baseline:
-        log("cpu baseline: oracle on a sample of rows")
-        line["cpu_baseline"] = cpu_baseline(main_case)
+        # the main workload's oracle rate, and the oracle on every workload
+        c1 = W.make_case(W.config(1))
+        per = {W.config(1).name: cpu_baseline(c1, full=True)}
+        for n in cfgs:
+            if n in results and "cpu_baseline" in results[n]:
+                per[results[n]["workload"]] = results[n].pop("cpu_baseline")
+        line["cpu_baseline"] = dict(per[main["workload"]])
+        line["cpu_baseline"]["per_workload"] = {k: {x: v[x] for x in ("value", "unit", "tokens_per_s", "seconds",
+                                                                       "sample")} for k, v in per.items()}
     line["also"] = {results[n]["workload"]: {k: v for k, v in results[n].items() if k != "workload"}
                     for n in cfgs[1:]}
     print(json.dumps(line), flush=True)

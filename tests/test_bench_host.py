@@ -78,3 +78,17 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_algorithmic_bytes_price_16_bit_types_alike():
+    """bf16 and fp16 elements are 2 bytes each, float32 4: the byte count of
+    a workload depends only on the element size."""
+    case = _lengths_case([5, 17, 32], [5, 17, 32], causal=True)
+    case.update(Hkv=2, dtype="bf16")
+    b16 = bench.alg_bytes(case)
+    assert bench.alg_bytes(dict(case, dtype="f16")) == b16
+    T, H, Hkv, D = case["T_q"], case["H"], 2, case["D"]
+    expect16 = 2.0 * T * H * D * 2 + 4.0 * T * H + 2.0 * case["T_k"] * Hkv * D * 2 + 8.0 * (case["B"] + 1)
+    assert b16 == expect16
+    expect32 = 2.0 * T * H * D * 4 + 4.0 * T * H + 2.0 * case["T_k"] * Hkv * D * 4 + 8.0 * (case["B"] + 1)
+    assert bench.alg_bytes(dict(case, dtype="f32")) == expect32
