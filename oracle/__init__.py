@@ -327,12 +327,20 @@ def _widen16(a, dtype):
 
 def sparse_sharedkv(case, tokens=None):
     """Attention of each query token over its sliding window of original
-    keys plus the compressed keys its indices select (one softmax, sinks as
-    extra logits; each key row is also its value row).  SparseAttnSharedkv
-    README, formula section (K~ = V~ from ori_kv, cmp_kv and the indices) and
-    its third scenario.  Readings: the window is [p - left, p + right] with
-    p = i + S2_b - Lq_b; an index outside [0, S2_b / cmp_ratio) selects
-    nothing; a repeated index is attended as often as it appears.
+    keys plus compressed keys, in one softmax (sinks as extra logits; each
+    key row is also its value row).  SparseAttnSharedkv README, formula
+    section (K~ = V~ from ori_kv, cmp_kv, cmp_ratio and the indices) and its
+    scenarios: with ``case["cmp_all"]`` false the compressed keys are those
+    the indices select (third scenario; none when topk = 0), with it true
+    every compressed key the mask admits (second scenario: ori_kv and cmp_kv
+    given, no indices).
+    Readings: the window is [p - left, p + right] with p = i + S2_b - Lq_b;
+    sequence b has S3_b = S2_b / cmp_ratio compressed keys, and the
+    compressed-key mask (cmp_mask_mode 3) is causal aligned to the
+    bottom-right of the Lq_b x S3_b matrix: row i sees compressed position t
+    iff t <= i + S3_b - Lq_b; an index outside [0, S3_b) or beyond that
+    bound selects nothing; a repeated index is attended as often as it
+    appears.
     Returns (out [n, H, D], lse [n, H]) in float64 for the given tokens (all
     tokens by default)."""
     cu_q = np.asarray(case["cu_q"], np.int64)
@@ -340,6 +348,7 @@ def sparse_sharedkv(case, tokens=None):
     g = H // Hkv
     toks = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
     left, right = case["window"]
+    cmp_all = bool(case.get("cmp_all", False))
     out = np.zeros((len(toks), H, D))
     lse = np.full((len(toks), H), -np.inf)
 
@@ -355,10 +364,14 @@ def sparse_sharedkv(case, tokens=None):
         S2 = int(case["seqused_kv"][b])
         S3 = S2 // case["cmp_ratio"]
         p = i + S2 - Lq
+        last = i + S3 - Lq  # last compressed position row i sees
         win = np.arange(max(0, p - left), min(S2 - 1, p + right) + 1)
         for c in range(Hkv):
-            sel = np.asarray(case["indices"][t, c], np.int64)
-            sel = sel[(sel >= 0) & (sel < S3)]
+            if cmp_all:
+                sel = np.arange(0, max(0, min(S3, last + 1)))
+            else:
+                sel = np.asarray(case["indices"][t, c], np.int64)
+                sel = sel[(sel >= 0) & (sel < S3) & (sel <= last)]
             kv = np.concatenate([rows(case["ori_kv"], case["ori_table"], case["ori_kv"].shape[1], b, win, c),
                                  rows(case["cmp_kv"], case["cmp_table"], case["cmp_kv"].shape[1], b, sel, c)])
             heads = np.arange(c * g, (c + 1) * g)

@@ -310,18 +310,24 @@ def _paged(rng, rows_per_seq, bs, Hkv, D, dtype, poison_val):
 
 def sparse_case(lens_q, seqused_kv, *, H=64, Hkv=1, D=128, dtype="bf16", window=(127, 0), topk=512,
                 cmp_ratio=4, ori_bs=128, cmp_bs=128, sinks=True, seed=4000, invalid_frac=0.0,
-                shared_indices=False, scale=None) -> dict:
-    """Inputs of sliding-window + sparse compressed attention over shared K/V
-    (the SparseAttnSharedkv README's third scenario, its shapes: TND q,
-    PA_ND caches through permuted block tables, int32 indices [T, H_kv, topk]).
+                shared_indices=False, scale=None, cmp_all=False, visible_indices=False) -> dict:
+    """Inputs of sliding-window + compressed attention over shared K/V (the
+    SparseAttnSharedkv README's second and third scenarios, its shapes: TND
+    q, PA_ND caches through permuted block tables, int32 indices [T, H_kv,
+    topk]).  ``cmp_all``: the second scenario (every compressed key the mask
+    admits; topk must be 0).
 
     Draw order from ``default_rng(seed)``: q [T, H, D]; per sequence the
     original rows [S2_b, H_kv, D] then the compressed rows [S2_b / ratio,
     H_kv, D] (standard normal, cast to ``dtype``); sinks [H]; the two block
-    permutations; the indices (uniform in [0, S3_b), drawn per token or once
-    per sequence when ``shared_indices``, as in the README example); then a
-    fraction ``invalid_frac`` of the indices replaced by out-of-range values
-    (-1 or S3_b + k)."""
+    permutations; the indices: uniform in [0, S3_b), drawn per token or once
+    per sequence when ``shared_indices``; or, with ``visible_indices``, as
+    the README example draws them: topk distinct positions of [0, S3_b -
+    Lq_b] (the compressed keys every query row of the sequence sees), once
+    per sequence; then a fraction ``invalid_frac`` of the indices replaced by
+    out-of-range values (-1 or S3_b + k)."""
+    if cmp_all and topk != 0:
+        raise ValueError("the second scenario takes no indices (topk = 0)")
     rng = np.random.default_rng(seed)
     lens_q = np.asarray(lens_q, np.int64)
     S2 = np.asarray(seqused_kv, np.int64)
@@ -345,7 +351,13 @@ def sparse_case(lens_q, seqused_kv, *, H=64, Hkv=1, D=128, dtype="bf16", window=
         if e == s or topk == 0:
             continue
         hi = max(S3, 1)
-        if shared_indices:
+        if visible_indices:
+            span = S3 - (e - s) + 1
+            if span < topk:
+                raise ValueError(f"sequence {b}: only {max(span, 0)} compressed keys visible to every row, topk {topk}")
+            for c in range(Hkv):
+                idx[s:e, c] = rng.choice(span, topk, replace=False)[None, :]
+        elif shared_indices:
             idx[s:e] = rng.integers(0, hi, (1, Hkv, topk))
         else:
             idx[s:e] = rng.integers(0, hi, (e - s, Hkv, topk))
@@ -359,6 +371,6 @@ def sparse_case(lens_q, seqused_kv, *, H=64, Hkv=1, D=128, dtype="bf16", window=
         idx = np.where(bad, np.where(alt == 0, -1, s3 + rng.integers(0, 5, idx.shape)), idx).astype(np.int32)
     return dict(B=B, T=T, H=H, Hkv=Hkv, D=D, dtype=dtype, cu_q=cu_q, seqused_kv=S2.astype(np.int32),
                 q=q, ori_kv=ori_kv, ori_table=ori_table, cmp_kv=cmp_kv, cmp_table=cmp_table, indices=idx,
-                sinks=sk, window=tuple(window), topk=topk, cmp_ratio=cmp_ratio,
+                sinks=sk, window=tuple(window), topk=topk, cmp_ratio=cmp_ratio, cmp_all=bool(cmp_all),
                 scale=(1.0 / math.sqrt(D)) if scale is None else scale,
                 max_seqlen_kv=int(S2.max()) if B else 0)
