@@ -254,17 +254,23 @@ def time_merge(steps, warmup, torch):
     return ms, nbytes
 
 
+# third scenario: 512 distinct indices per sequence drawn, as the README
+# example draws them, from the compressed keys every row of it sees
 SPARSE_SHAPE = dict(lens_q=[1024] * 4, seqused_kv=[8192] * 4, H=64, Hkv=1, D=128, window=(127, 0), topk=512,
-                    cmp_ratio=4, ori_bs=128, cmp_bs=128, seed=4600)
+                    cmp_ratio=4, ori_bs=128, cmp_bs=128, seed=4600, visible_indices=True)
 # the same at the Ascend operator's own head size
 SPARSE_SHAPE_D512 = dict(SPARSE_SHAPE, D=512, seed=4601)
+# second scenario at that head size: every compressed key the causal
+# compressed mask admits (1025 to 2048 per row) plus the window
+SPARSE_SHAPE_ALL_D512 = dict(SPARSE_SHAPE, D=512, topk=0, cmp_all=True, visible_indices=False, seed=4602)
 
 
 def sparse_work(sc):
-    """(FLOPs, algorithmic bytes) of sliding-window + sparse compressed
-    attention: 4 * D FLOPs per (token, head, valid key); bytes = q, out, lse,
-    the indices, block tables and each sequence's distinct original rows in
-    some window and distinct selected compressed rows (read once)."""
+    """(FLOPs, algorithmic bytes) of sliding-window + compressed attention:
+    4 * D FLOPs per (token, head, attended key); bytes = q, out, lse, the
+    indices, block tables and each sequence's distinct original rows in some
+    window and distinct attended compressed rows (read once).  Row i of a
+    sequence sees compressed positions up to i + S3 - Lq."""
     cu = sc["cu_q"]
     left, right = sc["window"]
     g = sc["H"] // sc["Hkv"]
@@ -277,14 +283,22 @@ def sparse_work(sc):
         p = np.arange(Lq) + S2 - Lq
         lo, hi = np.maximum(0, p - left), np.minimum(S2 - 1, p + right)
         nwin = np.maximum(0, hi - lo + 1)
-        idx = sc["indices"][cu[b]:cu[b + 1]] if sc["topk"] else np.zeros((Lq, sc["Hkv"], 0), np.int32)
-        ok = (idx >= 0) & (idx < S3)
-        keys += int(nwin.sum()) * sc["Hkv"] + int(ok.sum())
+        last = np.arange(Lq) + S3 - Lq
         seen = np.zeros(S2, bool)
         for a_, z in zip(lo, hi):
             if z >= a_:
                 seen[a_:z + 1] = True
-        rows += int(seen.sum()) * sc["Hkv"] + sum(len(np.unique(idx[:, c][ok[:, c]])) for c in range(sc["Hkv"]))
+        rows += int(seen.sum()) * sc["Hkv"]
+        keys += int(nwin.sum()) * sc["Hkv"]
+        if sc.get("cmp_all"):
+            ncmp = np.clip(last + 1, 0, S3)
+            keys += int(ncmp.sum()) * sc["Hkv"]
+            rows += int(ncmp.max()) * sc["Hkv"]
+            continue
+        idx = sc["indices"][cu[b]:cu[b + 1]] if sc["topk"] else np.zeros((Lq, sc["Hkv"], 0), np.int32)
+        ok = (idx >= 0) & (idx <= last[:, None, None])
+        keys += int(ok.sum())
+        rows += sum(len(np.unique(idx[:, c][ok[:, c]])) for c in range(sc["Hkv"]))
     D, es = sc["D"], 2
     fl = 4.0 * D * g * keys
     by = (2.0 * sc["T"] * sc["H"] * D * es + 4.0 * sc["T"] * sc["H"] + 4.0 * sc["indices"].size
@@ -298,15 +312,16 @@ def time_sparse(steps, warmup, torch, shape=SPARSE_SHAPE):
     import variable_length_attention_amd as va
     import workloads as W
     sc = W.sparse_case(**shape)
-    args = [_dev(sc[k], torch) for k in ("q", "ori_kv", "ori_table", "seqused_kv", "cmp_kv", "cmp_table",
-                                          "indices", "cu_q")]
+    args = [_dev(sc[k], torch) if sc["topk"] or k != "indices" else None
+            for k in ("q", "ori_kv", "ori_table", "seqused_kv", "cmp_kv", "cmp_table", "indices", "cu_q")]
     sinks = _dev(sc["sinks"], torch)
     out = torch.empty_like(args[0])
     lse = torch.empty((sc["T"], sc["H"]), dtype=torch.float32, device="cuda")
 
     def step():
         va.varlen_attn_sparse_sharedkv(*args, sc["max_seqlen_kv"], scale=sc["scale"], window=sc["window"],
-                                       cmp_ratio=sc["cmp_ratio"], sinks=sinks, out=out, lse=lse)
+                                       cmp_ratio=sc["cmp_ratio"], cmp_attend_all=sc["cmp_all"], sinks=sinks, out=out,
+                                       lse=lse)
     ms = timed_graph(step, steps, warmup, torch)
     fl, by = sparse_work(sc)
     return ms, fl, by
@@ -615,15 +630,18 @@ def main():
                                       "frac": gbs / PEAK_HBM_GBS, "traffic": None}}
         log(f"merge: {ms_m:.4f} ms/call, {gbs:.0f} GB/s")
     if not args.no_sparse:
-        for key, shape in (("sparse", SPARSE_SHAPE), ("sparse_d512", SPARSE_SHAPE_D512)):
+        for key, shape in (("sparse", SPARSE_SHAPE), ("sparse_d512", SPARSE_SHAPE_D512),
+                           ("sparse_all_d512", SPARSE_SHAPE_ALL_D512)):
             D = shape["D"]
+            what = ("every visible compressed key (1025 to 2048) of 4x compressed keys" if shape.get("cmp_all") else
+                    "512 selected of 4x compressed keys")
             log(f"sparse shared-KV attention (4 x 1024 tokens over 8192 keys, 64/1 heads, d{D}, "
-                "window 128 + 512 selected)")
+                f"window 128 + {what})")
             ms_s, fl_s, by_s = time_sparse(args.steps, args.warmup, torch, shape)
             tf_s, gb_s = fl_s / (ms_s * 1e-3) / 1e12, by_s / (ms_s * 1e-3) / 1e9
             hbm = (fl_s / by_s) < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
             line[key] = {
-                "workload": "sliding window (127, 0) + 512 selected of 4x compressed keys, shared K/V, "
+                "workload": f"sliding window (127, 0) + {what}, shared K/V, "
                             f"4 x 1024 tokens over 8192 keys, 64 heads / 1 kv head, d{D}, bf16",
                 "ms_per_step": ms_s, "tflops": tf_s, "gbs": gb_s, "flop": fl_s, "bytes": by_s,
                 "roofline": ({"bound": "hbm", "achieved": gb_s, "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -77,8 +77,9 @@ extern "C" {
  * varlen_attn_merge and varlen_attn_sparse_sharedkv (version 1 structs are
  * still accepted).  3: adds varlen_attn_bwd_sinks (+ its workspace size);
  * varlen_attn_bwd takes fp16 and alibi_slopes.  4: adds
- * varlen_attn_fwd_out_noalloc. */
-#define VARLEN_ATTN_ABI_VERSION 4
+ * varlen_attn_fwd_out_noalloc.  5: adds va_sparse_problem.cmp_attend_all (the
+ * second scenario; version 4 descriptors are still accepted). */
+#define VARLEN_ATTN_ABI_VERSION 5
 
 typedef enum {
     VA_OK = 0,
@@ -280,23 +281,28 @@ va_status varlen_attn_merge(int32_t n_parts, int32_t rows, int32_t num_heads, in
                             const float *lse_parts, const float *sinks, void *out, float *lse,
                             void *stream);
 
-/* Sliding-window + sparse compressed attention over shared K/V: the third
- * scenario of the SparseAttnSharedkv README (ori_kv, cmp_kv and
- * cmp_sparse_indices given; K~ = V~ in its formula: one tensor row serves as
- * key and value).  For token t (row i of sequence b, Lq_b rows, S2_b =
- * seqused_kv[b] original keys) and each query head h of kv head c:
+/* Sliding-window + compressed attention over shared K/V: the three
+ * scenarios of the SparseAttnSharedkv README (K~ = V~ in its formula: one
+ * tensor row serves as key and value).  For token t (row i of sequence b,
+ * Lq_b rows, S2_b = seqused_kv[b] original keys, S3_b = S2_b / cmp_ratio
+ * compressed keys) and each query head h of kv head c:
  *   window keys:   original positions j in [p - window_left, p + window_right]
  *                  and [0, S2_b), p = i + S2_b - Lq_b (aligned to the end),
  *                  read from ori_kv through ori_block_table;
- *   selected keys: compressed positions cmp_sparse_indices[t][c][0 .. topk-1]
- *                  read from cmp_kv through cmp_block_table; an index outside
- *                  [0, S2_b / cmp_ratio) selects nothing; a repeated index
- *                  is attended as often as it appears;
- *   out[t][h] = sum_j w_j kv_j,  w = softmax over the window and selected keys
- *               of scale <q[t][h], kv_j>, with sinks[h] as an extra logit;
+ *   compressed keys, read from cmp_kv through cmp_block_table, visible up to
+ *                  last = i + S3_b - Lq_b (its mask mode 3 read as causal,
+ *                  aligned to the bottom-right corner of the Lq_b x S3_b
+ *                  matrix, as mode 4 aligns the window to the end):
+ *     cmp_attend_all = 1 (second scenario): every position 0 .. last;
+ *     cmp_attend_all = 0 (third scenario):  the positions
+ *                  cmp_sparse_indices[t][c][0 .. topk-1]; one outside
+ *                  [0, last] selects nothing, a repeated one is attended as
+ *                  often as it appears; topk = 0 gives the first scenario;
+ *   out[t][h] = sum_j w_j kv_j,  w = softmax over the window and compressed
+ *               keys of scale <q[t][h], kv_j>, with sinks[h] as an extra logit;
  *   lse[t][h] = natural log of that softmax's denominator.
- * The README leaves the compression operator and its mask mode 3 undefined;
- * here the compressed rows are given and every selected row is visible.
+ * The README does not define the compression operator: the compressed rows
+ * are inputs.
  *   q, out            [total_q, H, D] dtype (VA_BF16 / VA_F16), TND
  *   ori_kv            [ori_num_blocks, ori_block_size, H_kv, D], PA_ND
  *   cmp_kv            [cmp_num_blocks, cmp_block_size, H_kv, D], PA_ND
@@ -307,8 +313,9 @@ va_status varlen_attn_merge(int32_t n_parts, int32_t rows, int32_t num_heads, in
  *   cu_seqlens_q      int32 [batch + 1]; sinks float32 [H] or NULL;
  *   lse               float32 [total_q, H] or NULL
  * Limits: D in {64, 128, 512} (512 is the README's head size); H / H_kv <= 64;
- * bounded window (both sides >= 0)
- * with window_left + window_right + 1 + topk <= 1536; cmp_ratio >= 1.  Same
+ * window sides >= 0 (a side >= 2^30 is unbounded);
+ * cmp_ratio >= 1; cmp_attend_all needs topk = 0.  A descriptor whose
+ * struct_size ends before cmp_attend_all (ABI 4 callers) reads it as 0.  Same
  * ownership, stream, alignment and aliasing rules as the forward; nothing
  * is allocated and no workspace is needed. */
 typedef struct {
@@ -323,6 +330,7 @@ typedef struct {
     int32_t cmp_ratio;          /* compressed keys of sequence b: S2_b / ratio  */
     int32_t ori_num_blocks, ori_block_size, ori_block_table_stride;
     int32_t cmp_num_blocks, cmp_block_size, cmp_block_table_stride;
+    int32_t cmp_attend_all;     /* 1: every visible compressed key (no indices) */
 } va_sparse_problem;
 
 va_status varlen_attn_sparse_sharedkv(const va_sparse_problem *p, const void *q, const void *ori_kv,

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.varlen_attn_abi_version() == 4
+    assert lib.varlen_attn_abi_version() == 5
 
 
 def test_problem_struct_matches_header(tmp_path):
@@ -266,8 +266,12 @@ def test_sparse_rejects_before_launching():
     assert _sparse(num_heads=128) == 4                # 128 query heads per kv head
     assert _sparse(head_dim=96) == 4
     assert _sparse(head_dim=256) == 4
-    assert _sparse(window_left=-1) == 4               # unbounded window
-    assert _sparse(topk=1500) == 4                    # window + topk beyond 1536 keys
+    assert _sparse(window_left=-1) == 4               # negative window side
+    assert _sparse(topk=-1) == 2
+    assert _sparse(cmp_attend_all=1) == 2             # every visible key takes no indices
+    assert _sparse(cmp_attend_all=1, topk=0) == 2     # ... nor an indices pointer
+    assert _sparse(cmp_attend_all=2, topk=0, idx=None) == 2
+    assert _sparse(struct_size=4 * 18) == 2           # ends before the last field of ABI 4
     assert _sparse(cmp_ratio=0) == 2
     assert _sparse(ori_block_table_stride=31) == 2    # 4096 / 128 = 32 needed
     assert _sparse(cmp_block_table_stride=7) == 2     # 1024 / 128 = 8 needed

@@ -92,3 +92,29 @@ def test_algorithmic_bytes_price_16_bit_types_alike():
     assert b16 == expect16
     expect32 = 2.0 * T * H * D * 4 + 4.0 * T * H + 2.0 * case["T_k"] * Hkv * D * 4 + 8.0 * (case["B"] + 1)
     assert bench.alg_bytes(dict(case, dtype="f32")) == expect32
+
+
+def test_sparse_work_counts_masked_keys_by_hand():
+    # one sequence of 2 rows over 8 original keys, ratio 2 (4 compressed),
+    # window (1, 0): row i sits at p = i + 6 and sees originals {5, 6} / {6, 7}
+    # and compressed positions up to i + 4 - 2, i.e. {0..2} / {0..3}
+    base = dict(lens_q=[2], seqused_kv=[8], H=4, Hkv=2, D=64, window=(1, 0), cmp_ratio=2, ori_bs=4, cmp_bs=4,
+                seed=1)
+    sc = W.sparse_case(**base, topk=0, cmp_all=True)
+    fl, by = bench.sparse_work(sc)
+    g, D, T, H = 2, 64, 2, 4
+    keys = 2 * (4 + 7)                     # per kv head: 4 window + 7 compressed
+    assert fl == 4.0 * D * g * keys
+    rows = 2 * (3 + 4)                     # distinct originals {5, 6, 7}, compressed {0..3}
+    tables = sc["ori_table"].size + sc["cmp_table"].size
+    assert by == 2.0 * T * H * D * 2 + 4.0 * T * H + 4.0 * tables + rows * D * 2
+    # indices: 3 for row 0 (one past its bound), 3 for row 1 (one invalid)
+    sc = W.sparse_case(**base, topk=3)
+    sc["indices"][0] = [[0, 3, 2], [1, 1, 0]]
+    sc["indices"][1] = [[3, -1, 3], [4, 2, 0]]
+    fl, by = bench.sparse_work(sc)
+    # per kv head 0: row 0 {0, 2}, row 1 {3, 3}; kv head 1: row 0 {1, 1, 0}, row 1 {2, 0}
+    keys = 2 * 4 + (2 + 2) + (3 + 2)
+    assert fl == 4.0 * D * g * keys
+    rows = 2 * 3 + len({0, 2, 3}) + len({0, 1, 2})
+    assert by == 2.0 * T * H * D * 2 + 4.0 * T * H + 4.0 * sc["indices"].size + 4.0 * tables + rows * D * 2

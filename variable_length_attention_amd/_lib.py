@@ -51,7 +51,7 @@ class VaSparseProblem(ctypes.Structure):
         "struct_size", "dtype", "batch", "total_q", "num_heads", "num_kv_heads", "head_dim",
         "max_seqlen_kv", "scale", "window_left", "window_right", "topk", "cmp_ratio",
         "ori_num_blocks", "ori_block_size", "ori_block_table_stride",
-        "cmp_num_blocks", "cmp_block_size", "cmp_block_table_stride")]
+        "cmp_num_blocks", "cmp_block_size", "cmp_block_table_stride", "cmp_attend_all")]
 
 
 _lock = threading.Lock()

@@ -388,12 +388,16 @@ def varlen_attn_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, sinks: 
 def varlen_attn_sparse_sharedkv(q, ori_kv, ori_block_table, seqused_kv, cmp_kv, cmp_block_table,
                                 cmp_sparse_indices, cu_seqlens_q, max_seqlen_kv: int, *,
                                 scale: Optional[float] = None, window: Tuple[int, int] = (127, 0),
-                                cmp_ratio: int = 4, sinks=None, out=None, lse=None, return_lse: bool = False):
-    """Sliding-window + sparse compressed attention over shared K/V.
+                                cmp_ratio: int = 4, cmp_attend_all: bool = False, sinks=None, out=None, lse=None,
+                                return_lse: bool = False):
+    """Sliding-window + compressed attention over shared K/V (the three
+    scenarios of the SparseAttnSharedkv README).
     q [total_q, H, D] bf16 / f16; ori_kv / cmp_kv paged caches
     [blocks, block_size, H_kv, D]; block tables int32 [batch, stride];
     seqused_kv int32 [batch]; cmp_sparse_indices int32 [total_q, H_kv, topk]
-    (or None for none); cu_seqlens_q int32 [batch + 1]."""
+    (or None); cu_seqlens_q int32 [batch + 1].  cmp_attend_all=True (indices
+    None) attends to every compressed key the causal compressed mask admits;
+    otherwise to the indexed ones it admits (none: window only)."""
     dev = _check_tensors(q, ori_kv, ori_block_table, seqused_kv, cmp_kv, cmp_block_table, cmp_sparse_indices,
                          cu_seqlens_q, sinks, out, lse)
     _need(q.dim() == 3 and q.dtype in (torch.bfloat16, torch.float16), "q must be bf16 / f16 [total_q, H, D]")
@@ -409,6 +413,8 @@ def varlen_attn_sparse_sharedkv(q, ori_kv, ori_block_table, seqused_kv, cmp_kv, 
         _need(cmp_sparse_indices.dtype == torch.int32 and cmp_sparse_indices.dim() == 3 and
               tuple(cmp_sparse_indices.shape[:2]) == (q.shape[0], ori_kv.shape[2]),
               "cmp_sparse_indices must be int32 [total_q, num_kv_heads, topk]")
+    _need(not (cmp_attend_all and cmp_sparse_indices is not None),
+          "cmp_attend_all attends to every visible compressed key: pass no cmp_sparse_indices")
     p = _lib.VaSparseProblem()
     p.struct_size = ctypes.sizeof(_lib.VaSparseProblem)
     p.dtype = _DTYPES[q.dtype]
@@ -417,7 +423,7 @@ def varlen_attn_sparse_sharedkv(q, ori_kv, ori_block_table, seqused_kv, cmp_kv, 
     p.max_seqlen_kv = int(max_seqlen_kv)
     p.scale = float(1.0 / math.sqrt(q.shape[2]) if scale is None else scale)
     p.window_left, p.window_right = int(window[0]), int(window[1])
-    p.topk, p.cmp_ratio = topk, int(cmp_ratio)
+    p.topk, p.cmp_ratio, p.cmp_attend_all = topk, int(cmp_ratio), int(bool(cmp_attend_all))
     p.ori_num_blocks, p.ori_block_size, p.ori_block_table_stride = (int(ori_kv.shape[0]), int(ori_kv.shape[1]),
                                                                     int(ori_block_table.shape[1]))
     p.cmp_num_blocks, p.cmp_block_size, p.cmp_block_table_stride = (int(cmp_kv.shape[0]), int(cmp_kv.shape[1]),

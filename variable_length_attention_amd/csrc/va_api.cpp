@@ -637,9 +637,16 @@ va_status varlen_attn_sparse_sharedkv(const va_sparse_problem *p, const void *q,
                                       const float *sinks, void *out, float *lse, void *stream)
 {
     if (!p) return fail(VA_ERR_NULL, "problem descriptor is NULL");
-    if (p->struct_size < sizeof(va_sparse_problem))
+    // descriptors of ABI 4 end before cmp_attend_all, which then reads as 0
+    constexpr size_t kSparseV4Size = offsetof(va_sparse_problem, cmp_attend_all);
+    if (p->struct_size < kSparseV4Size)
         return fail(VA_ERR_SHAPE, "va_sparse_problem.struct_size %u is smaller than %zu", p->struct_size,
-                    sizeof(va_sparse_problem));
+                    kSparseV4Size);
+    const int32_t attend_all = p->struct_size >= sizeof(va_sparse_problem) ? p->cmp_attend_all : 0;
+    if (attend_all != 0 && attend_all != 1)
+        return fail(VA_ERR_SHAPE, "cmp_attend_all %d is not 0 or 1", attend_all);
+    if (attend_all && (p->topk != 0 || cmp_sparse_indices))
+        return fail(VA_ERR_SHAPE, "cmp_attend_all takes no cmp_sparse_indices (topk %d)", p->topk);
     if (p->dtype != VA_BF16 && p->dtype != VA_F16)
         return fail(VA_ERR_DTYPE, "dtype %d is not VA_BF16 (1) or VA_F16 (2)", p->dtype);
     if (p->batch < 1 || p->total_q < 1) return fail(VA_ERR_SHAPE, "batch and total_q must be >= 1");
@@ -651,10 +658,10 @@ va_status varlen_attn_sparse_sharedkv(const va_sparse_problem *p, const void *q,
     if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 512)
         return fail(VA_ERR_UNSUPPORTED, "head_dim %d is not 64, 128 or 512", p->head_dim);
     if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return fail(VA_ERR_UNSUPPORTED, "scale must be finite and > 0");
-    if (p->window_left < 0 || p->window_right < 0 || p->topk < 0 ||
-        (long long)p->window_left + p->window_right + 1 + p->topk > va::kSpListMax)
-        return fail(VA_ERR_UNSUPPORTED, "window (%d, %d) must be bounded and window + topk %d at most %d keys",
-                    p->window_left, p->window_right, p->topk, va::kSpListMax);
+    if (p->window_left < 0 || p->window_right < 0)
+        return fail(VA_ERR_UNSUPPORTED, "window sides (%d, %d) must be >= 0 (2^30 and above: unbounded)",
+                    p->window_left, p->window_right);
+    if (p->topk < 0) return fail(VA_ERR_SHAPE, "topk %d < 0", p->topk);
     if (p->cmp_ratio < 1) return fail(VA_ERR_SHAPE, "cmp_ratio %d < 1", p->cmp_ratio);
     if (p->max_seqlen_kv < 0 || p->max_seqlen_kv > va::kMaxSeqlen)
         return fail(VA_ERR_SHAPE, "max_seqlen_kv %d outside [0, %d]", p->max_seqlen_kv, va::kMaxSeqlen);
@@ -698,7 +705,7 @@ va_status varlen_attn_sparse_sharedkv(const va_sparse_problem *p, const void *q,
     a.cmp_kv = cmp_kv; a.cmp_table = cmp_block_table; a.indices = cmp_sparse_indices; a.cu_q = cu_seqlens_q;
     a.sinks = sinks; a.out = out; a.lse = lse;
     a.B = p->batch; a.T = p->total_q; a.H = p->num_heads; a.Hkv = p->num_kv_heads;
-    a.g = p->num_heads / p->num_kv_heads; a.topk = p->topk;
+    a.g = p->num_heads / p->num_kv_heads; a.topk = p->topk; a.cmp_all = attend_all;
     a.ori_bs = p->ori_block_size; a.ori_stride = p->ori_block_table_stride;
     a.cmp_bs = p->cmp_block_size; a.cmp_stride = p->cmp_block_table_stride; a.cmp_ratio = p->cmp_ratio;
     a.ori_shift = a.cmp_shift = -1;
@@ -706,7 +713,7 @@ va_status varlen_attn_sparse_sharedkv(const va_sparse_problem *p, const void *q,
         if ((1 << sh) == a.ori_bs) a.ori_shift = sh;
         if ((1 << sh) == a.cmp_bs) a.cmp_shift = sh;
     }
-    a.left = p->window_left; a.right = p->window_right;
+    a.left = std::min(p->window_left, va::kInfOff); a.right = std::min(p->window_right, va::kInfOff);
     a.scale_log2 = p->scale * va::kLog2e;
     // tokens per workgroup: the fewest that keep the grid within whole rounds
     // of 1024 workgroups (4 per CU of 2 waves each), 1 to kSpTokMax each

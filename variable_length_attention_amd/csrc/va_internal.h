@@ -104,7 +104,7 @@ struct BwdArgs {
 // Sliding-window + sparse compressed attention over shared K/V (the
 // third scenario of the SparseAttnSharedkv README).
 constexpr int kSpTokMax = 16;    // tokens per workgroup, at most
-constexpr int kSpListMax = 1536; // window + selected keys per token, at most (a multiple of 128 and of the 64-key tile)
+constexpr int kSpListMax = 1536; // keys of one chunk of a token's list (a multiple of 128 and of the 64-key tile)
 struct SparseArgs {
     const void *q;                   // [T_q, H, D]
     const void *ori_kv;              // [ori_blocks, ori_bs, Hkv, D], K = V
@@ -118,6 +118,7 @@ struct SparseArgs {
     void *out;                       // [T_q, H, D]
     float *lse;                      // [T_q, H] or null
     int32_t B, T, H, Hkv, g, topk;
+    int32_t cmp_all;                 // 1: every visible compressed key, no indices
     int32_t tok_per_wg;              // consecutive tokens per workgroup
     int32_t ori_bs, ori_stride, cmp_bs, cmp_stride, cmp_ratio;
     int32_t ori_shift, cmp_shift;    // log2 of ori_bs / cmp_bs when a power of two, else -1

@@ -4,13 +4,19 @@
 // keys its sparse indices select, in one softmax, with per-head sinks; the
 // same tensor rows serve as keys and values).
 //
-// Per token t of sequence b, kv head c, the key list is
-//   window:   original positions [p - left, p + right] within [0, S2_b),
-//             p = i + S2_b - Lq_b (aligned to the end of the keys),
-//   selected: compressed positions cmp_sparse_indices[t, c, 0 .. topk-1],
-//             those outside [0, S2_b / cmp_ratio) select nothing;
+// Per token t (row i of sequence b), kv head c, the key list is
+//   window:     original positions [p - left, p + right] within [0, S2_b),
+//               p = i + S2_b - Lq_b (aligned to the end of the keys),
+//   compressed: with cmp_all (the README's second scenario) every position
+//               t' of the S3_b = S2_b / cmp_ratio compressed keys that the
+//               mask admits, t' <= i + S3_b - Lq_b (causal, aligned to the
+//               bottom-right of the Lq x S3 matrix); otherwise the positions
+//               cmp_sparse_indices[t, c, 0 .. topk-1] (third scenario),
+//               those outside [0, S3_b) or past that bound selecting nothing;
 // and for each of the g query heads h of c
 //   O[t, h] = softmax_j(scale <q[t, h], kv_j>, sink_h) . kv_j.
+// Lists longer than the LDS list (kSpListMax keys) are taken in chunks of
+// it, the running max / sum / O carried from chunk to chunk.
 //
 // One workgroup = 2 waves = up to 64 query heads of one kv head (heads on
 // the MFMA N side: each lane owns one head), a few consecutive tokens in
@@ -209,23 +215,52 @@ void k5_sparse16(SparseArgs a)
         const int win_lo = a.left >= kInfOff ? 0 : max(0, p - a.left);
         const int win_hi = a.right >= kInfOff ? S2 - 1 : min(S2 - 1, p + a.right);
         const int nwin = max(0, win_hi - win_lo + 1);
-        const int L = nwin + a.topk;                 // <= kSpListMax (checked on the host)
-        const int ntiles = (L + BN - 1) / BN;
+        const int last = i + S3 - Lq;  // last compressed position row i sees (< S3)
+        const int L = nwin + (a.cmp_all ? max(0, min(S3, last + 1)) : a.topk);
 
-        // physical rows of the key list, in two rounds of independent loads
-        // (the indices, then the block-table entries they name): thread tid
-        // takes keys tid, tid + 128, ...
+        // Q^T operand fragments: lane (head n, half h2) holds d = 16 ks + 8 h2 .. +8
+        v8 qf[KS];
+        {
+            const uint16_t *qp = (const uint16_t *)a.q + ((size_t)t * a.H + head) * D + h2 * 8;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 x = *(const u32x4 *)(qp + ks * 16);
+                if (!head_ok) x = u32x4{0, 0, 0, 0};
+                qf[ks] = __builtin_bit_cast(v8, x);
+            }
+        }
+        f32x16 o[MD];
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[md][v] = 0.f;
+            if constexpr (BIG) in_agpr(o[md]);
+        }
+        float m_run = sink2, l_run = (sink2 != -INFINITY && h2 == 0) ? 1.f : 0.f;
+
+        // the key list in chunks of at most kSpListMax keys
+        for (int base = 0; base < L; base += kSpListMax) {
+        const int Lc = min(L - base, kSpListMax);
+        const int ntiles = (Lc + BN - 1) / BN;
+
+        // physical rows of the chunk's keys, in two rounds of independent
+        // loads (the indices, then the block-table entries they name): thread
+        // tid takes keys base + tid, base + tid + 128, ...
         constexpr int KPT = kSpListMax / 128;
         static_assert(kSpListMax % 128 == 0, "whole rounds of 128 keys");
         int pos[KPT];   // position within its cache, -1: selects nothing
 #pragma unroll
         for (int k = 0; k < KPT; ++k) {
-            const int kk = tid + 128 * k;
+            const int kg = base + tid + 128 * k;
             pos[k] = -1;
-            if (kk < nwin) pos[k] = win_lo + kk;
-            else if (kk < L) {
-                const int idx = a.indices[((size_t)t * a.Hkv + c) * a.topk + (kk - nwin)];
-                pos[k] = (idx >= 0 && idx < S3) ? idx : -1;
+            if (kg < nwin) pos[k] = win_lo + kg;
+            else if (tid + 128 * k < Lc) {
+                if (a.cmp_all) {
+                    pos[k] = kg - nwin;
+                } else {
+                    const int idx = a.indices[((size_t)t * a.Hkv + c) * a.topk + (kg - nwin)];
+                    pos[k] = (idx >= 0 && idx <= last) ? idx : -1;
+                }
             }
         }
         // block and slot of a position: shifts for power-of-two block sizes
@@ -241,34 +276,24 @@ void k5_sparse16(SparseArgs a)
         int blk[KPT];
 #pragma unroll
         for (int k = 0; k < KPT; ++k) {
-            const int kk = tid + 128 * k;
+            const int kg = base + tid + 128 * k;
             blk[k] = 0;
             if (pos[k] >= 0)
-                blk[k] = kk < nwin ? a.ori_table[(size_t)b * a.ori_stride + blk_of(pos[k], true)]
+                blk[k] = kg < nwin ? a.ori_table[(size_t)b * a.ori_stride + blk_of(pos[k], true)]
                                    : a.cmp_table[(size_t)b * a.cmp_stride + blk_of(pos[k], false)];
         }
-        // entries up to the end of the last tile (-1 past L); whether any
-        // key of the token selects nothing decides if its tiles are masked
+        // entries up to the end of the chunk's last tile (-1 past its end);
+        // whether any key of the chunk selects nothing decides if its tiles
+        // are masked
         bool none_here = false;
 #pragma unroll
         for (int k = 0; k < KPT; ++k) {
-            const int kk = tid + 128 * k;
+            const int kk = tid + 128 * k, kg = base + kk;
             if (kk < ntiles * BN) {
-                const int bs = kk < nwin ? a.ori_bs : a.cmp_bs;
-                const int row = pos[k] >= 0 ? blk[k] * bs + slot_of(pos[k], kk < nwin) : -1;
+                const int bs = kg < nwin ? a.ori_bs : a.cmp_bs;
+                const int row = pos[k] >= 0 ? blk[k] * bs + slot_of(pos[k], kg < nwin) : -1;
                 s_list[kk] = row;
                 none_here |= row < 0;
-            }
-        }
-        // Q^T operand fragments: lane (head n, half h2) holds d = 16 ks + 8 h2 .. +8
-        v8 qf[KS];
-        {
-            const uint16_t *qp = (const uint16_t *)a.q + ((size_t)t * a.H + head) * D + h2 * 8;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                u32x4 x = *(const u32x4 *)(qp + ks * 16);
-                if (!head_ok) x = u32x4{0, 0, 0, 0};
-                qf[ks] = __builtin_bit_cast(v8, x);
             }
         }
         const bool masked = __syncthreads_or(none_here);  // the list is complete
@@ -282,28 +307,19 @@ void k5_sparse16(SparseArgs a)
 #pragma unroll
             for (int u = 0; u < LPW; ++u) {
                 const int r = (wave * LPW + u) * RPI + lane / NCH;
-                const int kk = tau * BN + r;
+                const int kg = base + tau * BN + r;
                 const int row = rows[u];
-                const char *base = (const char *)(kk < nwin ? a.ori_kv : a.cmp_kv);
+                const char *src = (const char *)(kg < nwin ? a.ori_kv : a.cmp_kv);
                 const int chunk = (lane % NCH) ^ swz<D>(r);
                 // a key that selects nothing re-reads row 0 of the original
                 // cache (finite data under a -inf bias)
                 const size_t off = ((size_t)(row >= 0 ? row : 0) * a.Hkv + c) * ROWB + chunk * 16;
-                copy16_global((row >= 0 ? base : (const char *)a.ori_kv) + off,
+                copy16_global((row >= 0 ? src : (const char *)a.ori_kv) + off,
                               lds_addr(s_tile + slot * TILEB + (wave * LPW + u) * 1024));
             }
         };
 
-        f32x16 o[MD];
-#pragma unroll
-        for (int md = 0; md < MD; ++md) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) o[md][v] = 0.f;
-            if constexpr (BIG) in_agpr(o[md]);
-        }
-        float m_run = sink2, l_run = (sink2 != -INFINITY && h2 == 0) ? 1.f : 0.f;
-
-        if (ntiles > 0) issue(0, 0);
+        issue(0, 0);
         wait_vmem();
         __syncthreads();
         for (int tau = 0; tau < ntiles; ++tau) {
@@ -393,6 +409,7 @@ void k5_sparse16(SparseArgs a)
             wait_vmem();
             __syncthreads();
         }
+        }  // chunks of the key list
 
         // epilogue: lane (head n, half h2) holds O^T[32 md + 8 i + 4 h2 + j]
         if constexpr (BIG) {
