@@ -54,6 +54,7 @@ KERNEL_SOURCES = {
     "decode_bf16": ["va_decode.hip"],
     "f32": ["va_prefill_f32.hip"],
     "window_bf16": ["va_window.hip"],
+    "sparse": ["va_sparse.hip"],
 }
 PATH_NAMES = ["prefill_bf16", "decode_bf16", "f32", "window_bf16"]  # index = varlen_attn_path
 
@@ -350,6 +351,81 @@ def measured_traffic(path_name, workload):
     return rec["hbm_bytes_per_launch"]
 
 
+def _profile_rows(csv_path, kernel_regex):
+    import csv
+    import re
+    rx = re.compile(kernel_regex)
+    with open(csv_path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            if rx.search(r["Kernel_Name"]):
+                yield r
+
+
+def counter_means(csv_path, kernel_regex):
+    """{counter: (mean per dispatch, dispatches)} over the dispatches of the
+    kernels matching kernel_regex in a rocprofv3 counter_collection CSV."""
+    per = {}
+    for r in _profile_rows(csv_path, kernel_regex):
+        d = per.setdefault(r["Counter_Name"], {})
+        d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return {c: (sum(v.values()) / len(v), len(v)) for c, v in per.items()}
+
+
+def trace_summary(path, kernel_regex=".", last=20):
+    """Per kernel (name, grid): dispatches and average / min / max duration
+    in microseconds from a rocprofv3 kernel trace (its CSV, or the SQLite
+    results database it writes by default), and the average over the last
+    `last` dispatches (the timed graph replay of a benchmark step)."""
+    import re
+    rx = re.compile(kernel_regex)
+    out = {}
+    if path.endswith(".db"):
+        import sqlite3
+        con = sqlite3.connect(path)
+        rows = con.execute("select name, grid_x, start, end from kernels order by start").fetchall()
+        con.close()
+        for name, grid, t0, t1 in rows:
+            if rx.search(name):
+                out.setdefault((name, int(grid)), []).append((t1 - t0) / 1e3)
+    else:
+        rows = sorted(_profile_rows(path, kernel_regex), key=lambda r: int(r["Start_Timestamp"]))
+        for r in rows:
+            key = (r["Kernel_Name"], int(r.get("Grid_Size") or r.get("Grid_Size_X") or 0))
+            out.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return {k: {"n": len(v), "avg_us": sum(v) / len(v), "min_us": min(v), "max_us": max(v),
+                "last_avg_us": sum(v[-last:]) / len(v[-last:])} for k, v in out.items()}
+
+
+def record_traffic(key, kernel_regex, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
+                   copy_bytes=1 << 30):
+    """Stores in profiles/traffic.json the HBM bytes per launch of the
+    kernels matching kernel_regex, from FETCH_SIZE and WRITE_SIZE runs
+    (KiB per dispatch), each scaled by what the same counter reads for a
+    plain device copy of copy_bytes (which reads and writes copy_bytes);
+    keyed by the hash of the kernel's own sources (key = path/workload)."""
+    path_name = key.split("/")[0]
+    f = counter_means(fetch_csv, kernel_regex)["FETCH_SIZE"]
+    w = counter_means(write_csv, kernel_regex)["WRITE_SIZE"]
+    cf = counter_means(copy_fetch_csv, "copyBuffer")["FETCH_SIZE"][0]
+    cw = counter_means(copy_write_csv, "copyBuffer")["WRITE_SIZE"][0]
+    fs, ws = copy_bytes / 1024.0 / cf, copy_bytes / 1024.0 / cw
+    rec = {"source_sha256": kernel_source_sha(path_name), "kernel_regex": kernel_regex,
+           "fetch_kib_raw": f[0], "write_kib_raw": w[0], "fetch_scale": fs, "write_scale": ws,
+           "fetch_bytes_per_launch": f[0] * fs * 1024.0, "write_bytes_per_launch": w[0] * ws * 1024.0,
+           "dispatches": [f[1], w[1]]}
+    rec["hbm_bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    fn = os.path.join(ROOT, "profiles", "traffic.json")
+    data = {}
+    if os.path.exists(fn):
+        with open(fn) as fh:
+            data = json.load(fh)
+    data[key] = rec
+    with open(fn, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    return rec
+
+
 def calibrate_copy(nbytes, reps):
     """A plain device copy of known size, for scaling the FETCH_SIZE /
     WRITE_SIZE counters (each copy reads and writes nbytes)."""
@@ -508,7 +584,24 @@ def main():
                     help="only measure a large bf16 GEMM and a large read-only reduction")
     ap.add_argument("--calibrate-mfma", type=int, default=0, metavar="ITERS",
                     help="only run the matrix-core stream probe (ITERS groups of 4 products per wave)")
+    ap.add_argument("--record-traffic", nargs=6, metavar=("KEY", "KERNEL_REGEX", "FETCH_CSV", "WRITE_CSV",
+                                                          "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="(no GPU) store a kernel's HBM bytes per launch from rocprofv3 counter CSVs")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("CSV", "KERNEL_REGEX"),
+                    help="(no GPU) per-dispatch counter means of matching kernels, as JSON")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("CSV", "KERNEL_REGEX"),
+                    help="(no GPU) dispatch durations of matching kernels from a kernel trace, as JSON lines")
     args = ap.parse_args()
+    if args.record_traffic:
+        print(json.dumps(record_traffic(*args.record_traffic)))
+        return
+    if args.counter_summary:
+        print(json.dumps(counter_means(*args.counter_summary)))
+        return
+    if args.trace_summary:
+        for (name, grid), s in trace_summary(*args.trace_summary).items():
+            print(json.dumps(dict(kernel=name, grid=grid, **s)))
+        return
     if args.calibrate_mfma:
         calibrate_mfma(args.calibrate_mfma)
         return
@@ -645,9 +738,9 @@ def main():
                             f"4 x 1024 tokens over 8192 keys, 64 heads / 1 kv head, d{D}, bf16",
                 "ms_per_step": ms_s, "tflops": tf_s, "gbs": gb_s, "flop": fl_s, "bytes": by_s,
                 "roofline": ({"bound": "hbm", "achieved": gb_s, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                              "frac": gb_s / PEAK_HBM_GBS, "traffic": None} if hbm else
+                              "frac": gb_s / PEAK_HBM_GBS, "traffic": measured_traffic("sparse", key)} if hbm else
                              {"bound": "mfma", "achieved": tf_s, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                              "frac": tf_s / PEAK_BF16_TFLOPS, "traffic": None})}
+                              "frac": tf_s / PEAK_BF16_TFLOPS, "traffic": measured_traffic("sparse", key)})}
             log(f"{key}: {ms_s:.4f} ms/call, {tf_s:.1f} TFLOP/s, {gb_s:.0f} GB/s (algorithmic)")
     if not args.no_cpu_baseline:
         # the main workload's oracle rate, and the oracle on every workload

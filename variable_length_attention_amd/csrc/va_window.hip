@@ -20,6 +20,8 @@
 // and 2 rows run at once (32 heads: 1 wave per row, 4 rows at once).
 #include "va_internal.h"
 
+#include <type_traits>
+
 namespace va {
 
 namespace {
@@ -105,13 +107,12 @@ __device__ __forceinline__ void pin(V &x)
 
 // The O accumulators hold O[head][d] with lane (n, h2) <-> d = 32 md + n and
 // register v <-> head (v/4) 8 + 4 h2 + v%4.  Per-head scalars live one head
-// per lane (lanes h and h + 32); this returns the one of register v's head.
+// per lane (lanes h and h + 32); this gives every lane register v's one: an
+// LDS-crossbar permute (no LDS memory, no vector ALU work) from lane
+// (v/4) 8 + 4 h2 + v%4.
 __device__ __forceinline__ float head_value(float x, int v, int h2)
 {
-    const int hh = (v >> 2) * 8 + (v & 3);
-    const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), hh));
-    const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), hh + 4));
-    return h2 ? hi : lo;
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(h2 * 16 + 4 * ((v >> 2) * 8 + (v & 3)), __float_as_int(x)));
 }
 
 __device__ __forceinline__ float halves_max(float x)
@@ -184,9 +185,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     // Q^T operand fragments of block row r (clamped to the block): lane
     // (head n, half h2) holds d = 16 ks + 8 h2 .. +8 (lanes past the group
-    // read head 0; their results are never stored).  Each row's are loaded
-    // before the previous row's stores: loads and stores share one counter,
-    // so the wait for them then leaves the stores in flight.
+    // read head 0; their results are never stored).  A row's fragments are
+    // loaded when the wave starts its previous row, so their latency hides
+    // behind a whole row of work; loads and stores share one counter, and
+    // the wait for them leaves the stores issued after them in flight.
     auto load_q = [&](int r, v8 (&dst)[KS]) {
         const size_t tq = (size_t)q0 + i0 + min(r, rows_here - 1);
         const uint16_t *qp = (const uint16_t *)a.q + (tq * a.H + head) * D + h2 * 8;
@@ -200,27 +202,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
 
     for (int r = wave / wpr; r < rows_here; r += rif) {
+        v8 qn[KS];
+        load_q(r + rif, qn);
         const int i = i0 + r;
         const int p = i + delta;
         const int kst = max(0, p - a.left);
         const int ken = min(Lk - 1, p + a.right);
         const int nk = max(0, ken - kst + 1);
-        const int ntiles = (nk + 63) / 64;
         const int base = kst - kv_lo;            // LDS row of the row's first key
         const size_t t = (size_t)q0 + i;
         // byte offsets within a row: K operand chunk 2 ks + h2 of a row
         // congruent to base + n (mod 16); V^T chunk 4 md + 2 ((lane & 31) >> 4)
-        // + ((l16 & 3) >> 1) of a row congruent to base + 4 h2 + q4 + 8 half
+        // + ((l16 & 3) >> 1) of a row congruent to base + 4 h2 + q4 + 8 half.
+        // A tile step of 64 rows keeps a row's residue mod 16, so these hold
+        // for every tile of the row.
         const int kx = swz<D>(base + n);
         const int vx0 = swz<D>(base + h2 * 4 + q4), vx1 = swz<D>(base + h2 * 4 + q4 + 8);
-        auto kofs = [&](int ks) -> uint32_t { return ((ks * 2 + h2) ^ kx) << 4; };
-        auto vofs = [&](int md, int half) -> uint32_t {
-            const int ch = md * 4 + ((lane & 31) >> 4) * 2 + ((l16 & 3) >> 1);
-            return ((ch ^ (half ? vx1 : vx0)) << 4) | ((l16 & 1) * 8);
-        };
-        // LDS row of a key, clamped to the allocation (a clamped row only
-        // serves keys past the row's window, whose weight is 0)
-        auto rowb = [&](int rr) -> uint32_t { return (uint32_t)min(rr, CAP - 1) * ROWB; };
+        uint32_t kofs[KS], vofs[MD][2];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kofs[ks] = ((ks * 2 + h2) ^ kx) << 4;
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int ch = md * 4 + ((lane & 31) >> 4) * 2 + ((l16 & 3) >> 1);
+                vofs[md][half] = ((ch ^ (half ? vx1 : vx0)) << 4) | ((l16 & 1) * 8);
+            }
 
         f32x16 o[MD];
 #pragma unroll
@@ -229,8 +236,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int v = 0; v < 16; ++v) o[md][v] = 0.f;
         float m_run = sink2, l_run = (sink2 != -INFINITY && h2 == 0) ? 1.f : 0.f;
 
-        for (int tau = 0; tau < ntiles; ++tau) {
+        // one 64-key tile at LDS row base + 64 tau.  FULL: all 64 keys are in
+        // the row's window, so no key is masked and every row read is below
+        // nwin <= CAP (whole-row offsets then fold into the instructions'
+        // immediates).  Otherwise the window's last, partial tile: keys past
+        // it get a -inf score and reads clamp to the allocation (a clamped
+        // row only serves such keys).
+        auto tile = [&](int tau, auto full) {
+            constexpr bool FULL = decltype(full)::value == 1;
             const int tb = base + tau * 64;
+            // the row's offsets enter each tile as they are (both kinds of
+            // tile share them; a tile adds its own row base to each)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) pin(kofs[ks]);
+#pragma unroll
+            for (int md = 0; md < MD; ++md) {
+                pin(vofs[md][0]);
+                pin(vofs[md][1]);
+            }
+            auto rowb = [&](int rr) -> uint32_t { return (uint32_t)min(rr, CAP - 1) * ROWB; };
+            // operand addresses: in a full tile one register per K chunk and
+            // per V^T chunk, the row steps within the tile in the
+            // instructions' immediates; in the partial tile per clamped row
+            const char *kp[KS], *vp[MD][2];
+            if constexpr (FULL) {
+                const char *kt = s_k + (tb + n) * ROWB;
+                const char *vt = s_v + (tb + h2 * 4 + q4) * ROWB;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) kp[ks] = kt + kofs[ks];
+#pragma unroll
+                for (int md = 0; md < MD; ++md) {
+                    vp[md][0] = vt + vofs[md][0];
+                    vp[md][1] = vt + vofs[md][1];
+                }
+            }
             // S^T = K Q^T: lane value v of block mb is key 64 tau + 32 mb + 8 (v/4) + 4 h2 + v%4
             f32x16 S[2];
 #pragma unroll
@@ -238,21 +277,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int v = 0; v < 16; ++v) S[mb][v] = 0.f;
                 // the block's K operands in one batch of reads, then the products
-                const char *kr = s_k + rowb(tb + mb * 32 + n);
                 v8 kf[KS];
+                if constexpr (FULL) {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const v8 *)(kr + kofs(ks));
+                    for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const v8 *)(kp[ks] + mb * 32 * ROWB);
+                } else {
+                    const char *kr = s_k + rowb(tb + mb * 32 + n);
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const v8 *)(kr + kofs[ks]);
+                }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) pin(kf[ks]);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) S[mb] = E::mfma(kf[ks], qf[ks], S[mb]);
             }
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) S[mb][v] *= a.scale_log2;
-            if (tau * 64 + 64 > nk) {
-                // the last tile of a window that is not a multiple of 64 keys
+            if constexpr (!FULL) {
                 const int lim = nk - tau * 64 - 4 * h2;
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
@@ -260,6 +299,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     for (int v = 0; v < 16; ++v)
                         S[mb][v] = mb * 32 + 8 * (v >> 2) + (v & 3) >= lim ? -INFINITY : S[mb][v];
             }
+            // the max of the unscaled scores, scaled once (scale > 0 keeps
+            // the order); the scale then rides in the exponent's FMA
             float mx = -INFINITY;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
@@ -268,7 +309,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // the running max moves only when a tile raises it by more than
             // 2^8 (log2 units) for some head: until then the probabilities
             // stay below 2^8 and the O / l rescale is skipped
-            mx = halves_max(mx);
+            mx = halves_max(mx) * a.scale_log2;
             if (__ballot(mx > m_run + 8.f) != 0ull) {
                 const float m_new = fmaxf(m_run, mx);
                 const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -281,13 +322,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 }
                 m_run = m_new;
             }
-            const float m_use = m_run == -INFINITY ? 0.f : m_run;
+            const float m_neg = m_run == -INFINITY ? 0.f : -m_run;
             float rs = 0.f;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const float pr = __builtin_amdgcn_exp2f(S[mb][v] - m_use);
+                    const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[mb][v], a.scale_log2, m_neg));
                     S[mb][v] = pr;
                     rs += pr;
                 }
@@ -301,28 +342,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int e = 0; e < 8; ++e) pv[e] = S[t4 >> 1][(t4 & 1) * 8 + e];
                 const v8 pb = __builtin_convertvector(pv, v8);
-                const char *v0 = s_v + rowb(tb + t4 * 16 + h2 * 4 + q4);
-                const char *v1 = s_v + rowb(tb + t4 * 16 + h2 * 4 + q4 + 8);
                 v8 vf[MD];
+                if constexpr (FULL) {
 #pragma unroll
-                for (int md = 0; md < MD; ++md) {
-                    const v4 va = E::read_tr(v0 + vofs(md, 0));
-                    const v4 vb = E::read_tr(v1 + vofs(md, 1));
-                    vf[md] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+                    for (int md = 0; md < MD; ++md) {
+                        const v4 va = E::read_tr(vp[md][0] + t4 * 16 * ROWB);
+                        const v4 vb = E::read_tr(vp[md][1] + (t4 * 16 + 8) * ROWB);
+                        vf[md] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+                    }
+                } else {
+                    const char *v0 = s_v + rowb(tb + t4 * 16 + h2 * 4 + q4);
+                    const char *v1 = s_v + rowb(tb + t4 * 16 + h2 * 4 + q4 + 8);
+#pragma unroll
+                    for (int md = 0; md < MD; ++md) {
+                        const v4 va = E::read_tr(v0 + vofs[md][0]);
+                        const v4 vb = E::read_tr(v1 + vofs[md][1]);
+                        vf[md] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+                    }
                 }
 #pragma unroll
                 for (int md = 0; md < MD; ++md) pin(vf[md]);
 #pragma unroll
                 for (int md = 0; md < MD; ++md) o[md] = E::mfma(pb, vf[md], o[md]);
             }
+        };
+        // (the first full tile is written out on its own: the register
+        // allocation of the loop then fits without spills)
+        const int nfull = nk >> 6;
+        if (nfull > 0) {
+            tile(0, std::integral_constant<int, 1>{});
+            for (int tau = 1; tau < nfull; ++tau) tile(tau, std::integral_constant<int, 1>{});
         }
+        if (nk & 63) tile(nfull, std::integral_constant<int, 0>{});
 
-        load_q(r + rif, qf);   // the next row's fragments (qf is not read again)
 
         // epilogue: register v of lane (n, h2) holds O[head (v/4) 8 + 4 h2 +
-        // v%4][32 md + n].  Neighbour lanes trade values (heads h, h + 1 at
-        // d = n, n + 1) so that each lane stores two consecutive d of one
-        // head: every store covers 64 contiguous bytes of 4 heads.  Buffer
+        // v%4][32 md + n].  Each lane packs its two heads h, h + 1 at d = n
+        // into one word, neighbour lanes trade the words and each keeps the
+        // halves of one head (h at d = n, n + 1 on even lanes, h + 1 at
+        // d = n - 1, n on odd ones): every store covers 64 contiguous bytes
+        // of 4 heads.  Buffer
         // stores over this row's heads of the group: the range check drops
         // heads past the group (and every LSE lane when lse is NULL), so no
         // branch splits the stores from the loads above.
@@ -334,23 +393,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
             (char *)a.out + (t * a.H + (size_t)c * a.g) * D * 2, (short)0, a.g * D * 2, 0x00020000);
         const bool odd = n & 1;
+        // byte selectors of v_perm (bytes 0-3: own word, 4-7: the neighbour's)
+        const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+        // the lane's store offset (its head parity and half, its pair of d);
+        // each store adds a constant (kept in the instruction and in an
+        // SGPR offset rather than in a register per store across rows)
+        uint32_t obase = (uint32_t)((((wave % wpr) * 32 + 4 * h2 + (odd ? 1 : 0)) * D + (n & ~1)) * 2);
+        pin(obase);
 #pragma unroll
         for (int md = 0; md < MD; ++md)
 #pragma unroll
             for (int vp = 0; vp < 8; ++vp) {
                 const float x = o[md][2 * vp] * iv[2 * vp], y = o[md][2 * vp + 1] * iv[2 * vp + 1];
-                // quad_perm [1, 0, 3, 2]: the value of lane n ^ 1
-                const float z = __int_as_float(
-                    __builtin_amdgcn_mov_dpp(__float_as_int(odd ? x : y), 0xB1, 0xF, 0xF, false));
-                const int hd = (wave % wpr) * 32 + (vp >> 1) * 8 + 4 * h2 + 2 * (vp & 1) + (odd ? 1 : 0);
-                const uint32_t pk =
-                    __builtin_bit_cast(uint32_t, __builtin_convertvector(odd ? f32x2{z, y} : f32x2{x, z}, v2));
-                __builtin_amdgcn_raw_buffer_store_b32(pk, ro, hd * D * 2 + (md * 32 + (n & ~1)) * 2, 0, 0);
+                const uint32_t own = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, v2));
+                // quad_perm [1, 0, 3, 2]: the word of lane n ^ 1
+                const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);
+                const uint32_t pk = __builtin_amdgcn_perm(nb, own, sel);
+                // head (wave % wpr) 32 + 8 (vp / 2) + 4 h2 + 2 (vp % 2) + odd, d = 32 md + (n & ~1)
+                __builtin_amdgcn_raw_buffer_store_b32(pk, ro, obase + (2 * (vp & 1) * D + md * 32) * 2,
+                                                      (vp >> 1) * 8 * D * 2, 0);
             }
         const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
             a.lse ? (void *)(a.lse + t * a.H + (size_t)c * a.g) : nullptr, (short)0, a.lse ? a.g * 4 : 0, 0x00020000);
         const float lse = l > 0.f ? (m_run + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, h2 == 0 ? hrow * 4 : a.g * 4, 0, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = qn[ks];
     }
 }
 
