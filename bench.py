@@ -577,6 +577,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-merge", action="store_true", help="skip the log-sum-exp merge timing")
     ap.add_argument("--no-sparse", action="store_true", help="skip the sparse shared-KV attention timing")
+    ap.add_argument("--sparse-shapes", default="sparse,sparse_d512,sparse_all_d512",
+                    help="sparse shared-KV workloads to time (comma-separated keys)")
     ap.add_argument("--configs", default="2,3,4,5", help="workloads to time (first is the main one)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
@@ -723,8 +725,9 @@ def main():
                                       "frac": gbs / PEAK_HBM_GBS, "traffic": None}}
         log(f"merge: {ms_m:.4f} ms/call, {gbs:.0f} GB/s")
     if not args.no_sparse:
-        for key, shape in (("sparse", SPARSE_SHAPE), ("sparse_d512", SPARSE_SHAPE_D512),
-                           ("sparse_all_d512", SPARSE_SHAPE_ALL_D512)):
+        shapes = {"sparse": SPARSE_SHAPE, "sparse_d512": SPARSE_SHAPE_D512, "sparse_all_d512": SPARSE_SHAPE_ALL_D512}
+        for key in [k for k in args.sparse_shapes.split(",") if k]:
+            shape = shapes[key]
             D = shape["D"]
             what = ("every visible compressed key (1025 to 2048) of 4x compressed keys" if shape.get("cmp_all") else
                     "512 selected of 4x compressed keys")
