@@ -502,6 +502,33 @@ def calibrate_mfma(iters):
         print(json.dumps(rows[-1]), flush=True)
 
 
+def calibrate_hbm(gib):
+    """Attainable HBM rate: a full-chip stream (libva_probe.so) over a
+    buffer of `gib` GiB, read only, copy and write only, at 4, 8 and 16
+    workgroups of 256 threads per CU and 4 or 16 16-byte accesses per lane
+    in flight."""
+    import ctypes
+    import torch
+    torch.cuda.init()
+    lib = ctypes.CDLL(os.path.join(ROOT, "variable_length_attention_amd", "libva_probe.so"))
+    d = ctypes.c_double
+    lib.va_probe_hbm_stream.argtypes = [ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.POINTER(d), ctypes.POINTER(d)]
+    lib.va_probe_hbm_stream.restype = ctypes.c_int
+    nbytes = int(gib * (1 << 30)) // 16 * 16
+    for mode, name in ((0, "read"), (1, "copy"), (2, "write")):
+        for deep in (0, 1):
+            for bpc in (4, 8, 16):
+                ms, gbs = d(), d()
+                rc = lib.va_probe_hbm_stream(mode, nbytes, 5, bpc, deep, ctypes.byref(ms), ctypes.byref(gbs))
+                if rc != 0:
+                    raise RuntimeError(f"va_probe_hbm_stream failed: hip error {rc}")
+                print(json.dumps({"stream": name, "bytes": nbytes, "workgroups_per_cu": bpc,
+                                  "in_flight_per_lane": 16 if deep else 4, "ms_5_reps": round(ms.value, 3),
+                                  "gbs": round(gbs.value, 1), "frac_of_peak": round(gbs.value / PEAK_HBM_GBS, 4)}),
+                      flush=True)
+
+
 # ---------------------------------------------------------------- CPU baseline
 CPU_THREADS = 16  # the host-thread share of one GPU on the measurement boxes
 
@@ -584,6 +611,8 @@ def main():
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     ap.add_argument("--calibrate-attainable", action="store_true",
                     help="only measure a large bf16 GEMM and a large read-only reduction")
+    ap.add_argument("--calibrate-hbm", type=float, default=0, metavar="GIB",
+                    help="only run the HBM stream probe over a GIB-GiB buffer (read, copy, write)")
     ap.add_argument("--calibrate-mfma", type=int, default=0, metavar="ITERS",
                     help="only run the matrix-core stream probe (ITERS groups of 4 products per wave)")
     ap.add_argument("--record-traffic", nargs=6, metavar=("KEY", "KERNEL_REGEX", "FETCH_CSV", "WRITE_CSV",
@@ -606,6 +635,9 @@ def main():
         return
     if args.calibrate_mfma:
         calibrate_mfma(args.calibrate_mfma)
+        return
+    if args.calibrate_hbm:
+        calibrate_hbm(args.calibrate_hbm)
         return
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, max(1, args.steps))

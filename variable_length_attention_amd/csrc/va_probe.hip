@@ -8,6 +8,12 @@
 // softmax interleaves them.  It reports the matrix rate the chip sustains
 // with that data under its power limit, and the shader clock it ran at
 // (s_memtime cycles against the 100 MHz s_memrealtime counter).
+//
+// va_probe_hbm_stream: a full-chip grid streams a buffer far larger than
+// the caches, 16 bytes per lane per access, 4 or 16 independent accesses in
+// flight per lane: read only, copy, or write only.  It reports the HBM rate
+// the chip sustains for such plain streams, the attainable ceiling beside
+// the 8 TB/s datasheet figure for the HBM-bound kernels.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -95,7 +101,101 @@ void launch(int grid, int iters, int zero, float *sink, unsigned long long *clk,
     hipLaunchKernelGGL((mfma_stream<K, OP>), dim3(grid), dim3(256), 0, s, iters, zero, sink, clk);
 }
 
+// mode 0: read src, 1: copy src -> dst, 2: write dst; n16 16-byte elements,
+// U independent 16-byte accesses per lane in flight
+template <int MODE, int U>
+__global__ __launch_bounds__(256) void hbm_stream(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst, long long n16,
+                                                  uint32_t *sink)
+{
+    const long long stride = (long long)gridDim.x * 256;
+    long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        if constexpr (MODE == 2) {
+            const u32x4 v = {(uint32_t)i, 1u, 2u, 3u};
+#pragma unroll
+            for (int k = 0; k < U; ++k) dst[i + k * stride] = v;
+        } else {
+            u32x4 v[U];
+#pragma unroll
+            for (int k = 0; k < U; ++k) v[k] = src[i + k * stride];
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                if constexpr (MODE == 1) dst[i + k * stride] = v[k];
+                else acc ^= v[k];
+            }
+        }
+    }
+    for (; i < n16; i += stride) {
+        if constexpr (MODE == 2) dst[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+        else if constexpr (MODE == 1) dst[i] = src[i];
+        else acc ^= src[i];
+    }
+    if constexpr (MODE == 0) {
+        // one word per thread, so the loads are not dropped
+        sink[(size_t)blockIdx.x * 256 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    }
+}
+
 }  // namespace
+
+// Streams `bytes` (a multiple of 16) on the current device with
+// blocks_per_cu workgroups of 256 threads per compute unit, 4 (16 if deep)
+// accesses per lane in flight, reps times
+// between HIP events: mode 0 reads a buffer, 1 copies it to a second one,
+// 2 writes one.  Outputs: time of the reps (ms) and the rate counting every
+// byte read and written (GB/s).  Allocates and frees its buffers.  Returns
+// 0, or a hipError_t.
+extern "C" int va_probe_hbm_stream(int mode, long long bytes, int reps, int blocks_per_cu, int deep, double *ms,
+                                   double *gbs)
+{
+    int dev = 0;
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return (int)e;
+    if (mode < 0 || mode > 2 || bytes < 16 || bytes % 16 != 0 || reps < 1 || blocks_per_cu < 1 || blocks_per_cu > 64)
+        return (int)hipErrorInvalidValue;
+    const int grid = prop.multiProcessorCount * blocks_per_cu;
+    const long long n16 = bytes / 16;
+    u32x4 *src = nullptr, *dst = nullptr;
+    uint32_t *sink = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (mode != 2) e = hipMalloc(&src, (size_t)bytes);
+    if (e == hipSuccess && mode != 0) e = hipMalloc(&dst, (size_t)bytes);
+    if (e == hipSuccess) e = hipMalloc(&sink, (size_t)grid * 256 * sizeof(uint32_t));
+    if (e == hipSuccess && src) e = hipMemset(src, 0x3c, (size_t)bytes);
+    if (e == hipSuccess) e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    auto run = [&]() {
+        if (mode == 0 && deep) hipLaunchKernelGGL((hbm_stream<0, 16>), dim3(grid), dim3(256), 0, 0, src, dst, n16, sink);
+        else if (mode == 0) hipLaunchKernelGGL((hbm_stream<0, 4>), dim3(grid), dim3(256), 0, 0, src, dst, n16, sink);
+        else if (mode == 1 && deep) hipLaunchKernelGGL((hbm_stream<1, 16>), dim3(grid), dim3(256), 0, 0, src, dst, n16, sink);
+        else if (mode == 1) hipLaunchKernelGGL((hbm_stream<1, 4>), dim3(grid), dim3(256), 0, 0, src, dst, n16, sink);
+        else if (deep) hipLaunchKernelGGL((hbm_stream<2, 16>), dim3(grid), dim3(256), 0, 0, src, dst, n16, sink);
+        else hipLaunchKernelGGL((hbm_stream<2, 4>), dim3(grid), dim3(256), 0, 0, src, dst, n16, sink);
+    };
+    if (e == hipSuccess) {
+        run();  // warm-up
+        hipEventRecord(e0, 0);
+        for (int r = 0; r < reps; ++r) run();
+        hipEventRecord(e1, 0);
+        e = hipEventSynchronize(e1);
+    }
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e == hipSuccess) {
+        float t = 0.f;
+        hipEventElapsedTime(&t, e0, e1);
+        *ms = t;
+        *gbs = (double)bytes * (mode == 1 ? 2.0 : 1.0) * reps / (t * 1e-3) / 1e9;
+    }
+    if (e0) hipEventDestroy(e0);
+    if (e1) hipEventDestroy(e1);
+    if (src) hipFree(src);
+    if (dst) hipFree(dst);
+    if (sink) hipFree(sink);
+    return (int)e;
+}
 
 // Runs the stream on the current device: waves_per_simd waves on each SIMD
 // of every compute unit, iters groups of 4 products per wave, K = valu
