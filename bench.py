@@ -688,9 +688,9 @@ def main():
             f"{r['tflops']:.1f} TFLOP/s, {r['gbs']:.0f} GB/s, roofline {r['roofline']['frac'] * 100:.1f}% "
             f"of {r['roofline']['bound']}")
         if not args.no_cpu_baseline:
-            # every row for the small and HBM-bound workloads, a sample of
-            # rows for the two large MFMA-bound ones
-            cb = cpu_baseline(case, full=n in (4, 5))
+            # one full run per workload (about 30 s for config 2), a sample
+            # of rows for the 16k x 16k full-attention shard (5 minutes in full)
+            cb = cpu_baseline(case, full=n in (2, 4, 5))
             r["cpu_baseline"] = cb
             log(f"config {n}: oracle {cb['value'] * 1e3:.1f} GFLOP/s on {cb['cores']} threads ({cb['sample']})")
         results[n] = r
