@@ -55,8 +55,9 @@ KERNEL_SOURCES = {
     "f32": ["va_prefill_f32.hip"],
     "window_bf16": ["va_window.hip"],
     "sparse": ["va_sparse.hip"],
+    "prefill512": ["va_prefill512.hip"],
 }
-PATH_NAMES = ["prefill_bf16", "decode_bf16", "f32", "window_bf16"]  # index = varlen_attn_path
+PATH_NAMES = ["prefill_bf16", "decode_bf16", "f32", "window_bf16", "prefill512"]  # index = varlen_attn_path
 
 
 def log(msg):
@@ -603,6 +604,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-merge", action="store_true", help="skip the log-sum-exp merge timing")
+    ap.add_argument("--no-d512", action="store_true", help="skip the head-size-512 forward timing")
     ap.add_argument("--no-sparse", action="store_true", help="skip the sparse shared-KV attention timing")
     ap.add_argument("--sparse-shapes", default="sparse,sparse_d512,sparse_all_d512",
                     help="sparse shared-KV workloads to time (comma-separated keys)")
@@ -747,6 +749,25 @@ def main():
                                          "unit": "TFLOP/s", "frac": tf_b / PEAK_BF16_TFLOPS,
                                          "scope": "whole backward call", "traffic": None}}
         log(f"backward: {ms_b:.4f} ms/call, {tf_b:.1f} TFLOP/s")
+    if not args.no_d512:
+        # the forward at head size 512 (its own kernel) on a causal GQA prefill
+        spec512 = W.Spec("bf16_causal_gqa_d512", 1512, "bf16", 32, 8, 512, ("fixed", [2048] * 4), causal=True)
+        log(f"{spec512.name} (4 x 2048 tokens, 32/8 heads, head size 512, causal): generating input")
+        c512 = W.make_case(spec512)
+        ms_s, ms_p, path_s, ms_e = time_case(c512, args.steps, args.warmup, torch)
+        ms_k = max(ms_s - ms_p, 1e-6)
+        fl = flops(c512)
+        tf_k = fl / (ms_k * 1e-3) / 1e12
+        line["prefill512"] = {
+            "workload": "bf16 causal GQA prefill at head size 512: 4 x 2048 tokens, 32 heads / 8 kv heads",
+            "kernel_path": PATH_NAMES[path_s], "ms_per_step": ms_s, "ms_per_step_eager": ms_e, "ms_kernel": ms_k,
+            "tflops": fl / (ms_s * 1e-3) / 1e12, "flop": fl,
+            "roofline": {"bound": "mfma", "achieved": tf_k, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf_k / PEAK_BF16_TFLOPS,
+                         "traffic": measured_traffic(PATH_NAMES[path_s], spec512.name)}}
+        log(f"prefill512: {ms_s:.4f} ms/step ({ms_e:.4f} eager), {tf_k:.1f} TFLOP/s kernel, "
+            f"{tf_k / PEAK_BF16_TFLOPS * 100:.1f}% of mfma")
+        del c512
     if not args.no_merge:
         log("merge of 8 float32 partials (32768 x 24 x 128): timing")
         ms_m, by_m = time_merge(args.steps, args.warmup, torch)

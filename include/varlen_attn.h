@@ -78,15 +78,16 @@ extern "C" {
  * still accepted).  3: adds varlen_attn_bwd_sinks (+ its workspace size);
  * varlen_attn_bwd takes fp16 and alibi_slopes.  4: adds
  * varlen_attn_fwd_out_noalloc.  5: adds va_sparse_problem.cmp_attend_all (the
- * second scenario; version 4 descriptors are still accepted). */
-#define VARLEN_ATTN_ABI_VERSION 5
+ * second scenario; version 4 descriptors are still accepted).  6: the
+ * forward entry points take head_dim 512 (bf16 / fp16; varlen_attn_path 4). */
+#define VARLEN_ATTN_ABI_VERSION 6
 
 typedef enum {
     VA_OK = 0,
     VA_ERR_NULL = 1,         /* a required pointer is NULL                        */
     VA_ERR_SHAPE = 2,        /* inconsistent sizes (H % H_kv, batch < 1, totals 0) */
     VA_ERR_DTYPE = 3,        /* dtype not VA_F32 / VA_BF16 / VA_F16               */
-    VA_ERR_UNSUPPORTED = 4,  /* head_dim not 64 / 128, window < -1, ...           */
+    VA_ERR_UNSUPPORTED = 4,  /* head_dim not 64 / 128 / 512, window < -1, ...     */
     VA_ERR_ALIAS = 5,        /* out or lse overlaps an input or each other        */
     VA_ERR_ALIGN = 6,        /* a data pointer is not 16-byte aligned             */
     VA_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than required           */
@@ -108,7 +109,7 @@ typedef struct {
     int32_t total_k;          /* rows of k / v (contiguous mode; ignored if paged) */
     int32_t num_heads;        /* H                                                 */
     int32_t num_kv_heads;     /* H_kv, divides H                                   */
-    int32_t head_dim;         /* D: 64 or 128                                      */
+    int32_t head_dim;         /* D: 64 or 128; 512 with bf16 / fp16 (forward)      */
     int32_t max_seqlen_q;     /* host upper bound of every Lq_b (grid sizing only) */
     int32_t max_seqlen_k;     /* host upper bound of every Lk_b                    */
     float scale;              /* multiplies q.k (not the sink); > 0                */
@@ -221,8 +222,8 @@ va_status varlen_attn_plan(const va_problem *p, int paged, const int32_t *cu_seq
  * The gradient of the sink logits is varlen_attn_bwd_sinks' output.  Same
  * ownership, stream and error rules as the forward (without the opt-in
  * device check); dq, dk, dv may not overlap any input, the
- * workspace or each other; p->dtype must be VA_BF16 or VA_F16 (else
- * VA_ERR_UNSUPPORTED).  `workspace` holds at least
+ * workspace or each other; p->dtype must be VA_BF16 or VA_F16 and head_dim
+ * 64 or 128 (else VA_ERR_UNSUPPORTED).  `workspace` holds at least
  * varlen_attn_bwd_workspace_size(p) bytes (a library helper; 0 for an
  * invalid p). */
 size_t varlen_attn_bwd_workspace_size(const va_problem *p);
@@ -343,7 +344,8 @@ va_status varlen_attn_sparse_sharedkv(const va_sparse_problem *p, const void *q,
  * Which kernel family a call with these arguments would use:
  * 0 = prefill tiles, 1 = split-KV decode with combine, 2 = float32 path,
  * 3 = sliding-window kernel (16-bit K/V, contiguous or paged, 32..64 query
- * heads per kv head, window bounded on both sides, no ALiBi); -1 if invalid. */
+ * heads per kv head, window bounded on both sides, no ALiBi), 4 = head size
+ * 512 (every shape); -1 if invalid. */
 int varlen_attn_path(const va_problem *p, int paged);
 
 /* Thread-local text for the last non-OK status returned on this thread. */

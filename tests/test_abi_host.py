@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.varlen_attn_abi_version() == 5
+    assert lib.varlen_attn_abi_version() == 6
 
 
 def test_problem_struct_matches_header(tmp_path):
@@ -92,6 +92,8 @@ def _fwd_out(p, q=A[0], k=A[1], v=A[2], cuq=A[3], cuk=A[4], sinks=None, out=A[5]
     (dict(dtype=7), 3),
     (dict(dtype=3), 3),
     (dict(head_dim=96), 4),
+    (dict(head_dim=256), 4),
+    (dict(dtype=0, head_dim=512), 4),             # head size 512 takes 16-bit inputs
     (dict(batch=0), 2),
     (dict(total_q=0), 2),                          # empty tensors are not accepted
     (dict(total_k=0), 2),
@@ -176,6 +178,8 @@ def test_workspace_size_and_kernel_path():
     assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, window_right=-1))), 0) == 0
     assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, window_left=149))), 0) == 0
     assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, dtype=0, head_dim=64))), 0) == 2
+    # head size 512: its own kernel for every shape (here the window shape)
+    assert lib.varlen_attn_path(ctypes.byref(_prob(**dict(c4, head_dim=512))), 0) == 4
     p = _prob(**c4)
     p.alibi_slopes = 0x10000000                                                          # ALiBi: tile kernel
     assert lib.varlen_attn_path(ctypes.byref(p), 0) == 0
@@ -206,6 +210,7 @@ def test_backward_rejects_before_launching():
     assert lib.varlen_attn_bwd_workspace_size(ctypes.byref(_prob(dtype=0))) == 0
     assert _bwd(_prob(dtype=0)) == 4                                   # float32: unsupported
     assert _bwd(_prob(head_dim=96)) == 4
+    assert _bwd(_prob(head_dim=512)) == 4                              # the forward only
     assert _bwd(_prob(dtype=2), ws_bytes=64) == 7                      # float16 accepted (then: workspace)
     assert _bwd(p, dout=None) == 1
     assert _bwd(p, lse=None) == 1

@@ -133,7 +133,8 @@ def workspace_size(problem: _lib.VaProblem, paged: bool = False) -> int:
 
 def kernel_path(problem: _lib.VaProblem, paged: bool = False) -> int:
     """0 = prefill tiles, 1 = split-KV decode + combine, 2 = float32 path,
-    3 = sliding-window kernel for 32..64 query heads per kv head."""
+    3 = sliding-window kernel for 32..64 query heads per kv head, 4 = head
+    size 512."""
     return int(_lib.load().varlen_attn_path(ctypes.byref(problem), 1 if paged else 0))
 
 

@@ -22,17 +22,19 @@ PROBE_SOURCES = ["va_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["va_api.cpp", "va_plan.hip", "va_prefill_bf16.hip", "va_prefill_f32.hip", "va_decode.hip",
-           "va_check.hip", "va_backward.hip", "va_merge.hip", "va_sparse.hip", "va_window.hip"]
+           "va_check.hip", "va_backward.hip", "va_merge.hip", "va_sparse.hip", "va_window.hip", "va_prefill512.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-command-line-argument"]
 # Per-file device options.  The backward's dK/dV kernel and the d512 sparse
-# shared-KV kernel keep their accumulators in AGPRs through inline assembly
+# shared-KV and dense forward kernels keep their accumulators in AGPRs
+# through inline assembly
 # and need every other matrix instruction in the VGPR form (the backend
 # otherwise picks the AGPR form for a whole kernel that may use more than
 # 256 registers).
 EXTRA = {"va_backward.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=1"],
-         "va_sparse.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=1"]}
+         "va_sparse.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=1"],
+         "va_prefill512.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

@@ -51,7 +51,7 @@ bool device_check_enabled()
     return e && e[0] == '1';
 }
 
-enum Path { kPathPrefill = 0, kPathDecode = 1, kPathF32 = 2, kPathWindow = 3 };
+enum Path { kPathPrefill = 0, kPathDecode = 1, kPathF32 = 2, kPathWindow = 3, kPath512 = 4 };
 
 struct Layout {
     int path = -1;
@@ -91,8 +91,10 @@ va_status check_problem(const va_problem *p, int paged)
     if (p->num_heads % p->num_kv_heads != 0)
         return fail(VA_ERR_SHAPE, "num_heads %d is not a multiple of num_kv_heads %d", p->num_heads,
                     p->num_kv_heads);
-    if (p->head_dim != 64 && p->head_dim != 128)
-        return fail(VA_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", p->head_dim);
+    if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 512)
+        return fail(VA_ERR_UNSUPPORTED, "head_dim %d is not 64, 128 or 512", p->head_dim);
+    if (p->head_dim == 512 && p->dtype == VA_F32)
+        return fail(VA_ERR_UNSUPPORTED, "head_dim 512 takes bf16 or fp16 inputs");
     if (p->max_seqlen_q < 1 || p->max_seqlen_q > va::kMaxSeqlen)
         return fail(VA_ERR_SHAPE, "max_seqlen_q %d outside [1, %d]", p->max_seqlen_q, va::kMaxSeqlen);
     if (p->max_seqlen_k < 0 || p->max_seqlen_k > va::kMaxSeqlen)
@@ -137,7 +139,12 @@ va_status make_layout(const va_problem *p, int paged, Layout &L)
 {
     const int g = p->num_heads / p->num_kv_heads;
     const int wrows = window_rows(p);
-    if (p->dtype == VA_F32) {
+    if (p->head_dim == 512) {
+        // every shape at head size 512: the prefill items, 32-key tiles
+        L.path = kPath512;
+        L.bm = va::kBM;
+        L.bn = 32;
+    } else if (p->dtype == VA_F32) {
         L.path = kPathF32;
         L.bm = va::kBMf32;
         L.bn = va::kBNf32;
@@ -356,7 +363,8 @@ va_status run(const Call &c, hipStream_t s)
     if (log_enabled())
         fprintf(stderr, "[varlen_attn] path=%s D=%d paged=%d B=%d H=%d Hkv=%d total_q=%d grid=%lld ws=%zu\n",
                 L.path == kPathPrefill ? "prefill16" : L.path == kPathDecode ? "decode16"
-                                                   : L.path == kPathWindow ? "window16" : "f32",
+                                                   : L.path == kPathWindow ? "window16"
+                                                   : L.path == kPath512    ? "prefill512" : "f32",
                 c.p->head_dim, c.paged, a.B, a.H, a.Hkv, c.p->total_q, L.grid, L.total);
     hipError_t e = va::launch_plan(pa, s);
     if (e == hipSuccess) {
@@ -372,6 +380,8 @@ va_status run(const Call &c, hipStream_t s)
                                     pa.count, (int)L.grid, s);
         else if (L.path == kPathF32)
             e = va::launch_prefill_f32(a, c.p->head_dim, c.paged, pa.items, pa.seqinfo, pa.count, (int)L.grid, s);
+        else if (L.path == kPath512)
+            e = va::launch_prefill512(a, c.p->dtype == VA_F16, c.paged, pa.items, pa.seqinfo, pa.count, (int)L.grid, s);
         else {
             char *ws = (char *)c.ws;
             float *po = (float *)(ws + L.off_part_o);
@@ -418,6 +428,8 @@ va_status bwd_layout(const va_problem *p, BwdLayout &L)
     if (st) return st;
     if (p->dtype != VA_BF16 && p->dtype != VA_F16)
         return fail(VA_ERR_UNSUPPORTED, "the backward takes bf16 or fp16 inputs");
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return fail(VA_ERR_UNSUPPORTED, "the backward takes head_dim 64 or 128, not %d", p->head_dim);
     const long long nq = ((long long)p->total_q + (long long)p->batch * (va::kBM - 1)) / va::kBM;
     const long long nk = ((long long)p->total_k + (long long)p->batch * (va::kBwdKeys - 1)) / va::kBwdKeys;
     const long long gq = nq * p->num_heads, gk = nk * p->num_kv_heads;

@@ -173,6 +173,8 @@ hipError_t launch_window16(const AttnArgs &a, bool f16, int head_dim, bool paged
 hipError_t launch_plan(const PlanArgs &pa, hipStream_t s);
 hipError_t launch_prefill16(const AttnArgs &a, bool f16, bool alibi, int head_dim, int mode, const int4 *items,
                             const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);
+hipError_t launch_prefill512(const AttnArgs &a, bool f16, bool paged, const int4 *items, const int4 *seqinfo,
+                             const int32_t *count, int grid, hipStream_t s);
 hipError_t launch_prefill_f32(const AttnArgs &a, int head_dim, bool paged, const int4 *items,
                               const int4 *seqinfo, const int32_t *count, int grid, hipStream_t s);
 hipError_t launch_decode16(const AttnArgs &a, bool f16, int head_dim, bool paged, const int4 *items,
