@@ -6,7 +6,8 @@ sink logits and an optional paged KV cache; writes O into a caller buffer and
 returns the float32 log-sum-exp; an out variant that allocates nothing; its
 backward (dq, dk, dv, and the sink-logit gradient) for bf16 / fp16
 contiguous K/V; the log-sum-exp merge of partial results over disjoint key
-sets; and sliding-window + sparse compressed attention over shared K/V.  The
+sets; and sliding-window + compressed attention over shared K/V.  Head sizes
+64 and 128 (and 512 for the 16-bit forward and the shared-KV op).  The
 computation runs in hand-written HIP kernels behind the C ABI of
 include/varlen_attn.h; this package only binds it.
 """
