@@ -503,6 +503,34 @@ def calibrate_mfma(iters):
         print(json.dumps(rows[-1]), flush=True)
 
 
+def calibrate_lds(iters):
+    """LDS read rate per compute unit (libva_probe.so): 16-byte reads and
+    transposing 8-byte reads, alone and supplying one operand of every
+    32x32x16 bf16 product (1 KB per product per wave, the attention tile
+    reads' ratio), at one and two workgroups of 4 waves per compute unit."""
+    import ctypes
+    import torch
+    torch.cuda.init()
+    lib = ctypes.CDLL(os.path.join(ROOT, "variable_length_attention_amd", "libva_probe.so"))
+    d = ctypes.c_double
+    lib.va_probe_lds_stream.argtypes = [ctypes.c_int] * 3 + [ctypes.POINTER(d)] * 4
+    lib.va_probe_lds_stream.restype = ctypes.c_int
+    names = ["ds_read_b128 -> product", "2 x ds_read_b64_tr_b16 -> product", "ds_read_b128 only",
+             "ds_read_b64_tr_b16 only"]
+    for wps in (1, 2):
+        for mode in range(4):
+            ms, tf, mhz, bpc = d(), d(), d(), d()
+            rc = lib.va_probe_lds_stream(wps, iters, mode, ctypes.byref(ms), ctypes.byref(tf), ctypes.byref(mhz),
+                                         ctypes.byref(bpc))
+            if rc != 0:
+                raise RuntimeError(f"va_probe_lds_stream failed: hip error {rc}")
+            row = {"waves_per_simd": wps, "mode": names[mode], "ms": round(ms.value, 4),
+                   "tflops": round(tf.value, 1) if mode <= 1 else None,
+                   "frac_of_peak": round(tf.value / PEAK_BF16_TFLOPS, 4) if mode <= 1 else None,
+                   "shader_mhz": round(mhz.value), "lds_bytes_per_clk_per_cu": round(bpc.value, 1)}
+            print(json.dumps(row), flush=True)
+
+
 def calibrate_hbm(gib):
     """Attainable HBM rate: a full-chip stream (libva_probe.so) over a
     buffer of `gib` GiB, read only, copy and write only, at 4, 8 and 16
@@ -617,6 +645,8 @@ def main():
                     help="only run the HBM stream probe over a GIB-GiB buffer (read, copy, write)")
     ap.add_argument("--calibrate-mfma", type=int, default=0, metavar="ITERS",
                     help="only run the matrix-core stream probe (ITERS groups of 4 products per wave)")
+    ap.add_argument("--calibrate-lds", type=int, default=0, metavar="ITERS",
+                    help="only run the LDS stream probe (ITERS groups of 4 products or 8 reads per wave)")
     ap.add_argument("--record-traffic", nargs=6, metavar=("KEY", "KERNEL_REGEX", "FETCH_CSV", "WRITE_CSV",
                                                           "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="(no GPU) store a kernel's HBM bytes per launch from rocprofv3 counter CSVs")
@@ -640,6 +670,9 @@ def main():
         return
     if args.calibrate_hbm:
         calibrate_hbm(args.calibrate_hbm)
+        return
+    if args.calibrate_lds:
+        calibrate_lds(args.calibrate_lds)
         return
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, max(1, args.steps))

@@ -14,6 +14,10 @@
 // flight per lane: read only, copy, or write only.  It reports the HBM rate
 // the chip sustains for such plain streams, the attainable ceiling beside
 // the 8 TB/s datasheet figure for the HBM-bound kernels.
+//
+// va_probe_lds_stream: the LDS read rate per compute unit (16-byte reads, or
+// the transposing 8-byte reads), alone or supplying one operand of every
+// product of a product stream, as the attention kernels' tile reads do.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -137,6 +141,98 @@ __global__ __launch_bounds__(256) void hbm_stream(const u32x4 *__restrict__ src,
     }
 }
 
+// LDS stream: MODE 0: one ds_read_b128 (1 KB per wave) supplies the first
+// operand of every product (four products in flight, each operand read four
+// products ahead of its use); MODE 1: two ds_read_b64_tr_b16 (2 x 512 B)
+// supply it; MODE 2: ds_read_b128 only, eight in flight, no products;
+// MODE 3: ds_read_b64_tr_b16 only.  32 KB of LDS per workgroup, every
+// address inside it, consecutive lanes on consecutive banks.
+template <int MODE>
+__global__ __launch_bounds__(256) void lds_stream(int iters, float *sink, unsigned long long *clk)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t lds[8192];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const uint32_t gid = blockIdx.x * 256 + tid;
+    for (int i = tid; i < 8192; i += 256) lds[i] = rand_bf16x2(gid * 131u + (uint32_t)i);
+    __syncthreads();
+    const char *base = (const char *)lds;
+    bf16x8 a[4], b[4];
+    f32x16 acc[4];
+    u32x4 r[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        u32x4 x, y;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            x[q] = rand_bf16x2(gid * 64 + j * 8 + q);
+            y[q] = rand_bf16x2(gid * 64 + j * 8 + 4 + q + 0x9e3779b9u);
+        }
+        a[j] = __builtin_bit_cast(bf16x8, x);
+        b[j] = __builtin_bit_cast(bf16x8, y);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r[k] = u32x4{0u, 0u, 0u, 0u};
+
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int slot = (it * 4 + j) & 31;
+            if constexpr (MODE == 0) {
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[j], acc[j], 0, 0, 0);
+                a[j] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(base + slot * 1024 + lane * 16));
+            } else if constexpr (MODE == 1) {
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[j], acc[j], 0, 0, 0);
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                typedef bf16x4 __attribute__((address_space(3))) lds_v4;
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_v4 *)((__attribute__((address_space(3))) char *)(base + slot * 1024 + lane * 8)));
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_v4 *)((__attribute__((address_space(3))) char *)(base + slot * 1024 + 512 + lane * 8)));
+                a[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            } else if constexpr (MODE == 2) {
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    asm volatile("" ::"v"(r[j * 2 + k]));
+                    r[j * 2 + k] = *(const u32x4 *)(base + ((slot * 2 + k) & 31) * 1024 + lane * 16);
+                }
+            } else {
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                typedef bf16x4 __attribute__((address_space(3))) lds_v4;
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    asm volatile("" ::"v"(r[j * 2 + k]));
+                    const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (lds_v4 *)((__attribute__((address_space(3))) char *)(base + slot * 1024 + k * 512 + lane * 8)));
+                    const uint2 u = __builtin_bit_cast(uint2, x);
+                    r[j * 2 + k] = u32x4{u.x, u.y, 0u, 0u};
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) asm volatile("" ::"v"(r[k]));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s += acc[j][v];
+        s += (float)a[j][0];
+    }
+    sink[gid] = s;
+    if (lane == 0) {
+        const int w = gid >> 6;
+        clk[2 * w] = t1 - t0;
+        clk[2 * w + 1] = r1 - r0;
+    }
+}
+
 }  // namespace
 
 // Streams `bytes` (a multiple of 16) on the current device with
@@ -253,6 +349,67 @@ extern "C" int va_probe_mfma_stream(int waves_per_simd, int iters, int zero_data
         *ms = t;
         *tflops = (double)waves * iters * 4.0 * 32768.0 / (t * 1e-3) / 1e12;
         *mhz = real > 0 ? cyc / real * 100.0 : 0.0;
+    }
+    if (e0) hipEventDestroy(e0);
+    if (e1) hipEventDestroy(e1);
+    if (sink) hipFree(sink);
+    if (clk) hipFree(clk);
+    return (int)e;
+}
+
+// Runs the LDS stream (mode 0..3, above) on the current device:
+// waves_per_simd workgroups of 4 waves per compute unit, iters groups of 4
+// products (modes 0, 1) or of 8 reads (modes 2, 3) per wave.  Outputs:
+// kernel time (ms), matrix rate (TFLOP/s, modes 0 and 1), mean shader
+// clock (MHz) and LDS bytes read per clock per compute unit (the waves'
+// bytes over their mean cycle count).  Returns 0, or a hipError_t.
+extern "C" int va_probe_lds_stream(int waves_per_simd, int iters, int mode, double *ms, double *tflops, double *mhz,
+                                   double *bytes_per_clk)
+{
+    int dev = 0;
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return (int)e;
+    if (waves_per_simd < 1 || waves_per_simd > 4 || iters < 1 || mode < 0 || mode > 3)
+        return (int)hipErrorInvalidValue;
+    const int cus = prop.multiProcessorCount;
+    const int grid = cus * waves_per_simd;
+    const int waves = grid * 4;
+    float *sink = nullptr;
+    unsigned long long *clk = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    auto go = [&](int n) {
+        if (mode == 0) hipLaunchKernelGGL((lds_stream<0>), dim3(grid), dim3(256), 0, 0, n, sink, clk);
+        else if (mode == 1) hipLaunchKernelGGL((lds_stream<1>), dim3(grid), dim3(256), 0, 0, n, sink, clk);
+        else if (mode == 2) hipLaunchKernelGGL((lds_stream<2>), dim3(grid), dim3(256), 0, 0, n, sink, clk);
+        else hipLaunchKernelGGL((lds_stream<3>), dim3(grid), dim3(256), 0, 0, n, sink, clk);
+    };
+    e = hipMalloc(&sink, (size_t)grid * 256 * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc(&clk, (size_t)waves * 2 * sizeof(unsigned long long));
+    if (e == hipSuccess) e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    if (e == hipSuccess) {
+        go(iters / 4 + 1);  // warm-up (clock ramp)
+        hipEventRecord(e0, 0);
+        go(iters);
+        hipEventRecord(e1, 0);
+        e = hipEventSynchronize(e1);
+    }
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e == hipSuccess) {
+        float t = 0.f;
+        hipEventElapsedTime(&t, e0, e1);
+        unsigned long long *h = new unsigned long long[(size_t)waves * 2];
+        e = hipMemcpy(h, clk, (size_t)waves * 2 * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+        double cyc = 0, real = 0;
+        for (int w = 0; w < waves; ++w) { cyc += (double)h[2 * w]; real += (double)h[2 * w + 1]; }
+        delete[] h;
+        const double per_wave = mode == 2 ? 8192.0 : 4096.0;  // bytes per iteration
+        *ms = t;
+        *tflops = mode <= 1 ? (double)waves * iters * 4.0 * 32768.0 / (t * 1e-3) / 1e12 : 0.0;
+        *mhz = real > 0 ? cyc / real * 100.0 : 0.0;
+        *bytes_per_clk = cyc > 0 ? (double)waves * iters * per_wave / (cyc / waves) / cus : 0.0;
     }
     if (e0) hipEventDestroy(e0);
     if (e1) hipEventDestroy(e1);
