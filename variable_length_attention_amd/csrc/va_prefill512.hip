@@ -134,7 +134,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int MD = D / 32;         // 32-wide blocks of the head dimension
     constexpr int ROWB = D * 2;        // bytes per row (one 64-lane copy)
     constexpr int TILEB = BN * ROWB;
-    constexpr int CPW = 2 * BN / 4;    // copies per wave per tile: waves 0, 1 take K rows, 2, 3 V rows
+    constexpr int CPW = 2 * BN / 4;
+    constexpr int KPF = 4, VPF = 3;   // LDS operand reads in flight ahead of their product (K, V)    // copies per wave per tile: waves 0, 1 take K rows, 2, 3 V rows
     __shared__ __attribute__((aligned(16))) char s_k[2 * TILEB];
     __shared__ __attribute__((aligned(16))) char s_v[2 * TILEB];
 
@@ -251,15 +252,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const char *kt = s_k + slot * TILEB;
             const char *vt = s_v + slot * TILEB;
             // S^T = K Q^T: lane value v is key j0 + 8 (v/4) + 4 h2 + v%4 of row n
-            f32x16 S;
+            // two accumulators (even / odd k-steps), K operands read KPF
+            // steps ahead of their product
+            f32x16 S, S1;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) S[v] = 0.f;
+            for (int v = 0; v < 16; ++v) { S[v] = 0.f; S1[v] = 0.f; }
+            v8 kb[KPF];
+#pragma unroll
+            for (int p = 0; p < KPF; ++p) kb[p] = *(const v8 *)(kt + koff(p));
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                S = E::mfma(*(const v8 *)(kt + koff(ks)), qf[ks], S);
-                // at most 8 K operand reads ahead (Q^T holds 128 registers)
-                if (ks % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+                const v8 cur = kb[ks % KPF];
+                if (ks + KPF < KS) kb[ks % KPF] = *(const v8 *)(kt + koff(ks + KPF));
+                if (ks & 1) S1 = E::mfma(cur, qf[ks], S1);
+                else S = E::mfma(cur, qf[ks], S);
+                __builtin_amdgcn_sched_barrier(0);
             }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) S[v] += S1[v];
             if (a.alibi) {
                 const float base = pos - (float)(j0 + 4 * h2);
 #pragma unroll
@@ -310,19 +320,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
             l_run += rs;
             // O^T += V^T P^T, 16 keys per step
+            v8 pb[BN / 16];
 #pragma unroll
             for (int t4 = 0; t4 < BN / 16; ++t4) {
                 f32x8 pv;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) pv[e] = S[t4 * 8 + e];
-                const v8 pb = __builtin_convertvector(pv, v8);
+                pb[t4] = __builtin_convertvector(pv, v8);
+            }
+            // step st = (t4, md); its V^T operand is read VPF steps ahead
+            constexpr int NST = BN / 16 * MD;
+            auto vread = [&](int st) -> v8 {
+                const int t4 = st / MD, md = st % MD;
+                const v4 va = E::read_tr(vt + toff(md, 0) + t4 * 16 * ROWB);
+                const v4 vb = E::read_tr(vt + toff(md, 1) + t4 * 16 * ROWB);
+                return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+            v8 vbuf[VPF];
 #pragma unroll
-                for (int md = 0; md < MD; ++md) {
-                    const v4 va = E::read_tr(vt + toff(md, 0) + t4 * 16 * ROWB);
-                    const v4 vb = E::read_tr(vt + toff(md, 1) + t4 * 16 * ROWB);
-                    const v8 vf = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-                    E::mfma_agpr(o[md], vf, pb);
-                }
+            for (int p = 0; p < VPF; ++p) vbuf[p] = vread(p);
+#pragma unroll
+            for (int st = 0; st < NST; ++st) {
+                const v8 cur = vbuf[st % VPF];
+                if (st + VPF < NST) vbuf[st % VPF] = vread(st + VPF);
+                E::mfma_agpr(o[st % MD], cur, pb[st / MD]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         wait_vmem();
