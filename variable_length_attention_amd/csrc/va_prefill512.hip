@@ -13,8 +13,11 @@
 // (one wave per SIMD) and the Q^T fragments take 128 VGPRs.  Per 32-key
 // tile, K and V rows go global -> LDS (double buffered, 128 KB) and are
 // read row-wise (K operand) and through the transposing LDS read (V^T
-// operand), one XOR swizzle of the 16-byte chunks serving both.  Tiles a
-// wave cannot see are skipped; masks are evaluated only on tiles that
+// operand), one XOR swizzle of the 16-byte chunks serving both.  The
+// matrix instructions take their LDS operands several products after the
+// reads are issued, and the exponentials of tile t run between the
+// products of tile t + 1 (software pipeline, one barrier per tile).  Tiles
+// a wave cannot see are skipped; masks are evaluated only on tiles that
 // straddle a mask edge.
 #include "va_internal.h"
 
@@ -103,6 +106,22 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 
 __device__ __forceinline__ void copy16_global(const void *src, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "m0");
+}
+// The same copy from a wave-uniform base (SGPR pair) plus a 32-bit lane
+// offset, to LDS address lds + ldsoff (M0 formed here, so that the
+// destinations of a tile's rows are not each held in a register).
+__device__ __forceinline__ void copy16_global_sv(const void *sbase, uint32_t voff, uint32_t lds, uint32_t ldsoff)
+{
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 : : "v"(voff), "s"(sbase), "s"(lds), "s"(ldsoff) : "m0", "scc");
+}
+// (lane16 ^ x) + y computed at the point of use (kept out of
+// loop-invariant hoisting, which would hold one register per distinct x)
+__device__ __forceinline__ uint32_t xor_add_here(uint32_t lane16, uint32_t x, uint32_t y)
+{
+    uint32_t r;
+    asm volatile("v_xor_b32 %0, %1, %2\n\tv_add_u32 %0, %3, %0" : "=&v"(r) : "s"(x), "v"(lane16), "s"(y));
+    return r;
 }
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
@@ -206,150 +225,214 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         return r * ROWB + ((ch ^ swz(r)) << 4) + (l16 & 1) * 8 + (md >> 2) * 256;
     };
 
-    // tile tau's K and V rows into buffer slot.  The row of a copy is the
-    // same for all its lanes, so a paged row's block-table entry is one
-    // scalar load; all of a wave's entries are read before its copies.
-    // Rows past the item's key range repeat its last row (finite data
-    // under the mask).
+    // tile tau's K rows (waves 0, 1) or V rows (waves 2, 3) into buffer
+    // slot; one 64-lane copy per row.  Rows past the item's key range repeat
+    // its last row (finite data under the mask).  Contiguous K/V: the rows
+    // of a tile are a constant stride apart, so the tile has one base and a
+    // row's offset joins the lane's chunk offset.  Paged K/V: the row of a
+    // copy is the same for all its lanes, so its block-table entry is one
+    // scalar load; the entries of 8 copies are read before those copies.
     const bool is_v = wave >= 2;
-    auto issue = [&](int tau, int slot) {
-        size_t roff[CPW];
+    auto issue = [&](int tau, int slot) __attribute__((always_inline)) {
+        const char *src = (const char *)(is_v ? a.v : a.k);
+        // LDS address of the wave's first row in the slot
+        const uint32_t dst = lds_addr((is_v ? s_v : s_k) + slot * TILEB + (wave & 1) * CPW * ROWB);
+        const int jt = kv_lo + tau * BN;   // the tile's first key (< kv_hi)
+        if constexpr (!PAGED) {
+            const char *tb = src + ((size_t)(k0 + jt) * a.Hkv + c) * (D * 2);
+            const int rmax = kv_hi - 1 - jt;
+            const uint32_t rstride = (uint32_t)a.Hkv * (D * 2);
 #pragma unroll
-        for (int u = 0; u < CPW; ++u) {
-            const int r = (wave & 1) * CPW + u;
-            const int j = __builtin_amdgcn_readfirstlane(min(kv_lo + tau * BN + r, kv_hi - 1));
-            size_t row;
-            if constexpr (PAGED) {
-                const int bi = a.bs_shift >= 0 ? j >> a.bs_shift : j / a.block_size;
-                // the table is read-only here: through the constant address
-                // space the entry is a scalar load (its own counter, no wait
-                // on the copies in flight)
-                const int blk = ((const __attribute__((address_space(4))) int32_t *)a.block_table)[(size_t)b * a.bt_stride + bi];
-                row = (size_t)blk * a.block_size + (j - bi * a.block_size);
-            } else {
-                row = (size_t)(k0 + j);
+            for (int u = 0; u < CPW; ++u) {
+                const int r = (wave & 1) * CPW + u;
+                const uint32_t roff = (uint32_t)min(r, rmax) * rstride;
+                copy16_global_sv(tb, xor_add_here(lane * 16, swz(r) * 16, roff), dst, u * ROWB);
             }
-            roff[u] = (row * a.Hkv + c) * (D * 2);
-        }
+        } else {
 #pragma unroll
-        for (int u = 0; u < CPW; ++u) {
-            const int r = (wave & 1) * CPW + u;
-            const size_t off = roff[u] + (size_t)((lane ^ swz(r)) * 16);
-            copy16_global((const char *)(is_v ? a.v : a.k) + off,
-                          lds_addr((is_v ? s_v : s_k) + slot * TILEB + r * ROWB));
+            for (int h = 0; h < CPW; h += 8) {
+                const char *rb[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int r = (wave & 1) * CPW + h + u;
+                    const int j = min(jt + r, kv_hi - 1);
+                    const int bi = a.bs_shift >= 0 ? j >> a.bs_shift : j / a.block_size;
+                    // the table is read-only here: through the constant
+                    // address space the entry is a scalar load (its own
+                    // counter, no wait on the copies in flight)
+                    const int blk = ((const __attribute__((address_space(4))) int32_t *)a.block_table)[(size_t)b * a.bt_stride + bi];
+                    const size_t row = (size_t)blk * a.block_size + (j - bi * a.block_size);
+                    rb[u] = src + (row * a.Hkv + c) * (D * 2);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int r = (wave & 1) * CPW + h + u;
+                    copy16_global_sv(rb[u], xor_add_here(lane * 16, swz(r) * 16, 0u), dst, (h + u) * ROWB);
+                }
+            }
         }
     };
 
     const int ntiles = kv_hi > kv_lo ? (kv_hi - kv_lo + BN - 1) / BN : 0;
-    if (ntiles > 0) issue(0, 0);
-    wait_vmem();
-    __syncthreads();
-    for (int tau = 0; tau < ntiles; ++tau) {
-        const int slot = tau & 1;
-        if (tau + 1 < ntiles) issue(tau + 1, slot ^ 1);
+    auto visible = [&](int tau) __attribute__((always_inline)) {   // some row of the wave sees a key of tile tau
         const int j0 = kv_lo + tau * BN;
-        if (j0 <= whi && j0 + BN - 1 >= wlo) {   // some row of the wave sees a key of the tile
-            const char *kt = s_k + slot * TILEB;
-            const char *vt = s_v + slot * TILEB;
-            // S^T = K Q^T: lane value v is key j0 + 8 (v/4) + 4 h2 + v%4 of row n
-            // two accumulators (even / odd k-steps), K operands read KPF
-            // steps ahead of their product
-            f32x16 S, S1;
+        return j0 <= whi && j0 + BN - 1 >= wlo;
+    };
+
+    // S^T = K Q^T for the tile in kt: lane value v is key j0 + 8 (v/4) +
+    // 4 h2 + v%4 of row n.  Two accumulators (even / odd k-steps); K
+    // operands read KPF steps ahead of their product; hook(ks) runs after
+    // step ks (independent vector work placed between the products).
+    auto qk = [&](f32x16 &S, const char *kt, auto &&hook) __attribute__((always_inline)) {
+        f32x16 S1;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) { S[v] = 0.f; S1[v] = 0.f; }
-            v8 kb[KPF];
+        for (int v = 0; v < 16; ++v) { S[v] = 0.f; S1[v] = 0.f; }
+        v8 kb[KPF];
 #pragma unroll
-            for (int p = 0; p < KPF; ++p) kb[p] = *(const v8 *)(kt + koff(p));
+        for (int p = 0; p < KPF; ++p) kb[p] = *(const v8 *)(kt + koff(p));
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const v8 cur = kb[ks % KPF];
-                if (ks + KPF < KS) kb[ks % KPF] = *(const v8 *)(kt + koff(ks + KPF));
-                if (ks & 1) S1 = E::mfma(cur, qf[ks], S1);
-                else S = E::mfma(cur, qf[ks], S);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int ks = 0; ks < KS; ++ks) {
+            const v8 cur = kb[ks % KPF];
+            if (ks + KPF < KS) kb[ks % KPF] = *(const v8 *)(kt + koff(ks + KPF));
+            if (ks & 1) S1 = E::mfma(cur, qf[ks], S1);
+            else S = E::mfma(cur, qf[ks], S);
+            hook(ks);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-            for (int v = 0; v < 16; ++v) S[v] += S1[v];
-            if (a.alibi) {
-                const float base = pos - (float)(j0 + 4 * h2);
+        for (int v = 0; v < 16; ++v) S[v] += S1[v];
+    };
+    // ALiBi and the mask on the raw scores of tile tau, their row max, and
+    // the running max moved (O and l rescaled) only when the tile raises it
+    // by more than 2^8 (log2 units) for some row: until then the
+    // probabilities stay below 2^8.  The max is taken on raw scores (scale > 0).
+    auto row_max = [&](f32x16 &S, int tau) __attribute__((always_inline)) {
+        const int j0 = kv_lo + tau * BN;
+        if (a.alibi) {
+            const float base = pos - (float)(j0 + 4 * h2);
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    S[v] = fmaf(-alibi_r, fabsf(base - (float)(8 * (v >> 2) + (v & 3))), S[v]);
-            }
-#pragma unroll
-            for (int v = 0; v < 16; ++v) S[v] *= a.scale_log2;
-            if (!(j0 >= flo && j0 + BN - 1 <= fhi)) {
-                // key j is visible iff (unsigned)(j - lo) <= (unsigned)(hi - lo);
-                // rows that see nothing (hi < lo) get span 0 and offsets >= 1
-                const bool none = hi < lo;
-                const uint32_t span = none ? 0u : (uint32_t)(hi - lo);
-                const int jb = none ? 1 : j0 + 4 * h2 - lo;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const uint32_t d = (uint32_t)(jb + 8 * (v >> 2) + (v & 3));
-                    S[v] = d > span ? -INFINITY : S[v];
-                }
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[v]);
-            // the running max moves only when a tile raises it by more than
-            // 2^8 (log2 units) for some row: until then the probabilities
-            // stay below 2^8 and the O / l rescale is skipped
-            mx = halves_max(mx);
-            if (__ballot(mx > m_run + 8.f) != 0ull) {
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
-#pragma unroll
-                for (int md = 0; md < MD; ++md) {
-                    mfma_agpr_drain(o[md]);
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
-                    in_agpr(o[md]);
-                }
-                m_run = m_new;
-            }
-            const float m_use = m_run == -INFINITY ? 0.f : m_run;
-            float rs = 0.f;
+            for (int v = 0; v < 16; ++v)
+                S[v] = fmaf(-alibi_r, fabsf(base - (float)(8 * (v >> 2) + (v & 3))), S[v]);
+        }
+        if (!(j0 >= flo && j0 + BN - 1 <= fhi)) {
+            // key j is visible iff (unsigned)(j - lo) <= (unsigned)(hi - lo);
+            // rows that see nothing (hi < lo) get span 0 and offsets >= 1
+            const bool none = hi < lo;
+            const uint32_t span = none ? 0u : (uint32_t)(hi - lo);
+            const int jb = none ? 1 : j0 + 4 * h2 - lo;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float pr = __builtin_amdgcn_exp2f(S[v] - m_use);
-                S[v] = pr;
-                rs += pr;
-            }
-            l_run += rs;
-            // O^T += V^T P^T, 16 keys per step
-            v8 pb[BN / 16];
-#pragma unroll
-            for (int t4 = 0; t4 < BN / 16; ++t4) {
-                f32x8 pv;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pv[e] = S[t4 * 8 + e];
-                pb[t4] = __builtin_convertvector(pv, v8);
-            }
-            // step st = (t4, md); its V^T operand is read VPF steps ahead
-            constexpr int NST = BN / 16 * MD;
-            auto vread = [&](int st) -> v8 {
-                const int t4 = st / MD, md = st % MD;
-                const v4 va = E::read_tr(vt + toff(md, 0) + t4 * 16 * ROWB);
-                const v4 vb = E::read_tr(vt + toff(md, 1) + t4 * 16 * ROWB);
-                return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-            };
-            v8 vbuf[VPF];
-#pragma unroll
-            for (int p = 0; p < VPF; ++p) vbuf[p] = vread(p);
-#pragma unroll
-            for (int st = 0; st < NST; ++st) {
-                const v8 cur = vbuf[st % VPF];
-                if (st + VPF < NST) vbuf[st % VPF] = vread(st + VPF);
-                E::mfma_agpr(o[st % MD], cur, pb[st / MD]);
-                __builtin_amdgcn_sched_barrier(0);
+                const uint32_t d = (uint32_t)(jb + 8 * (v >> 2) + (v & 3));
+                S[v] = d > span ? -INFINITY : S[v];
             }
         }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[v]);
+        mx = halves_max(mx) * a.scale_log2;
+        if (__ballot(mx > m_run + 8.f) != 0ull) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int md = 0; md < MD; ++md) {
+                mfma_agpr_drain(o[md]);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
+                in_agpr(o[md]);
+            }
+            m_run = m_new;
+        }
+    };
+    // probability v of the tile in S, in place: 2^(scale_log2 S - m)
+    auto prob = [&](f32x16 &S, int v, float neg_m, float &rs) __attribute__((always_inline)) {
+        const float pr = __builtin_amdgcn_exp2f(fmaf(S[v], a.scale_log2, neg_m));
+        S[v] = pr;
+        rs += pr;
+    };
+    // O^T += V^T P^T over the tile in vt, step st = (t4, md) of 16 keys;
+    // V^T operands read VPF steps ahead of their product
+    auto pv = [&](const f32x16 &P, const char *vt) __attribute__((always_inline)) {
+        v8 pb[BN / 16];
+#pragma unroll
+        for (int t4 = 0; t4 < BN / 16; ++t4) {
+            f32x8 x;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = P[t4 * 8 + e];
+            pb[t4] = __builtin_convertvector(x, v8);
+        }
+        constexpr int NST = BN / 16 * MD;
+        auto vread = [&](int st) __attribute__((always_inline)) -> v8 {
+            const int t4 = st / MD, md = st % MD;
+            const v4 va = E::read_tr(vt + toff(md, 0) + t4 * 16 * ROWB);
+            const v4 vb = E::read_tr(vt + toff(md, 1) + t4 * 16 * ROWB);
+            return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        v8 vbuf[VPF];
+#pragma unroll
+        for (int p = 0; p < VPF; ++p) vbuf[p] = vread(p);
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+            const v8 cur = vbuf[st % VPF];
+            if (st + VPF < NST) vbuf[st % VPF] = vread(st + VPF);
+            E::mfma_agpr(o[st % MD], cur, pb[st / MD]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Software pipeline over the tiles: K and V rings of two slots (tile t
+    // in slot t & 1).  Iteration t computes S^T of tile t + 1 with the
+    // exponentials of tile t placed between its products, then O^T +=
+    // V^T P^T of tile t, then the row max of tile t + 1; its copies (issued
+    // at the top, landed by its closing barrier) bring K(t + 2) into the slot
+    // K(t) left and V(t + 1) into the slot V(t - 1) left.
+    f32x16 sa, sb;
+    if (ntiles > 0) {
+        issue(0, 0);                           // K(0) by waves 0, 1; V(0) by waves 2, 3
+        if (!is_v && ntiles > 1) issue(1, 1);  // K(1)
+    }
+    wait_vmem();
+    __syncthreads();
+    bool vc = ntiles > 0 && visible(0);
+    if (vc) {
+        qk(sa, s_k, [](int) {});
+        row_max(sa, 0);
+    }
+    __syncthreads();  // K slot 0 is refilled by iteration 0
+
+    auto iteration = [&](int t, auto BUFC, f32x16 &Sc, f32x16 &Sn) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(BUFC)::value;
+        if (is_v) {
+            if (t + 1 < ntiles) issue(t + 1, BUF ^ 1);
+        } else {
+            if (t + 2 < ntiles) issue(t + 2, BUF);
+        }
+        const bool vn = t + 1 < ntiles && visible(t + 1);
+        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+        float rs = 0.f;
+        if (vn) {
+            qk(Sn, s_k + (BUF ^ 1) * TILEB, [&](int ks) {
+                if (ks & 1) prob(Sc, ks >> 1, neg_m, rs);
+            });
+        } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) prob(Sc, v, neg_m, rs);
+        }
+        if (vc) {
+            l_run += rs;
+            pv(Sc, s_v + BUF * TILEB);
+        }
+        if (vn) row_max(Sn, t + 1);
+        vc = vn;
         wait_vmem();
         __syncthreads();
+    };
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+        iteration(t, std::integral_constant<int, 0>{}, sa, sb);
+        iteration(t + 1, std::integral_constant<int, 1>{}, sb, sa);
     }
+    if (t < ntiles) iteration(t, std::integral_constant<int, 0>{}, sa, sb);
 
     // epilogue: lane (row n, half h2) holds O^T[32 md + 8 ii + 4 h2 + j]
 #pragma unroll
