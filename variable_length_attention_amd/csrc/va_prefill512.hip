@@ -334,12 +334,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const float m_new = fmaxf(m_run, mx);
             const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
+            // rows whose running max is still -inf have O = 0: no rescale
+            // while the whole wave is in that state (its first tile)
+            if (__ballot(m_run != -INFINITY) != 0ull) {
 #pragma unroll
-            for (int md = 0; md < MD; ++md) {
-                mfma_agpr_drain(o[md]);
+                for (int md = 0; md < MD; ++md) {
+                    mfma_agpr_drain(o[md]);
 #pragma unroll
-                for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
-                in_agpr(o[md]);
+                    for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
+                    in_agpr(o[md]);
+                }
             }
             m_run = m_new;
         }
