@@ -158,6 +158,7 @@ void k5_sparse16(SparseArgs a)
     constexpr int LPW = BN / RPI / 2;  // copies per wave per tile (2 waves)
     constexpr int ROWB = D * 2;
     constexpr int TILEB = BN * ROWB;
+    constexpr int KPF = 4, VPF = 3;    // LDS operand reads in flight ahead of their product (K, V)
     __shared__ __attribute__((aligned(16))) char s_tile[2 * TILEB];
     __shared__ __attribute__((aligned(16))) int s_list[kSpListMax];  // physical row per key, -1: none
 
@@ -237,6 +238,7 @@ void k5_sparse16(SparseArgs a)
             if constexpr (BIG) in_agpr(o[md]);
         }
         float m_run = sink2, l_run = (sink2 != -INFINITY && h2 == 0) ? 1.f : 0.f;
+        bool o_acc = false;   // some P V step has accumulated into O (wave-uniform)
 
         // the key list in chunks of at most kSpListMax keys
         for (int base = 0; base < L; base += kSpListMax) {
@@ -327,17 +329,33 @@ void k5_sparse16(SparseArgs a)
             if (tau + 1 < ntiles) issue(tau + 1, slot ^ 1);
             const char *kt = s_tile + slot * TILEB;
             // S^T = K Q^T: lane value v of block mb is key 32 mb + 8 (v/4) + 4 h2 + v%4
-            f32x16 S[NMB];
+            // steps st = (ks, mb), mb fastest; K operands read KPF steps
+            // ahead of their product.  With one 32-key block the even and
+            // odd k-steps go to two accumulators (two independent chains).
+            f32x16 S[NMB], S1;
 #pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) {
+            for (int v = 0; v < 16; ++v) S1[v] = 0.f;
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) S[mb][v] = 0.f;
+            {
+                constexpr int NST = KS * NMB;
+                v8 kb[KPF];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    S[mb] = E::mfma(*(const v8 *)(kt + koff(mb, ks)), qf[ks], S[mb]);
-                    // d512: at most 8 K operand reads ahead (Q^T holds 128 registers)
-                    if constexpr (BIG)
-                        if (ks % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+                for (int q = 0; q < KPF; ++q) kb[q] = *(const v8 *)(kt + koff(q % NMB, q / NMB));
+#pragma unroll
+                for (int st = 0; st < NST; ++st) {
+                    const int ks = st / NMB, mb = st % NMB;
+                    const v8 cur = kb[st % KPF];
+                    if (st + KPF < NST) kb[st % KPF] = *(const v8 *)(kt + koff((st + KPF) % NMB, (st + KPF) / NMB));
+                    if (NMB == 1 && (ks & 1)) S1 = E::mfma(cur, qf[ks], S1);
+                    else S[mb] = E::mfma(cur, qf[ks], S[mb]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if constexpr (NMB == 1) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) S[0][v] += S1[v];
                 }
             }
             float mx = -INFINITY;
@@ -370,12 +388,14 @@ void k5_sparse16(SparseArgs a)
                 const float m_new = fmaxf(m_run, mx);
                 const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
                 l_run *= alpha;
+                if (o_acc) {   // O is zero until the token's first P V step
 #pragma unroll
-                for (int md = 0; md < MD; ++md) {
-                    if constexpr (BIG) mfma_agpr_drain(o[md]);
+                    for (int md = 0; md < MD; ++md) {
+                        if constexpr (BIG) mfma_agpr_drain(o[md]);
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
-                    if constexpr (BIG) in_agpr(o[md]);
+                        for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
+                        if constexpr (BIG) in_agpr(o[md]);
+                    }
                 }
                 m_run = m_new;
             }
@@ -390,22 +410,37 @@ void k5_sparse16(SparseArgs a)
                     rs += pr;
                 }
             l_run += rs;
-            // O^T += V^T P^T, 16 keys per step
+            // O^T += V^T P^T, steps st = (t4, md) of 16 keys; V^T operands
+            // read VPF steps ahead of their product
+            {
+                v8 pb[NT4];
 #pragma unroll
-            for (int t4 = 0; t4 < NT4; ++t4) {
-                f32x8 pv;
+                for (int t4 = 0; t4 < NT4; ++t4) {
+                    f32x8 pv;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pv[e] = S[t4 >> 1][(t4 & 1) * 8 + e];
-                const v8 pb = __builtin_convertvector(pv, v8);
-#pragma unroll
-                for (int md = 0; md < MD; ++md) {
+                    for (int e = 0; e < 8; ++e) pv[e] = S[t4 >> 1][(t4 & 1) * 8 + e];
+                    pb[t4] = __builtin_convertvector(pv, v8);
+                }
+                constexpr int NST = NT4 * MD;
+                auto vread = [&](int st) __attribute__((always_inline)) -> v8 {
+                    const int t4 = st / MD, md = st % MD;
                     const v4 va = E::read_tr(kt + toff(md, 0) + t4 * 16 * ROWB);
                     const v4 vb = E::read_tr(kt + toff(md, 1) + t4 * 16 * ROWB);
-                    const v8 vf = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-                    if constexpr (BIG) E::mfma_agpr(o[md], vf, pb);
-                    else o[md] = E::mfma(vf, pb, o[md]);
+                    return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+                };
+                v8 vbuf[VPF];
+#pragma unroll
+                for (int q = 0; q < VPF; ++q) vbuf[q] = vread(q);
+#pragma unroll
+                for (int st = 0; st < NST; ++st) {
+                    const v8 cur = vbuf[st % VPF];
+                    if (st + VPF < NST) vbuf[st % VPF] = vread(st + VPF);
+                    if constexpr (BIG) E::mfma_agpr(o[st % MD], cur, pb[st / MD]);
+                    else o[st % MD] = E::mfma(cur, pb[st / MD], o[st % MD]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
+            o_acc = true;
             wait_vmem();
             __syncthreads();
         }
