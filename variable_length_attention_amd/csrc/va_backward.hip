@@ -742,14 +742,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             pin(d);
             P[kb][v] = d;
         };
+        // dO^T operand of step (half, md), read one step ahead of its products
+        auto oread = [&](int step) __attribute__((always_inline)) -> v8 {
+            const int t4 = rh * 2 + step / MD, md = step % MD;
+            const v4 ta = E::read_tr(ot + toff(md, 0) + t4 * 16 * ROWB);
+            const v4 tb = E::read_tr(ot + toff(md, 1) + t4 * 16 * ROWB);
+            return __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        v8 ofn = oread(0);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            const int t4 = rh * 2 + half;  // 16-row step of the tile
 #pragma unroll
             for (int md = 0; md < MD; ++md) {
-                const v4 ta = E::read_tr(ot + toff(md, 0) + t4 * 16 * ROWB);
-                const v4 tb = E::read_tr(ot + toff(md, 1) + t4 * 16 * ROWB);
-                const v8 of = __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7);
+                const v8 of = ofn;
+                if (half * MD + md + 1 < 2 * MD) ofn = oread(half * MD + md + 1);
                 // 32 values over 4 MD matrix instructions
                 constexpr int EPD = 8 / MD;
                 static_assert(4 * MD * EPD == 32, "every dS value gets a slot");

@@ -197,13 +197,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto qk = [&](f32x16 (&S)[2], const char *kt, auto &&hook) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) { S[0][v] = 0.f; S[1][v] = 0.f; }
+        // K operands read one step ahead of their products
+        v8 kf0 = *(const v8 *)(kt + koff(0));
+        v8 kf1 = *(const v8 *)(kt + koff(0) + 32 * ROWB);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const v8 kf0 = *(const v8 *)(kt + koff(ks));
-            const v8 kf1 = *(const v8 *)(kt + koff(ks) + 32 * ROWB);
+            v8 n0 = kf0, n1 = kf1;
+            if (ks + 1 < KS) {
+                n0 = *(const v8 *)(kt + koff(ks + 1));
+                n1 = *(const v8 *)(kt + koff(ks + 1) + 32 * ROWB);
+            }
             S[0] = E::mfma(kf0, qf[ks], S[0]);
             S[1] = E::mfma(kf1, qf[ks], S[1]);
             hook(ks);
+            kf0 = n0;
+            kf1 = n1;
         }
     };
     // mask (edge tiles only) and row max, then move the running max if the
@@ -281,13 +289,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         return __builtin_convertvector(pv, v8);
     };
-    // O^T += V^T P^T for one step of 16 keys
+    // V^T operand of block md for PV step t4 (transposing LDS reads)
+    auto vread = [&](int t4, int md, const char *vt) -> v8 {
+        const v4 va = E::read_tr((const uint16_t *)(vt + voff(md) + t4 * 16 * ROWB));
+        const v4 vb = E::read_tr((const uint16_t *)(vt + voff(md) + (t4 * 16 + 8) * ROWB));
+        return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // O^T += V^T P^T for one step of 16 keys; V^T operands read two
+    // products ahead
     auto pv = [&](const v8 &P, int t4, const char *vt) {
+        v8 vb0 = vread(t4, 0, vt), vb1 = vread(t4, 1, vt);
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
-            const v4 va = E::read_tr((const uint16_t *)(vt + voff(md) + t4 * 16 * ROWB));
-            const v4 vb = E::read_tr((const uint16_t *)(vt + voff(md) + (t4 * 16 + 8) * ROWB));
-            const v8 vf = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+            const v8 vf = (md & 1) ? vb1 : vb0;
+            if (md + 2 < MD) {
+                if (md & 1) vb1 = vread(t4, md + 2, vt);
+                else vb0 = vread(t4, md + 2, vt);
+            }
             o[md] = E::mfma(vf, P, o[md]);
         }
     };
@@ -336,6 +354,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         float rs = 0.f;
         constexpr int PER_KS = 16 / KS;
         static_assert(PER_KS * KS == 16, "16 probabilities over the K steps");
+        // matrix phases at a raised wave priority (the co-resident wave's
+        // vector-only phases yield the issue slot to them)
+        __builtin_amdgcn_s_setprio(1);
         if (vn) {
             qk(Sn, k_next, [&](int ks) {
                 if (ks % KEVERY == KEVERY - 1) issue_u(t + 2, false, k_dst, ks / KEVERY, rs_k);
@@ -369,6 +390,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         } else {
             issue(t + 1, true, v_dst);
         }
+        __builtin_amdgcn_s_setprio(0);
         if (vn) row_max(Sn, t + 1);
         vc = vn;
         wait_vmem();
