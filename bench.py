@@ -784,7 +784,7 @@ def main():
         log(f"backward: {ms_b:.4f} ms/call, {tf_b:.1f} TFLOP/s")
     if not args.no_d512:
         # the forward at head size 512 (its own kernel) on a causal GQA prefill
-        spec512 = W.Spec("bf16_causal_gqa_d512", 1512, "bf16", 32, 8, 512, ("fixed", [2048] * 4), causal=True)
+        spec512 = W.D512_PREFILL
         log(f"{spec512.name} (4 x 2048 tokens, 32/8 heads, head size 512, causal): generating input")
         c512 = W.make_case(spec512)
         ms_s, ms_p, path_s, ms_e = time_case(c512, args.steps, args.warmup, torch)

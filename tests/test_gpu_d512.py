@@ -3,7 +3,8 @@ C ABI) with the fp64 oracle: causal GQA with ragged and single-row
 sequences, the SparseAttnSharedkv README's first scenario shape on the dense
 path (64 heads on one kv head, window (127, 0), sinks), a two-sided window
 without causality, paged K/V for prefill and decode shapes, fp16, ALiBi,
-rows that see no key (with and without sinks), and the out variant.
+rows that see no key (with and without sinks), the out variant, and the
+benchmark's head-size-512 workload at full size, every row.
 
 Tolerances are the forward's (bf16: 2e-2 on O, 1e-3 on LSE; f16: 5e-3,
 1e-3): the kernel accumulates the 512-term scores and P V in fp32, so the
@@ -18,7 +19,7 @@ import pytest
 
 import oracle
 import workloads as W
-from helpers import announce, assert_close, run_case, to_f64
+from helpers import ORACLE_THREADS, announce, assert_close, assert_close_blocks, run_case, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -92,3 +93,19 @@ def test_d512_out_variant_matches_allocating_variant_bitwise():
     assert out_b.data_ptr() == buf.data_ptr()
     assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
     assert torch.equal(lse_a, lse_b)
+
+
+def test_d512_benchmark_workload_full_size_elementwise():
+    """The benchmark's head-size-512 workload (4 x 2048 tokens, causal,
+    32 / 8 heads, bf16) in its launch configuration, every (token, head) row
+    against the fp64 oracle (5.5e11 oracle FLOPs, about 15 s on 16 host
+    threads), compared in blocks of rows."""
+    announce("d512 benchmark workload: generating")
+    case = W.make_case(W.D512_PREFILL)
+    announce("d512 benchmark workload: running")
+    out, lse = run_case(case, torch)
+    torch.cuda.synchronize()
+    announce(f"d512 benchmark workload: oracle on all {case['T_q'] * case['H']} rows")
+    ref_o, ref_l = oracle.forward(case, nthreads=ORACLE_THREADS)
+    errs = assert_close_blocks(case, out, lse, ref_o, ref_l, "d512 benchmark workload")
+    announce(f"d512 benchmark workload: max |dO| = {errs[0]:.3e}, max |dLSE| = {errs[1]:.3e}")

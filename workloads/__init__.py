@@ -95,6 +95,11 @@ def config(n: int) -> Spec:
     return CONFIGS[n]
 
 
+# The head-size-512 forward workload (the SparseAttnSharedkv README's head
+# size on the dense path): 4 x 2048 tokens, causal, 32 query / 8 kv heads.
+D512_PREFILL = Spec("bf16_causal_gqa_d512", 1512, "bf16", 32, 8, 512, ("fixed", [2048] * 4), causal=True)
+
+
 def scaled(spec: Spec, *, B: int = 6, max_len: int = 300, seed: Optional[int] = None,
            name: Optional[str] = None) -> Spec:
     """Same structure (heads, dims, mask, sinks, paging) at sizes a slow CPU
