@@ -358,8 +358,10 @@ def test_stress_value_ranges_of_the_ascend_example():
 # ------------------------------------------------------------------ work partition
 def _plan_cpu(case, mode, bm=128, bn=64, sort=True):
     """Independent recomputation of the pre-pass list (deterministic order:
-    cost descending, then item index; index order for the sliding-window
-    kernel's items)."""
+    prefill items by their sequence's key-tile count descending, then item
+    index descending -- sequence by sequence, the last query block first;
+    decode items by cost descending, then item index; index order for the
+    sliding-window kernel's items)."""
     INF = 1 << 30
     left = case["window_left"] if case["window_left"] >= 0 else INF
     right = 0 if case["causal"] else (case["window_right"] if case["window_right"] >= 0 else INF)
@@ -384,7 +386,7 @@ def _plan_cpu(case, mode, bm=128, bn=64, sort=True):
             for s in range((Lq + bm - 1) // bm):
                 i0, i1 = s * bm, min(Lq, s * bm + bm)
                 lo, hi = rows_range(i0, i1, Lk - Lq, Lk) if Lk > 0 else (0, 0)
-                items.append(((hi - lo + bn - 1) // bn, (b, i0, lo, hi)))
+                items.append(((Lk + bn - 1) // bn, (b, i0, lo, hi)))
     else:
         vis = []
         for b in range(case["B"]):
@@ -402,7 +404,12 @@ def _plan_cpu(case, mode, bm=128, bn=64, sort=True):
                 k_hi = min(hi, k_lo + split)
                 items.append(((k_hi - k_lo + 255) // 256, (b, idx, k_lo, k_hi)))
                 idx += 1
-    order = sorted(range(len(items)), key=lambda i: (-min(items[i][0], 4095), i) if sort else i)
+    if not sort:
+        order = list(range(len(items)))
+    elif mode == "prefill":
+        order = sorted(range(len(items)), key=lambda i: (-min(items[i][0], 4095), -i))
+    else:
+        order = sorted(range(len(items)), key=lambda i: (-min(items[i][0], 4095), i))
     return np.asarray([items[i][1] for i in order], np.int32).reshape(-1, 4)
 
 

@@ -12,8 +12,12 @@
 // Decode mode:  one item per (sequence, split) where the visible key range of
 //   the whole sequence is cut into splits of a common size chosen from the
 //   total visible key count; the item carries its split slot.
-// Items are ordered by descending cost (longest first), ties by ascending
-// item index, so the result is deterministic.
+// Order (deterministic): prefill items sequence by sequence, the sequence
+// with the most bn-key tiles first (ties: the later sequence first), and
+// within a sequence its last query block first (under a causal mask its
+// costliest): the workgroups running at one time then share one sequence's
+// K/V in L2, and the list still ends with short work.  Decode and backward
+// items by descending cost (longest first), ties by ascending item index.
 #include "va_internal.h"
 
 namespace va {
@@ -192,6 +196,14 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
         return make_int4(b, idx, k_lo, k_hi);
     };
 
+    // ordering key: a cost bin (higher first) and, for prefill items, the
+    // index taken in reverse
+    const bool by_seq = a.mode == kPlanPrefill;
+    auto order_bin = [&](const int4 &itm, int cost) {
+        return min(by_seq ? (k_len(itm.x) + a.bn - 1) / a.bn : cost, kCostBins - 1);
+    };
+    auto order_idx = [&](int idx) { return by_seq ? N - 1 - idx : idx; };  // an involution
+
     if (a.mode == kPlanWindow) {
         // 3w. index order
         for (int idx = tid; idx < N; idx += kPlanThreads) {
@@ -201,11 +213,11 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
             a.seqinfo[idx] = seq_info(itm.x);
         }
     } else if (N <= kSortMax) {
-        // 3a. sort keys in LDS: ascending key = descending cost, then index
+        // 3a. sort keys in LDS: ascending key = descending bin, then index
         for (int idx = tid; idx < N; idx += kPlanThreads) {
             int cost;
-            make_item(idx, cost);
-            s_keys[idx] = ((uint32_t)(kCostBins - 1 - min(cost, kCostBins - 1)) << 19) | (uint32_t)idx;
+            const int4 itm = make_item(idx, cost);
+            s_keys[idx] = ((uint32_t)(kCostBins - 1 - order_bin(itm, cost)) << 19) | (uint32_t)order_idx(idx);
         }
         __syncthreads();
         if (N <= kRankSortMax) {
@@ -215,7 +227,7 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
                 int rank = 0;
                 for (int j = 0; j < N; ++j) rank += s_keys[j] < key;
                 int cost;
-                const int4 itm = make_item((int)(key & ((1u << 19) - 1u)), cost);
+                const int4 itm = make_item(order_idx((int)(key & ((1u << 19) - 1u))), cost);
                 a.items[rank] = itm;
                 a.seqinfo[rank] = seq_info(itm.x);
             }
@@ -240,20 +252,22 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
             }
             for (int i = tid; i < N; i += kPlanThreads) {
                 int cost;
-                const int4 itm = make_item((int)(s_keys[i] & ((1u << 19) - 1u)), cost);
+                const int4 itm = make_item(order_idx((int)(s_keys[i] & ((1u << 19) - 1u))), cost);
                 a.items[i] = itm;
                 a.seqinfo[i] = seq_info(itm.x);
             }
         }
     } else {
-        // 3b. large lists: counting placement, highest cost first, stable
+        // 3b. large lists: counting placement, highest bin first, stable in
+        // the order of order_idx
         for (int i = tid; i < kCostBins; i += kPlanThreads) s_bins[i] = 0;
         __syncthreads();
         for (int idx = tid; idx < N; idx += kPlanThreads) {
             int cost;
-            a.unsorted[idx] = make_item(idx, cost);
-            a.cost[idx] = cost;
-            atomicAdd(&s_bins[min(cost, kCostBins - 1)], 1);
+            const int4 itm = make_item(idx, cost);
+            a.unsorted[idx] = itm;
+            a.cost[idx] = order_bin(itm, cost);
+            atomicAdd(&s_bins[order_bin(itm, cost)], 1);
         }
         __syncthreads();
         constexpr int per = kCostBins / kPlanThreads;
@@ -268,12 +282,12 @@ __global__ __launch_bounds__(kPlanThreads) void k0_plan(PlanArgs a)
             run += c;
         }
         __syncthreads();
-        if (tid < 64) {  // one wave, 64 items at a time in index order
+        if (tid < 64) {  // one wave, 64 items at a time in order_idx order
             const int lane = tid;
             for (int base = 0; base < N; base += 64) {
-                const int idx = base + lane;
-                const bool active = idx < N;
-                const int c = active ? min(a.cost[idx], kCostBins - 1) : -1;
+                const bool active = base + lane < N;
+                const int idx = active ? order_idx(base + lane) : 0;
+                const int c = active ? a.cost[idx] : -1;
                 unsigned long long remaining = __ballot(active);
                 while (remaining) {
                     const int leader = __ffsll((long long)remaining) - 1;
