@@ -50,12 +50,12 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 # (profiles/traffic.json): a measurement counts only for the exact sources
 # it was taken with.
 KERNEL_SOURCES = {
-    "prefill_bf16": ["va_prefill_bf16.hip", "va_device.h"],
+    "prefill_bf16": ["va_prefill_bf16.hip", "va_device.h", "va_plan.hip"],  # the item order sets L2 reuse
     "decode_bf16": ["va_decode.hip"],
     "f32": ["va_prefill_f32.hip"],
     "window_bf16": ["va_window.hip"],
     "sparse": ["va_sparse.hip"],
-    "prefill512": ["va_prefill512.hip"],
+    "prefill512": ["va_prefill512.hip", "va_plan.hip"],
 }
 PATH_NAMES = ["prefill_bf16", "decode_bf16", "f32", "window_bf16", "prefill512"]  # index = varlen_attn_path
 
