@@ -100,16 +100,12 @@ __device__ __forceinline__ void in_agpr(f32x16 &acc)
 // chunk's bank depends on its index mod 16 only).
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-// 16 bytes per lane, global -> LDS (lane i writes LDS bytes [lds + 16 i, +16));
-// no register results, M0 carries the LDS address.  Ordered by the kernel's
-// own vector-memory wait and barrier before a buffer is read.
-__device__ __forceinline__ void copy16_global(const void *src, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "m0");
-}
-// The same copy from a wave-uniform base (SGPR pair) plus a 32-bit lane
-// offset, to LDS address lds + ldsoff (M0 formed here, so that the
-// destinations of a tile's rows are not each held in a register).
+// 16 bytes per lane, global -> LDS (lane i writes LDS bytes [lds + ldsoff
+// + 16 i, +16)) from a wave-uniform base (SGPR pair) plus a 32-bit lane
+// offset; no register results.  M0 (the LDS address) is formed here, so
+// that the destinations of a tile's rows are not each held in a register.
+// Ordered by the kernel's own vector-memory wait and barrier before a
+// buffer is read.
 __device__ __forceinline__ void copy16_global_sv(const void *sbase, uint32_t voff, uint32_t lds, uint32_t ldsoff)
 {
     asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"

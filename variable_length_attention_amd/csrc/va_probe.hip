@@ -273,23 +273,23 @@ extern "C" int va_probe_hbm_stream(int mode, long long bytes, int reps, int bloc
     };
     if (e == hipSuccess) {
         run();  // warm-up
-        hipEventRecord(e0, 0);
-        for (int r = 0; r < reps; ++r) run();
-        hipEventRecord(e1, 0);
-        e = hipEventSynchronize(e1);
+        e = hipEventRecord(e0, 0);
+        for (int r = 0; r < reps && e == hipSuccess; ++r) run();
+        if (e == hipSuccess) e = hipEventRecord(e1, 0);
+        if (e == hipSuccess) e = hipEventSynchronize(e1);
     }
     if (e == hipSuccess) e = hipGetLastError();
     if (e == hipSuccess) {
         float t = 0.f;
-        hipEventElapsedTime(&t, e0, e1);
+        e = hipEventElapsedTime(&t, e0, e1);
         *ms = t;
         *gbs = (double)bytes * (mode == 1 ? 2.0 : 1.0) * reps / (t * 1e-3) / 1e9;
     }
-    if (e0) hipEventDestroy(e0);
-    if (e1) hipEventDestroy(e1);
-    if (src) hipFree(src);
-    if (dst) hipFree(dst);
-    if (sink) hipFree(sink);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (src) (void)hipFree(src);
+    if (dst) (void)hipFree(dst);
+    if (sink) (void)hipFree(sink);
     return (int)e;
 }
 
@@ -332,17 +332,17 @@ extern "C" int va_probe_mfma_stream(int waves_per_simd, int iters, int zero_data
     if (e == hipSuccess) e = hipEventCreate(&e1);
     if (e == hipSuccess) {
         fn(grid, iters / 4 + 1, zero_data, sink, clk, 0);  // warm-up (clock ramp)
-        hipEventRecord(e0, 0);
-        fn(grid, iters, zero_data, sink, clk, 0);
-        hipEventRecord(e1, 0);
-        e = hipEventSynchronize(e1);
+        e = hipEventRecord(e0, 0);
+        if (e == hipSuccess) fn(grid, iters, zero_data, sink, clk, 0);
+        if (e == hipSuccess) e = hipEventRecord(e1, 0);
+        if (e == hipSuccess) e = hipEventSynchronize(e1);
     }
     if (e == hipSuccess) e = hipGetLastError();
     if (e == hipSuccess) {
         float t = 0.f;
-        hipEventElapsedTime(&t, e0, e1);
-        unsigned long long *h = new unsigned long long[(size_t)waves * 2];
-        e = hipMemcpy(h, clk, (size_t)waves * 2 * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+        e = hipEventElapsedTime(&t, e0, e1);
+        unsigned long long *h = new unsigned long long[(size_t)waves * 2]();
+        if (e == hipSuccess) e = hipMemcpy(h, clk, (size_t)waves * 2 * sizeof(unsigned long long), hipMemcpyDeviceToHost);
         double cyc = 0, real = 0;
         for (int w = 0; w < waves; ++w) { cyc += (double)h[2 * w]; real += (double)h[2 * w + 1]; }
         delete[] h;
@@ -350,10 +350,10 @@ extern "C" int va_probe_mfma_stream(int waves_per_simd, int iters, int zero_data
         *tflops = (double)waves * iters * 4.0 * 32768.0 / (t * 1e-3) / 1e12;
         *mhz = real > 0 ? cyc / real * 100.0 : 0.0;
     }
-    if (e0) hipEventDestroy(e0);
-    if (e1) hipEventDestroy(e1);
-    if (sink) hipFree(sink);
-    if (clk) hipFree(clk);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (sink) (void)hipFree(sink);
+    if (clk) (void)hipFree(clk);
     return (int)e;
 }
 
@@ -391,17 +391,17 @@ extern "C" int va_probe_lds_stream(int waves_per_simd, int iters, int mode, doub
     if (e == hipSuccess) e = hipEventCreate(&e1);
     if (e == hipSuccess) {
         go(iters / 4 + 1);  // warm-up (clock ramp)
-        hipEventRecord(e0, 0);
-        go(iters);
-        hipEventRecord(e1, 0);
-        e = hipEventSynchronize(e1);
+        e = hipEventRecord(e0, 0);
+        if (e == hipSuccess) go(iters);
+        if (e == hipSuccess) e = hipEventRecord(e1, 0);
+        if (e == hipSuccess) e = hipEventSynchronize(e1);
     }
     if (e == hipSuccess) e = hipGetLastError();
     if (e == hipSuccess) {
         float t = 0.f;
-        hipEventElapsedTime(&t, e0, e1);
-        unsigned long long *h = new unsigned long long[(size_t)waves * 2];
-        e = hipMemcpy(h, clk, (size_t)waves * 2 * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+        e = hipEventElapsedTime(&t, e0, e1);
+        unsigned long long *h = new unsigned long long[(size_t)waves * 2]();
+        if (e == hipSuccess) e = hipMemcpy(h, clk, (size_t)waves * 2 * sizeof(unsigned long long), hipMemcpyDeviceToHost);
         double cyc = 0, real = 0;
         for (int w = 0; w < waves; ++w) { cyc += (double)h[2 * w]; real += (double)h[2 * w + 1]; }
         delete[] h;
@@ -411,9 +411,9 @@ extern "C" int va_probe_lds_stream(int waves_per_simd, int iters, int mode, doub
         *mhz = real > 0 ? cyc / real * 100.0 : 0.0;
         *bytes_per_clk = cyc > 0 ? (double)waves * iters * per_wave / (cyc / waves) / cus : 0.0;
     }
-    if (e0) hipEventDestroy(e0);
-    if (e1) hipEventDestroy(e1);
-    if (sink) hipFree(sink);
-    if (clk) hipFree(clk);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (sink) (void)hipFree(sink);
+    if (clk) (void)hipFree(clk);
     return (int)e;
 }
