@@ -358,11 +358,9 @@ void k5_sparse16(SparseArgs a)
                     for (int v = 0; v < 16; ++v) S[0][v] += S1[v];
                 }
             }
+            // raw scores (scale > 0: the max of the raw scores scaled is the
+            // max of the scaled ones; the scale rides in the exponent's FMA)
             float mx = -INFINITY;
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) S[mb][v] *= a.scale_log2;
             if (masked) {
                 // keys that select nothing (list entry -1) drop out
 #pragma unroll
@@ -383,7 +381,7 @@ void k5_sparse16(SparseArgs a)
             // the running max moves only when a tile raises it by more than
             // 2^8 (log2 units) for some head: until then the probabilities
             // stay below 2^8 and the O / l rescale is skipped
-            mx = halves_max(mx);
+            mx = halves_max(mx) * a.scale_log2;
             if (__ballot(mx > m_run + 8.f) != 0ull) {
                 const float m_new = fmaxf(m_run, mx);
                 const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -399,13 +397,13 @@ void k5_sparse16(SparseArgs a)
                 }
                 m_run = m_new;
             }
-            const float m_use = m_run == -INFINITY ? 0.f : m_run;
+            const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
             float rs = 0.f;
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const float pr = __builtin_amdgcn_exp2f(S[mb][v] - m_use);
+                    const float pr = __builtin_amdgcn_exp2f(fmaf(S[mb][v], a.scale_log2, neg_m));
                     S[mb][v] = pr;
                     rs += pr;
                 }
