@@ -144,8 +144,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ __attribute__((aligned(16))) char s_k[CAP * ROWB];
     __shared__ __attribute__((aligned(16))) char s_v[CAP * ROWB];
 
-    const int c = blockIdx.x % a.Hkv;
-    const int item = blockIdx.x / a.Hkv;
+    // each XCD takes a contiguous range of items: neighbouring rows share
+    // most of their window, which then stays in that XCD's L2
+    const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int c = wg % a.Hkv;
+    const int item = wg / a.Hkv;
     const int n_items = *count;
     if (item >= n_items) return;
     const int4 it = items[item];
